@@ -1,0 +1,360 @@
+"""CPU oracle for the DeepSeek-Sparse-Attention read path of Kimi K3.1's global layers.
+
+TEST INFRASTRUCTURE ONLY.  This module is a plain, slow, fp64 restatement of what the
+path computes, written from the page "Kimi K3.1 Pro: Sparse-Zugriffe, keine kleinere
+Historie" (flozi.net guide on the K3.1 DSA indexer and cache).  Only the test suite, the
+package smoke check and the CPU-baseline leg of the benchmark may import it; the product
+path (the HIP library and its Python binding) never does, and shares no code with it.
+
+Every function works on numpy arrays in float64.  BF16 tensors arrive as their raw 16-bit
+patterns (uint16) and are decoded here by this module's own codec.  A library primitive
+(matmul, sort, exp) is used as a single step; nothing is blocked, fused or reordered.
+
+Readings of the page where it is silent or garbled (its three display equations were lost
+in extraction) are stated at each function; all of them are listed in the design notes.
+Every function below is pinned by the CPU tests in tests/test_oracle_*.py against
+closed forms, library routines, brute force or the page's printed arithmetic.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ----------------------------------------------------------------------------------------
+# Shapes fixed by the page (section "Was ändert sich – und was nicht?" and section
+# "Der neue Indexer ..." paragraph): 32 indexer query heads of width 128, one shared
+# 128-wide index key per stored position, a selection budget of 2048 positions, 96 main
+# attention heads, KV latent rank 512 plus a 64-wide companion key component.
+# ----------------------------------------------------------------------------------------
+INDEX_HEADS = 32
+INDEX_DIM = 128
+TOPK = 2048
+MLA_HEADS = 96
+LATENT_DIM = 512
+COMPANION_DIM = 64
+QK_DIM = LATENT_DIM + COMPANION_DIM  # 576
+
+
+# ----------------------------------------------------------------------------------------
+# BF16 codec (the oracle's own; no code is shared with the input generators or the GPU).
+# ----------------------------------------------------------------------------------------
+def bf16_to_f64(bits) -> np.ndarray:
+    """Decode raw bf16 bit patterns: a bf16 is the upper half of an IEEE binary32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """Round float64 values to bf16 with round-to-nearest-even, in ONE rounding step.
+
+    bf16 keeps 8 significant bits and binary32's exponent range.  For |x| with leading bit
+    2^(e-1) the spacing of bf16 numbers is 2^(e-8), never below the subnormal spacing
+    2^-133.  Scaling by a power of two is exact in float64, and numpy's round() breaks
+    ties to even, so round(x / q) * q is the correctly rounded value.  Results at or
+    above 2^128 overflow to infinity; NaN becomes the canonical quiet NaN 0x7FC0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)
+    q_exp = np.maximum(e - 8, -133)
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = np.ldexp(np.round(np.ldexp(a, -q_exp)), q_exp)
+        r = np.where(r >= 2.0 ** 128, np.inf, r)
+        r = np.where(np.isinf(a), np.inf, r)
+        bits = (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = np.where(np.signbit(x), bits | np.uint16(0x8000), bits).astype(np.uint16)
+    bits = np.where(np.isnan(x), np.uint16(0x7FC0), bits).astype(np.uint16)
+    return bits
+
+
+# ----------------------------------------------------------------------------------------
+# Stage 1: index-key LayerNorm.
+# Page section "Eine Query durch den Indexer verfolgen": a projection maps residual states
+# to keys [S,128], followed by LayerNorm; the adapter paragraph after it fixes LayerNorm
+# (not RMSNorm), FP32 key normalisation, no Hadamard transform and index_rope_dim = 0
+# (no rotation of the keys).  Reading: biased variance, affine gamma/beta in fp32, an eps
+# passed by the caller, result stored as bf16 (round to nearest even).
+# ----------------------------------------------------------------------------------------
+def layernorm_keys(raw, gamma, beta, eps) -> np.ndarray:
+    """Exact-as-fp64 LayerNorm of each 128-wide row; returns float64 [N,128]."""
+    x = np.asarray(raw, dtype=np.float32).astype(np.float64)
+    g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    b = np.asarray(beta, dtype=np.float32).astype(np.float64)
+    eps = float(np.float32(eps))
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def layernorm_keys_bf16(raw, gamma, beta, eps) -> np.ndarray:
+    """Stage-1 output as stored in the index-key cache: bf16 bit patterns [N,128]."""
+    return f64_to_bf16(layernorm_keys(raw, gamma, beta, eps))
+
+
+# ----------------------------------------------------------------------------------------
+# Admissible set.
+# Page section "Eine Query durch den Indexer verfolgen": the scoring path picks up to 2048
+# *causal* candidates per query.  Reading: a query at absolute position p in request b
+# may see positions j <= p that exist in b's cache, i.e. j in [0, n_t) with
+# n_t = min(p + 1, S_b).  The diagonal is admissible.
+# ----------------------------------------------------------------------------------------
+def admissible_count(q_pos: int, s_b: int) -> int:
+    return int(max(0, min(int(q_pos) + 1, int(s_b))))
+
+
+def request_lengths(kv_off) -> np.ndarray:
+    off = np.asarray(kv_off, dtype=np.int64)
+    return off[1:] - off[:-1]
+
+
+# ----------------------------------------------------------------------------------------
+# Stage 2: indexer scores.
+# The page names the ingredients (32 heads x 128 queries [T,32,128], one shared key [S,128]
+# per position, 32 head weights per query from the BF16 head-gate path); the combination
+# is the weighted-ReLU sum  s_tj = sum_h w_th * max(0, q_th . k_j)  over admissible j.
+# No further scale, softmax or rounding is applied: weights are used as given.
+# ----------------------------------------------------------------------------------------
+def indexer_scores_one(q_t, w_t, keys_rows) -> np.ndarray:
+    """Scores of one query against a block of key rows (all float64 inputs).
+
+    q_t: [H, D], w_t: [H], keys_rows: [n, D]  ->  [n]
+    """
+    logits = q_t @ keys_rows.T  # [H, n]
+    return w_t @ np.maximum(logits, 0.0)
+
+
+def indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, rows=None):
+    """Scores of every query over its admissible positions.
+
+    q_idx [T,H,D] bf16 bits, w [T,H] bf16 bits, keys [N,D] bf16 bits, kv_off [B+1] int64
+    row offsets of each request's segment, q_req [T] request of each query, q_pos [T]
+    absolute position of each query.  Returns a list of float64 arrays, one per query
+    (or per query listed in `rows`), each of length n_t.
+    """
+    q_idx = np.asarray(q_idx)
+    w = np.asarray(w)
+    keys = np.asarray(keys)
+    kv_off = np.asarray(kv_off, dtype=np.int64)
+    s_len = request_lengths(kv_off)
+    out = []
+    for t in (range(q_idx.shape[0]) if rows is None else rows):
+        b = int(q_req[t])
+        n = admissible_count(q_pos[t], s_len[b])
+        k_rows = bf16_to_f64(keys[kv_off[b]: kv_off[b] + n])
+        out.append(indexer_scores_one(bf16_to_f64(q_idx[t]), bf16_to_f64(w[t]), k_rows))
+    return out
+
+
+def indexer_score_magnitude(q_idx, w, keys, kv_off, q_req, q_pos, rows=None):
+    """Condition magnitude  sum_h |w_th| * ReLU(q_th . k_j)  per admissible position."""
+    q_idx = np.asarray(q_idx)
+    kv_off = np.asarray(kv_off, dtype=np.int64)
+    s_len = request_lengths(kv_off)
+    out = []
+    for t in (range(q_idx.shape[0]) if rows is None else rows):
+        b = int(q_req[t])
+        n = admissible_count(q_pos[t], s_len[b])
+        k_rows = bf16_to_f64(np.asarray(keys)[kv_off[b]: kv_off[b] + n])
+        logits = bf16_to_f64(q_idx[t]) @ k_rows.T
+        out.append(np.abs(bf16_to_f64(np.asarray(w)[t])) @ np.maximum(logits, 0.0))
+    return out
+
+
+def row_scale(scores_row) -> float:
+    """Root-mean-square of a query's admissible scores (0 for an empty row)."""
+    s = np.asarray(scores_row, dtype=np.float64)
+    return float(np.sqrt(np.mean(s * s))) if s.size else 0.0
+
+
+# ----------------------------------------------------------------------------------------
+# Stage 3: top-k selection.
+# Page section "Eine Query durch den Indexer verfolgen": up to 2048 causal candidates per
+# query, a logical position-ID array [T,2048], invalid entries and short prefixes handled
+# by the backend.  Section "Die Mathematik ...": I_t holds the up-to-2048 positions with
+# the highest scores.  Readings (the page is silent): when n_t <= k every admissible
+# position is selected; a tie at the k-th score goes to the lower position; -0 equals +0;
+# NaN ranks below every number; a row lists its selected IDs in ascending position order
+# followed by -1 entries up to k.
+# ----------------------------------------------------------------------------------------
+def topk_ids(scores_row, k: int = TOPK) -> np.ndarray:
+    """Canonical top-k position IDs of one row of scores (float32 or float64)."""
+    s = np.asarray(scores_row)
+    n = int(s.shape[0])
+    ids = np.full(k, -1, dtype=np.int32)
+    if n <= k:
+        ids[:n] = np.arange(n, dtype=np.int32)
+        return ids
+    nan = np.isnan(s)
+    v = np.where(nan, 0.0, s.astype(np.float64)) + 0.0  # -0 + 0 = +0: one zero
+    # np.lexsort sorts by the LAST key first: non-NaN first, then larger score, then
+    # lower position.  The sort is a full sort of the row: the textbook definition.
+    order = np.lexsort((np.arange(n), -v, nan))
+    ids[:] = np.sort(order[:k]).astype(np.int32)
+    return ids
+
+
+def topk_rows(score_rows, k: int = TOPK) -> np.ndarray:
+    return np.stack([topk_ids(r, k) for r in score_rows]) if len(score_rows) else \
+        np.zeros((0, k), np.int32)
+
+
+def kth_score(scores_row, k: int = TOPK):
+    """The score of the k-th selected position (None when n_t <= k)."""
+    s = np.asarray(scores_row, dtype=np.float64)
+    if s.shape[0] <= k:
+        return None
+    ids = topk_ids(s, k)
+    return float(np.min(s[ids]))
+
+
+def selection_band(scores_row, k: int = TOPK, rel: float = 1e-3) -> np.ndarray:
+    """Positions whose reference score lies within `rel` of the k-th score.
+
+    Reading of the stated set tolerance: a GPU selection may differ from the oracle's only
+    at positions j with |s_j - theta| <= rel * max(|theta|, r_t), where theta is the k-th
+    score and r_t the row's RMS score (a floor for rows whose weighted heads cancel).
+    """
+    s = np.asarray(scores_row, dtype=np.float64)
+    theta = kth_score(s, k)
+    if theta is None:
+        return np.zeros(0, dtype=np.int64)
+    tol = rel * max(abs(theta), row_scale(s))
+    return np.nonzero(np.abs(s - theta) <= tol)[0]
+
+
+# ----------------------------------------------------------------------------------------
+# Stage 4: absorbed-MLA read restricted to I_t.
+# Section "Die Mathematik ...": the sparse read is a softmax restricted to I_t over the
+# main-attention logits a_tj of each head (the display equation itself was lost).  The
+# notation abstracts absorbed MLA projections: per-head K/V are not materialised; all 96
+# heads read the one shared latent (section "Warum Top-2048 ..." last paragraphs, and the
+# Gated-MLA paragraph: a 64-wide companion key component beside the 512-wide latent,
+# skip_rope, no rotation).  Readings: a_tj = scale * q_th . [c_j ; kpe_j] over 576 dims,
+# values are the 512-wide latent rows only, scale = 1/sqrt(192) is passed by the caller,
+# lse = log sum exp a over I_t.  IDs < 0 or >= S_b are padding and are skipped; a row with
+# no valid ID reads zero with lse = -inf.
+# ----------------------------------------------------------------------------------------
+def gather_rows(latent, kpe, row_index):
+    """[n,576] float64 rows: latent[:, :512] next to kpe[:, :64] for absolute rows."""
+    lat = bf16_to_f64(np.asarray(latent)[row_index, :LATENT_DIM])
+    kp = bf16_to_f64(np.asarray(kpe)[row_index, :COMPANION_DIM])
+    return np.concatenate([lat, kp], axis=1)
+
+
+def restricted_softmax_read(q_t, rows576, scale):
+    """One query, all heads: softmax over the given rows only, then read their latents.
+
+    q_t [H,576] float64, rows576 [n,576] float64 -> (o [H,512], lse [H]).
+    """
+    h = q_t.shape[0]
+    if rows576.shape[0] == 0:
+        return np.zeros((h, LATENT_DIM)), np.full(h, -np.inf)
+    a = scale * (q_t @ rows576.T)  # [H, n]
+    m = a.max(axis=1, keepdims=True)
+    p = np.exp(a - m)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ rows576[:, :LATENT_DIM]) / l
+    return o, (m + np.log(l))[:, 0]
+
+
+def valid_ids(ids_row, s_b):
+    r = np.asarray(ids_row, dtype=np.int64)
+    return r[(r >= 0) & (r < s_b)]
+
+
+def sparse_mla(q, latent, kpe, kv_off, q_req, ids, scale, rows=None):
+    """Stage 4 for every query (or the listed ones): returns (out [T,H,512], lse [T,H])."""
+    q = np.asarray(q)
+    kv_off = np.asarray(kv_off, dtype=np.int64)
+    s_len = request_lengths(kv_off)
+    sel = list(range(q.shape[0]) if rows is None else rows)
+    out = np.zeros((len(sel), q.shape[1], LATENT_DIM))
+    lse = np.zeros((len(sel), q.shape[1]))
+    for i, t in enumerate(sel):
+        b = int(q_req[t])
+        j = valid_ids(ids[t], s_len[b])
+        c = gather_rows(latent, kpe, kv_off[b] + j)
+        out[i], lse[i] = restricted_softmax_read(bf16_to_f64(q[t]), c, scale)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------------------
+# Dense reference and dropped mass (oracle only, never timed).
+# Section "Die Mathematik ...": compared with a hypothetical full read at fixed logits and
+# values, with eps the full softmax mass outside I_t, the retained and dropped reads are
+# convex combinations of bounded values (the bound's display was lost).  Reading:
+#   o_full = (1 - eps) o_sparse + eps o_drop   (exact identity)
+#   |o_sparse - o_full|_c <= eps * (max_j v_jc - min_j v_jc)   per coordinate c
+#   ||o_sparse - o_full|| <= eps * max_{i,j} ||v_i - v_j|| <= 2 eps max_j ||v_j||.
+# ----------------------------------------------------------------------------------------
+def dense_read(q, latent, kpe, kv_off, q_req, q_pos, ids, scale, rows=None):
+    """Full causal read and the split into retained/dropped parts.
+
+    Returns dict with o_full [T,H,512], eps [T,H], o_drop [T,H,512] (zeros where eps=0),
+    v_range [T,512] (max - min of each latent coordinate over the admissible rows) and
+    v_diam [T] (max pairwise distance of admissible latent rows, bounded by 2 max norm).
+    """
+    q = np.asarray(q)
+    kv_off = np.asarray(kv_off, dtype=np.int64)
+    s_len = request_lengths(kv_off)
+    sel = list(range(q.shape[0]) if rows is None else rows)
+    h = q.shape[1]
+    res = {k: [] for k in ("o_full", "eps", "o_drop", "v_range", "v_maxnorm")}
+    for t in sel:
+        b = int(q_req[t])
+        n = admissible_count(q_pos[t], s_len[b])
+        c = gather_rows(latent, kpe, kv_off[b] + np.arange(n))
+        if n == 0:
+            res["o_full"].append(np.zeros((h, LATENT_DIM)))
+            res["eps"].append(np.zeros(h))
+            res["o_drop"].append(np.zeros((h, LATENT_DIM)))
+            res["v_range"].append(np.zeros(LATENT_DIM))
+            res["v_maxnorm"].append(0.0)
+            continue
+        a = scale * (bf16_to_f64(q[t]) @ c.T)
+        pi = np.exp(a - a.max(axis=1, keepdims=True))
+        pi /= pi.sum(axis=1, keepdims=True)
+        v = c[:, :LATENT_DIM]
+        in_i = np.zeros(n, dtype=bool)
+        in_i[valid_ids(ids[t], n)] = True
+        eps = pi[:, ~in_i].sum(axis=1)
+        drop = pi[:, ~in_i] @ v[~in_i]
+        o_drop = np.where(eps[:, None] > 0, drop / np.where(eps > 0, eps, 1.0)[:, None], 0.0)
+        res["o_full"].append(pi @ v)
+        res["eps"].append(eps)
+        res["o_drop"].append(o_drop)
+        res["v_range"].append(v.max(axis=0) - v.min(axis=0))
+        res["v_maxnorm"].append(float(np.sqrt((v * v).sum(axis=1)).max()))
+    return {k: np.asarray(x) for k, x in res.items()}
+
+
+# ----------------------------------------------------------------------------------------
+# Byte budget, section "Warum Top-2048 keinen 2048-Token-Cache bedeutet": per global layer
+# and position a 512+64 element MLA representation plus a 128-element index key, all BF16,
+# summed over the 24 global layers; and the selected fraction at the 1,048,576-token limit.
+# ----------------------------------------------------------------------------------------
+GLOBAL_LAYERS = 24
+CONTEXT_LIMIT = 1_048_576
+
+
+def payload_bytes_per_position_per_layer(elem_bytes: int = 2) -> int:
+    return (LATENT_DIM + COMPANION_DIM + INDEX_DIM) * elem_bytes
+
+
+def payload_bytes_per_token(layers: int = GLOBAL_LAYERS, elem_bytes: int = 2) -> int:
+    return layers * payload_bytes_per_position_per_layer(elem_bytes)
+
+
+def payload_bytes_at(tokens: int, layers: int = GLOBAL_LAYERS) -> int:
+    return tokens * payload_bytes_per_token(layers)
+
+
+def selection_fraction(k: int = TOPK, context: int = CONTEXT_LIMIT) -> float:
+    return k / context
+
+
+def attention_scale(qk_head_dim: int = 192) -> float:
+    """Softmax scale 1/sqrt(192) of the main attention (used as given by the caller)."""
+    return 1.0 / math.sqrt(qk_head_dim)
