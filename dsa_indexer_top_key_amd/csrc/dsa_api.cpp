@@ -1,0 +1,233 @@
+// Host side of the C ABI declared in include/dsa.h: argument validation (before any HIP
+// call), workspace sizing, launch dispatch and error reporting.  No allocation, no host
+// synchronisation, no state kept between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "dsa.h"
+
+namespace dsa {
+hipError_t launch_ln_keys(const float* raw, const float* gamma, const float* beta, float eps,
+                          uint16_t* keys, int64_t n_rows, hipStream_t stream);
+hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
+                                 const int64_t* kv_off, const int32_t* q_req,
+                                 const int32_t* q_pos, int32_t T, int32_t B, int64_t max_s,
+                                 float* scores, int64_t ld, hipStream_t stream);
+hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
+                       const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
+                       int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream);
+hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t ld_lat,
+                             const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
+                             const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
+                             uint16_t* out, float* lse, void* workspace, hipStream_t stream);
+size_t sparse_mla_workspace_bytes(int32_t T);
+}  // namespace dsa
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status_t fail(dsa_status_t code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+dsa_status_t ok() {
+    g_err[0] = '\0';
+    return DSA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+dsa_status_t from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(DSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+#define DSA_REQUIRE(cond, code, ...) \
+    do {                             \
+        if (!(cond)) return fail(code, __VA_ARGS__); \
+    } while (0)
+
+constexpr size_t kAlign = DSA_WORKSPACE_ALIGN;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Common checks of the indexer arguments (stages 2 and 2+3).
+dsa_status_t check_indexer(const char* fn, const uint16_t* q_idx, const uint16_t* w,
+                           const uint16_t* keys, const int64_t* kv_off, const int32_t* q_req,
+                           const int32_t* q_pos, int32_t T, int32_t B, int64_t max_S,
+                           int32_t n_heads, int32_t head_dim) {
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    DSA_REQUIRE(B >= 1, DSA_ERR_INVALID_ARG, "%s: B=%d must be >= 1", fn, B);
+    DSA_REQUIRE(max_S >= 1 && max_S <= INT32_MAX, DSA_ERR_INVALID_ARG,
+                "%s: max_S=%lld must be in [1, 2^31-1]", fn, static_cast<long long>(max_S));
+    DSA_REQUIRE(n_heads == DSA_INDEX_HEADS && head_dim == DSA_INDEX_DIM, DSA_ERR_UNSUPPORTED,
+                "%s: indexer shape %d heads x %d is unsupported (only %d x %d)", fn, n_heads,
+                head_dim, DSA_INDEX_HEADS, DSA_INDEX_DIM);
+    DSA_REQUIRE(q_idx && w && keys && kv_off && q_req && q_pos, DSA_ERR_INVALID_ARG,
+                "%s: null input pointer", fn);
+    DSA_REQUIRE(aligned(q_idx, 16) && aligned(keys, 16), DSA_ERR_INVALID_ARG,
+                "%s: q_idx and keys must be 16-byte aligned", fn);
+    DSA_REQUIRE(aligned(w, 2) && aligned(kv_off, 8) && aligned(q_req, 4) && aligned(q_pos, 4),
+                DSA_ERR_INVALID_ARG, "%s: misaligned w/kv_off/q_req/q_pos", fn);
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return 1; }
+
+const char* dsa_status_string(int status) {
+    switch (status) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape or option not implemented";
+        case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP runtime error";
+        default: return "unknown dsa status";
+    }
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+dsa_status_t dsa_index_keys_layernorm(const float* raw, const float* gamma, const float* beta,
+                                      float eps, uint16_t* keys, int64_t n_rows, void* stream) {
+    const char* fn = "dsa_index_keys_layernorm";
+    DSA_REQUIRE(n_rows >= 0, DSA_ERR_INVALID_ARG, "%s: n_rows=%lld is negative", fn,
+                static_cast<long long>(n_rows));
+    DSA_REQUIRE(std::isfinite(eps) && eps >= 0.f, DSA_ERR_INVALID_ARG,
+                "%s: eps must be finite and >= 0", fn);
+    if (n_rows == 0) return ok();
+    DSA_REQUIRE(raw && gamma && beta && keys, DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+    DSA_REQUIRE(aligned(raw, 16) && aligned(gamma, 16) && aligned(beta, 16) && aligned(keys, 16),
+                DSA_ERR_INVALID_ARG, "%s: raw, gamma, beta and keys must be 16-byte aligned", fn);
+    return from_hip(dsa::launch_ln_keys(raw, gamma, beta, eps, keys, n_rows,
+                                        static_cast<hipStream_t>(stream)), fn);
+}
+
+dsa_status_t dsa_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
+                                const int64_t* kv_off, const int32_t* q_req,
+                                const int32_t* q_pos, int32_t T, int32_t B, int64_t max_S,
+                                int32_t n_heads, int32_t head_dim, float* scores,
+                                int64_t ld_scores, void* stream) {
+    const char* fn = "dsa_indexer_scores";
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    if (T == 0) return ok();
+    dsa_status_t st = check_indexer(fn, q_idx, w, keys, kv_off, q_req, q_pos, T, B, max_S,
+                                    n_heads, head_dim);
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(scores, DSA_ERR_INVALID_ARG, "%s: scores is null", fn);
+    DSA_REQUIRE(aligned(scores, 4), DSA_ERR_INVALID_ARG, "%s: scores must be 4-byte aligned", fn);
+    DSA_REQUIRE(ld_scores >= max_S, DSA_ERR_INVALID_ARG, "%s: ld_scores=%lld < max_S=%lld", fn,
+                static_cast<long long>(ld_scores), static_cast<long long>(max_S));
+    return from_hip(dsa::launch_indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, T, B,
+                                               max_S, scores, ld_scores,
+                                               static_cast<hipStream_t>(stream)), fn);
+}
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int32_t T,
+                      int64_t max_n, int32_t topk, int32_t* ids, void* stream) {
+    const char* fn = "dsa_topk";
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    DSA_REQUIRE(topk == DSA_TOPK, DSA_ERR_UNSUPPORTED, "%s: topk=%d unsupported (only %d)", fn,
+                topk, DSA_TOPK);
+    if (T == 0) return ok();
+    DSA_REQUIRE(scores && n_valid && ids, DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+    DSA_REQUIRE(max_n >= 0 && max_n <= INT32_MAX, DSA_ERR_INVALID_ARG,
+                "%s: max_n=%lld must be in [0, 2^31-1]", fn, static_cast<long long>(max_n));
+    DSA_REQUIRE(ld >= max_n && ld >= 1, DSA_ERR_INVALID_ARG, "%s: ld=%lld < max_n=%lld", fn,
+                static_cast<long long>(ld), static_cast<long long>(max_n));
+    DSA_REQUIRE(aligned(scores, 4) && aligned(n_valid, 4) && aligned(ids, 4),
+                DSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    return from_hip(dsa::launch_topk(scores, ld, n_valid, nullptr, nullptr, nullptr, T, max_n,
+                                     ids, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t dsa_indexer_topk_workspace_size(int32_t T, int64_t max_S) {
+    if (T <= 0 || max_S <= 0) return 0;
+    return round_up(static_cast<size_t>(T) * static_cast<size_t>(max_S) * sizeof(float));
+}
+
+dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
+                              const int64_t* kv_off, const int32_t* q_req,
+                              const int32_t* q_pos, int32_t T, int32_t B, int64_t max_S,
+                              int32_t n_heads, int32_t head_dim, int32_t topk, int32_t* ids,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "dsa_indexer_topk";
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    DSA_REQUIRE(topk == DSA_TOPK, DSA_ERR_UNSUPPORTED, "%s: topk=%d unsupported (only %d)", fn,
+                topk, DSA_TOPK);
+    if (T == 0) return ok();
+    dsa_status_t st = check_indexer(fn, q_idx, w, keys, kv_off, q_req, q_pos, T, B, max_S,
+                                    n_heads, head_dim);
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(ids && aligned(ids, 4), DSA_ERR_INVALID_ARG, "%s: ids null or misaligned", fn);
+    const size_t need = dsa_indexer_topk_workspace_size(T, max_S);
+    DSA_REQUIRE(workspace && aligned(workspace, kAlign), DSA_ERR_WORKSPACE,
+                "%s: workspace null or not %zu-byte aligned", fn, kAlign);
+    DSA_REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE,
+                "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* scores = static_cast<float*>(workspace);
+    hipError_t e = dsa::launch_indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, T, B, max_S,
+                                              scores, max_S, s);
+    if (e != hipSuccess) return from_hip(e, fn);
+    return from_hip(dsa::launch_topk(scores, max_S, nullptr, kv_off, q_req, q_pos, T, max_S, ids, s),
+                    fn);
+}
+
+size_t dsa_sparse_mla_workspace_size(int32_t T, int32_t n_heads, int32_t topk) {
+    if (T <= 0 || n_heads != DSA_MLA_HEADS || topk != DSA_TOPK) return 0;
+    return round_up(dsa::sparse_mla_workspace_bytes(T));
+}
+
+dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int64_t ld_latent,
+                                 const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
+                                 const int32_t* q_req, const int32_t* ids, int32_t T,
+                                 int32_t B, int32_t n_heads, int32_t topk, float scale,
+                                 uint16_t* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    const char* fn = "dsa_sparse_mla_attn";
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    DSA_REQUIRE(n_heads == DSA_MLA_HEADS, DSA_ERR_UNSUPPORTED,
+                "%s: n_heads=%d unsupported (only %d)", fn, n_heads, DSA_MLA_HEADS);
+    DSA_REQUIRE(topk == DSA_TOPK, DSA_ERR_UNSUPPORTED, "%s: topk=%d unsupported (only %d)", fn,
+                topk, DSA_TOPK);
+    if (T == 0) return ok();
+    DSA_REQUIRE(B >= 1, DSA_ERR_INVALID_ARG, "%s: B=%d must be >= 1", fn, B);
+    DSA_REQUIRE(std::isfinite(scale), DSA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    DSA_REQUIRE(q && latent && kpe && kv_off && q_req && ids && out, DSA_ERR_INVALID_ARG,
+                "%s: null pointer", fn);
+    DSA_REQUIRE(aligned(q, 16) && aligned(latent, 16) && aligned(kpe, 16) && aligned(out, 16),
+                DSA_ERR_INVALID_ARG, "%s: q, latent, kpe and out must be 16-byte aligned", fn);
+    DSA_REQUIRE(aligned(kv_off, 8) && aligned(q_req, 4) && aligned(ids, 4) &&
+                    (lse == nullptr || aligned(lse, 4)),
+                DSA_ERR_INVALID_ARG, "%s: misaligned kv_off/q_req/ids/lse", fn);
+    DSA_REQUIRE(ld_latent >= DSA_LATENT_DIM && ld_latent % 8 == 0, DSA_ERR_INVALID_ARG,
+                "%s: ld_latent=%lld must be >= 512 and a multiple of 8", fn,
+                static_cast<long long>(ld_latent));
+    DSA_REQUIRE(ld_kpe >= DSA_COMPANION_DIM && ld_kpe % 8 == 0, DSA_ERR_INVALID_ARG,
+                "%s: ld_kpe=%lld must be >= 64 and a multiple of 8", fn,
+                static_cast<long long>(ld_kpe));
+    const size_t need = dsa_sparse_mla_workspace_size(T, n_heads, topk);
+    if (need > 0) {
+        DSA_REQUIRE(workspace && aligned(workspace, kAlign), DSA_ERR_WORKSPACE,
+                    "%s: workspace null or not %zu-byte aligned", fn, kAlign);
+        DSA_REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE,
+                    "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+    }
+    return from_hip(dsa::launch_sparse_mla(q, latent, ld_latent, kpe, ld_kpe, kv_off, q_req, ids,
+                                           T, scale, out, lse, workspace,
+                                           static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

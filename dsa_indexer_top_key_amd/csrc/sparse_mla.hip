@@ -1,0 +1,427 @@
+// Stage 4: absorbed-MLA read restricted to the selected positions I_t.
+//
+// Page "Kimi K3.1 Pro: Sparse-Zugriffe, keine kleinere Historie", section "Die Mathematik
+// der Sparse Attention und ihrer fehlenden Masse": for each main-attention head the read is
+// a softmax over the logits a_tj restricted to j in I_t; the notation abstracts absorbed
+// MLA projections (per-head K/V are never materialised).  Section "Warum Top-2048 ..." (last
+// paragraphs) and the Gated-MLA paragraph: all 96 heads share one 512-wide latent, with a
+// 64-wide companion key component beside it and no rotation (skip_rope).
+//
+//   a_thj = scale * q_th . [c_j ; kpe_j]     (576 dims)
+//   o_th  = sum_j softmax_j(a_thj) c_j        (512 dims, j in I_t)
+//
+// Work per query: 2048 gathered rows of 1152 B, 96 x 2048 x (576 + 512) MACs.
+//
+// Block = 4 waves for one (query, split of the ID row).  Waves 0..2 each own 32 heads:
+// their 32 x 576 absorbed queries live in registers for the whole block, as the B operand
+// of  S^T = C . Q^T  (v_mfma_f32_32x32x16_bf16, M = 32 gathered rows, N = 32 heads), which
+// leaves each lane with one head and 16 rows -- exactly the A-operand layout the P . V
+// product needs, so probabilities never leave registers.  The 32 x 512 output of a head
+// group accumulates in registers across the split.  Wave 3 gathers the selected rows
+// (coalesced 16-byte loads of whole 1152-byte rows) into a three-deep LDS ring, two tiles
+// ahead of the consumers.  The V operand of P . V (rows x latent dims) is read from the
+// row-major LDS tile with the gfx950 transposing load ds_read_b64_tr_b16.
+//
+// Softmax (fp32, log2 domain) uses a fixed per-head reference: the maximum logit of the
+// first tile.  Later probabilities p = 2^(x - ref) may exceed 1; that is exact after the
+// final division by the sum, and fp32/bf16 keep full relative precision while p <= 2^32.
+// If any logit exceeds its reference by more than 32 (never for sane data), the split is
+// recomputed once with the exact per-head maximum recorded during the first pass, so no
+// accumulator is ever rescaled in the hot loop (which would not fit the register budget:
+// the 32 x 480 accumulators of a head group already fill the 240 AGPRs it owns).
+// Splits write normalised fp32 partials and a log2-sum-exp; a small kernel merges them.  A
+// block maps to an XCD chosen by its query, so all splits of a query share one L2.
+#include "common.h"
+
+namespace dsa {
+
+constexpr int kTile = 32;            // gathered rows per step
+constexpr int kRowStride = kQK + 8;  // padded LDS row, bf16 elements (1168 B)
+constexpr int kNBuf = 3;             // LDS ring depth
+constexpr int kChunksPerRow = kQK / 8;                      // 72 x 16 B
+constexpr float kLn2 = 0.69314718055994531f;
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+constexpr int kNTiles = kLatent / 32;        // 16 output tiles of 32 latent dims
+constexpr int kConsTiles = kNTiles - 1;       // kept by the head-group waves
+constexpr int kHelpTile = kNTiles - 1;        // computed by the gather wave for all heads
+
+struct MlaSmem {
+    uint16_t c[kNBuf][kTile * kRowStride];   // ring of gathered row tiles
+    int32_t rows[kTopK];                     // compacted request-local IDs of the split
+    u32x4 pfrag[3][64][2];                   // P (bf16) in A-operand layout, per head group
+    float inv_l[kMlaHeads];                  // per-head 1/l at the end
+    uint32_t wcnt[4];
+    uint32_t redo;                           // some logit exceeded its reference by > 2^32
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Gather one tile of rows straight into LDS with gfx950's global_load_lds_dwordx4: each
+// instruction writes 64 consecutive 16-byte LDS slots (lane l -> slot base + l), so the tile
+// buffer is viewed as 32 rows x 73 slots (72 data chunks of a 1152-byte row -- 64 latent +
+// 8 companion -- and one padding slot).  Padding slots and rows past the split's end are
+// not loaded (their lanes are inactive).  The data bypasses registers entirely; completion
+// is tracked with vmcnt by the issuing wave.
+constexpr int kSlotsPerRow = kChunksPerRow + 1;              // 73
+constexpr int kTileSlots = kTile * kSlotsPerRow;             // 2336
+constexpr int kDmaPerTile = (kTileSlots + 63) / 64;          // 37 instructions
+static_assert(kSlotsPerRow * 8 == kRowStride, "LDS row = 73 slots of 16 bytes");
+
+__device__ __forceinline__ void gather_tile(uint16_t* buf, int tile, int n_rows,
+                                            const int32_t* rows, const uint16_t* latent,
+                                            int64_t ld_lat, const uint16_t* kpe, int64_t ld_kpe,
+                                            int64_t base, int lane) {
+    // all row IDs first (LDS reads), then the DMA stream, so the reads do not serialise it
+    int32_t rid[kDmaPerTile];
+#pragma unroll
+    for (int k = 0; k < kDmaPerTile; ++k) {
+        const int sidx = 64 * k + lane;
+        const int slot = tile * kTile + sidx / kSlotsPerRow;
+        rid[k] = (sidx < kTileSlots && slot < n_rows) ? rows[slot] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kDmaPerTile; ++k) {
+        const int sidx = 64 * k + lane;
+        const int cc = sidx - (sidx / kSlotsPerRow) * kSlotsPerRow;
+        if (rid[k] >= 0 && cc < kChunksPerRow) {
+            const int64_t row = base + rid[k];
+            const uint16_t* src = cc < 64 ? latent + row * ld_lat + 8 * cc
+                                          : kpe + row * ld_kpe + 8 * (cc - 64);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 64 * 8 * k), 16, 0, 0);
+        }
+    }
+}
+
+// Wait until at most n of this wave's vector-memory operations are outstanding
+// (s_waitcnt vmcnt(n) with expcnt/lgkmcnt left at their maxima; n <= 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// V operand of P . V for latent tile nt and K-chunk c (rows 16c .. 16c+15 of the tile).
+// Lane l needs latent column 32 nt + (l % 32) at rows 16c + 4hh + {0..3} and
+// 16c + 8 + 4hh + {0..3} (hh = l / 32), matching the P fragment's row order.  Within each
+// 16-lane group, lane q points at row q/4, columns 4(q%4)..4(q%4)+3 of a 4 x 16 block; the
+// transposing load returns column q of the block's four rows.
+__device__ __forceinline__ bf16x8 v_fragment(const uint16_t* vbase, int nt, int c) {
+    const uint16_t* vp = vbase + 16 * c * kRowStride + 32 * nt;
+    const bf16x4 v0 = lds_read_tr16(vp);
+    const bf16x4 v1 = lds_read_tr16(vp + 8 * kRowStride);
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t ld_lat,
+    const uint16_t* __restrict__ kpe, int64_t ld_kpe, const int64_t* __restrict__ kv_off,
+    const int32_t* __restrict__ q_req, const int32_t* __restrict__ ids, int32_t T,
+    int32_t nsplit, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    __shared__ MlaSmem sm;
+    const int g = blockIdx.x;
+    const int j = g >> 3;
+    const int t = (g & 7) + 8 * (j / nsplit);
+    const int split = j - (j / nsplit) * nsplit;
+    if (t >= T) return;
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int hh = lane >> 5;  // lane half
+    const int hl = lane & 31;  // head column (S^T) / A-operand row
+    const int L = kTopK / nsplit;
+    const int b = q_req[t];
+    const int64_t base = kv_off[b];
+    const int64_t s_b = kv_off[b + 1] - base;
+
+    // ---- ordered compaction of this split's valid IDs into sm.rows
+    const int32_t* idr = ids + static_cast<int64_t>(t) * kTopK + static_cast<int64_t>(split) * L;
+    if (tid == 0) sm.redo = 0;
+    // rows past the end of a split are never loaded: start from a zeroed ring so the masked
+    // rows of a partial tile hold finite values (their probabilities are exactly 0)
+    for (int i = tid; i < kNBuf * kTile * kRowStride / 8; i += 256)
+        reinterpret_cast<u32x4*>(&sm.c[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+    int n_rows = 0;
+    for (int i0 = 0; i0 < L; i0 += 256) {
+        const int i = i0 + tid;
+        const int32_t id = i < L ? idr[i] : -1;
+        const bool ok = id >= 0 && static_cast<int64_t>(id) < s_b;
+        const uint64_t m = __ballot(ok);
+        if (lane == 0) sm.wcnt[wave] = __popcll(m);
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) {
+            before += wv < wave ? sm.wcnt[wv] : 0u;
+            total += sm.wcnt[wv];
+        }
+        if (ok) sm.rows[n_rows + before + __popcll(m & ((1ull << lane) - 1ull))] = id;
+        n_rows += total;
+        __syncthreads();
+    }
+    const int n_tiles = (n_rows + kTile - 1) / kTile;
+    const int q16 = lane & 15;
+    const int vrow = 4 * hh + (q16 >> 2);
+    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
+    const int64_t ps = static_cast<int64_t>(t) * nsplit + split;
+
+    // Per step i there are two barriers: A_i (tile i is in ring slot i%3) and B_i (the head
+    // groups have published P of tile i).  A second pass (rare) repeats the whole sequence.
+    if (wave == 3) {
+        // ================= gather wave: ring producer + last latent tile of every head
+        f32x16 orest[3];
+        for (int pass = 0; pass < 2; ++pass) {
+            orest[0] = f32x16{};
+            orest[1] = f32x16{};
+            orest[2] = f32x16{};
+            if (n_tiles > 0) gather_tile(sm.c[0], 0, n_rows, sm.rows, latent, ld_lat, kpe, ld_kpe, base, lane);
+            if (n_tiles > 1) gather_tile(sm.c[1], 1, n_rows, sm.rows, latent, ld_lat, kpe, ld_kpe, base, lane);
+            wait_vmcnt<0>();
+            __syncthreads();  // A_0
+            for (int i = 0; i < n_tiles; ++i) {
+                __syncthreads();  // B_i
+                const uint16_t* vbase = sm.c[i % kNBuf] + vrow * kRowStride + vcol;
+                const bf16x8 v0 = v_fragment(vbase, kHelpTile, 0);
+                const bf16x8 v1 = v_fragment(vbase, kHelpTile, 1);
+#pragma unroll
+                for (int hg = 0; hg < 3; ++hg) {
+                    orest[hg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][0]), v0, orest[hg], 0, 0, 0);
+                    orest[hg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][1]), v1, orest[hg], 0, 0, 0);
+                }
+                // tile i+2 -> ring slot (i+2)%3 (last read in step i-1); tile i+1, issued one
+                // step earlier, must have landed before A_{i+1} publishes it
+                if (i + 2 < n_tiles) {
+                    gather_tile(sm.c[(i + 2) % kNBuf], i + 2, n_rows, sm.rows, latent, ld_lat, kpe, ld_kpe, base, lane);
+                    wait_vmcnt<kDmaPerTile>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                __syncthreads();  // A_{i+1}
+            }
+            if (pass == 0) {
+                __syncthreads();  // E: the head groups have published their overflow flags
+                if (sm.redo == 0) break;
+            }
+        }
+        __syncthreads();  // the head groups have published 1/l
+#pragma unroll
+        for (int hg = 0; hg < 3; ++hg)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hd = 32 * hg + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float v = orest[hg][r] * sm.inv_l[hd];
+                const int col = 32 * kHelpTile + hl;
+                if (nsplit == 1)
+                    out[(static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + col] = f32_to_bf16(v);
+                else
+                    part_o[(ps * kMlaHeads + hd) * kLatent + col] = v;
+            }
+        return;
+    }
+
+    // ================= head-group waves: heads 32*wave .. 32*wave+31
+    u32x4 qf[kQK / 16];  // 36 K-steps; lane half hh covers dims [288 hh, 288 hh + 288)
+    {
+        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK + 288 * hh;
+#pragma unroll
+        for (int s = 0; s < kQK / 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qh + 8 * s);
+    }
+    f32x16 o[kConsTiles];
+    float m_ref = -INFINITY;   // reference logit of this lane's head (log2 domain)
+    float m_seen = -INFINITY;  // largest logit seen (exact maximum after a full pass)
+    float l_run = 0.f;         // this lane's partial sum of 2^(x - m_ref) over its rows
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int nt = 0; nt < kConsTiles; ++nt) o[nt] = f32x16{};
+        l_run = 0.f;
+        bool overflow = false;
+        __syncthreads();  // A_0
+        for (int i = 0; i < n_tiles; ++i) {
+            const uint16_t* buf = sm.c[i % kNBuf];
+            // ---- S^T tile (32 rows x 32 heads): A = gathered rows from LDS, B = q registers.
+            f32x16 sacc = {};
+            const uint16_t* arow = buf + hl * kRowStride + 288 * hh;
+            u32x4 a0 = *reinterpret_cast<const u32x4*>(arow);
+#pragma unroll
+            for (int s = 0; s < kQK / 16; ++s) {
+                u32x4 a1 = a0;
+                if (s + 1 < kQK / 16) a1 = *reinterpret_cast<const u32x4*>(arow + 8 * (s + 1));
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[s]), sacc, 0, 0, 0);
+                a0 = a1;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // ---- probabilities relative to the fixed per-head reference
+            const int valid_rows = n_rows - i * kTile;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+                sacc[r] = row < valid_rows ? sacc[r] * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sacc[r]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            m_seen = fmaxf(m_seen, mx);
+            if (m_ref == -INFINITY) m_ref = mx;  // first tile of pass 0 (uniform per head)
+            overflow |= mx > m_ref + 32.f;
+            const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+            float psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] = exp2f(sacc[r] - m_use);
+                psum += sacc[r];
+            }
+            l_run += psum;
+            u32x4 pa0, pa1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                pa0[k] = pack_bf16x2(sacc[2 * k], sacc[2 * k + 1]);
+                pa1[k] = pack_bf16x2(sacc[8 + 2 * k], sacc[8 + 2 * k + 1]);
+            }
+            sm.pfrag[wave][lane][0] = pa0;
+            sm.pfrag[wave][lane][1] = pa1;
+            __syncthreads();  // B_i
+            // ---- O += P . V over this wave's 15 latent tiles
+            const uint16_t* vbase = buf + vrow * kRowStride + vcol;
+            bf16x8 v0 = v_fragment(vbase, 0, 0);
+#pragma unroll
+            for (int step = 0; step < 2 * kConsTiles; ++step) {
+                bf16x8 v1 = v0;
+                if (step + 1 < 2 * kConsTiles) v1 = v_fragment(vbase, (step + 1) >> 1, (step + 1) & 1);
+                o[step >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((step & 1) ? pa1 : pa0), v0, o[step >> 1], 0, 0, 0);
+                v0 = v1;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();  // A_{i+1}
+        }
+        if (pass == 0) {
+            if (__ballot(overflow) && lane == 0) sm.redo = 1;
+            __syncthreads();  // E
+            if (sm.redo == 0) break;
+            m_ref = m_seen;  // second pass: the exact maximum, so every p <= 1
+        }
+    }
+    // ---- epilogue: rows of O are heads 8(r/4) + 4hh + r%4 of this group
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse2 = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;
+    const int head0 = 32 * wave;
+    if (hh == 0) {
+        sm.inv_l[head0 + hl] = inv;
+        if (nsplit == 1) {
+            if (lse) lse[static_cast<int64_t>(t) * kMlaHeads + head0 + hl] = lse2 * kLn2;
+        } else {
+            part_lse[ps * kMlaHeads + head0 + hl] = lse2;
+        }
+    }
+    __syncthreads();  // publish 1/l to the gather wave
+    float ir[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ir[r] = __shfl(inv, 8 * (r >> 2) + 4 * hh + (r & 3));
+    if (nsplit == 1) {
+        uint16_t* ot = out + static_cast<int64_t>(t) * kMlaHeads * kLatent;
+#pragma unroll
+        for (int nt = 0; nt < kConsTiles; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hd = head0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                ot[hd * kLatent + 32 * nt + hl] = f32_to_bf16(o[nt][r] * ir[r]);
+            }
+    } else {
+        float* po = part_o + ps * kMlaHeads * kLatent;
+#pragma unroll
+        for (int nt = 0; nt < kConsTiles; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hd = head0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                po[hd * kLatent + 32 * nt + hl] = o[nt][r] * ir[r];
+            }
+    }
+}
+
+// Merge split partials: one wave per (query, head), 8 latent dims per lane.
+__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse,
+                                                          int32_t T, int32_t nsplit,
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+    const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (pair >= static_cast<int64_t>(T) * kMlaHeads) return;
+    const int t = static_cast<int>(pair / kMlaHeads), hd = static_cast<int>(pair % kMlaHeads);
+    const int lane = lane_id();
+    float m = -INFINITY;
+    for (int s = 0; s < nsplit; ++s)
+        m = fmaxf(m, part_lse[(static_cast<int64_t>(t) * nsplit + s) * kMlaHeads + hd]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+        for (int s = 0; s < nsplit; ++s) {
+            const int64_t ps = static_cast<int64_t>(t) * nsplit + s;
+            const float ls = part_lse[ps * kMlaHeads + hd];
+            if (ls == -INFINITY) continue;
+            const float wgt = exp2f(ls - m);
+            wsum += wgt;
+            const float4* src = reinterpret_cast<const float4*>(part_o + (ps * kMlaHeads + hd) * kLatent + 8 * lane);
+            const float4 a = src[0], bq = src[1];
+            acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
+            acc[4] += wgt * bq.x; acc[5] += wgt * bq.y; acc[6] += wgt * bq.z; acc[7] += wgt * bq.w;
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    u32x4 o;
+    o[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    o[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    o[2] = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+    o[3] = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+    *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + 8 * lane) = o;
+    if (lse && lane == 0)
+        lse[static_cast<int64_t>(t) * kMlaHeads + hd] = wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+int sparse_mla_nsplit(int32_t T) {
+    int ns = 1;
+    while (ns < 16 && static_cast<int64_t>(T) * ns < 256) ns *= 2;
+    return ns;
+}
+
+size_t sparse_mla_workspace_bytes(int32_t T) {
+    const int ns = sparse_mla_nsplit(T);
+    if (ns == 1 || T <= 0) return 0;
+    const size_t parts = static_cast<size_t>(T) * ns;
+    const size_t o_bytes = parts * kMlaHeads * kLatent * sizeof(float);
+    const size_t l_bytes = parts * kMlaHeads * sizeof(float);
+    return o_bytes + ((l_bytes + 255) & ~static_cast<size_t>(255));
+}
+
+hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t ld_lat,
+                             const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
+                             const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
+                             uint16_t* out, float* lse, void* workspace, hipStream_t stream) {
+    const int ns = sparse_mla_nsplit(T);
+    const int64_t groups = (static_cast<int64_t>(T) + 7) / 8;
+    const int64_t blocks = groups * 8 * ns;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    float* part_o = nullptr;
+    float* part_lse = nullptr;
+    if (ns > 1) {
+        part_o = static_cast<float*>(workspace);
+        part_lse = part_o + static_cast<size_t>(T) * ns * kMlaHeads * kLatent;
+    }
+    const float scale_log2 = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL(sparse_mla_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, ns,
+                       scale_log2, out, lse, part_o, part_lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ns == 1) return e;
+    const int64_t cblocks = (static_cast<int64_t>(T) * kMlaHeads + 3) / 4;
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(static_cast<unsigned>(cblocks)), dim3(256), 0,
+                       stream, part_o, part_lse, T, ns, out, lse);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

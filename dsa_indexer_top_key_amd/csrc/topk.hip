@@ -1,0 +1,363 @@
+// Stage 3: per-row top-2048 selection -> request-local position IDs, ascending, -1 padded.
+//
+// Page "Kimi K3.1 Pro: Sparse-Zugriffe, keine kleinere Historie", section "Eine Query durch
+// den Indexer verfolgen": up to 2048 causal candidates per query, a logical [T,2048]
+// position-ID array, short prefixes and invalid entries handled by the backend; section
+// "Die Mathematik der Sparse Attention ...": I_t holds the up-to-2048 highest-scoring
+// positions.  Tie rule (the page is silent): equal scores go to the lower position, -0 ==
+// +0, NaN ranks lowest -- so the selected set, and the ascending ID row, are unique.
+//
+// One 1024-thread block per row.  Scores become order-preserving u32 keys (0 is reserved
+// for "no element"), kept in registers (E per thread, position e*1024 + tid) when the row
+// fits, re-streamed from global memory per pass otherwise.  Selection is a radix-style
+// threshold search on an LDS histogram of 2048 bins:
+//   level 0  bins linear in the score value between the row's finite min and max (a
+//            monotone map, so whole bins are above / below the threshold; spreading the
+//            bulk of the row over many bins keeps LDS atomic conflicts low),
+//   level 1+ exact bins on the key bits inside the threshold bin's key range (11 bits per
+//            level) until the threshold bin is taken whole or holds a single key value.
+// The threshold bin of a level is found with a block-wide scan over the histogram.  The
+// final compaction is an ordered scan (wave ballot + mbcnt within a wave, an LDS scan of the
+// per-(element, wave) counts across the block) that writes the selected positions in
+// ascending order; ties at the threshold key are ranked by position with the same scan.
+#include "common.h"
+
+namespace dsa {
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kBins = 2048;
+constexpr int kBinBits = 11;
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // key of -inf
+constexpr uint32_t kKeyPosInf = 0xFF800000u;  // key of +inf
+
+// Order-preserving key: larger score -> larger key; -0 and +0 share a key; every NaN maps
+// to 1 (below -inf); 0 is never produced (it marks an absent element).
+__device__ __forceinline__ uint32_t score_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Value-linear bin of a key (monotone non-decreasing in the key).
+__device__ __forceinline__ int value_bin(uint32_t k, float lo, float scale) {
+    if (k <= kKeyNegInf) return 0;
+    if (k >= kKeyPosInf) return kBins - 1;
+    const float f = (key_to_score(k) - lo) * scale;
+    return f < static_cast<float>(kBins) ? static_cast<int>(f) : kBins - 1;
+}
+
+__device__ __forceinline__ int shift_for(uint32_t span) {
+    const int bits = span ? 32 - __clz(span) : 0;
+    return bits > kBinBits ? bits - kBinBits : 0;
+}
+
+struct TopkSmem {
+    uint32_t hist[kBins];
+    uint32_t cnt[kTopkThreads];
+    uint32_t wtot[kTopkWaves];
+    uint32_t red[4][kTopkWaves];
+    uint32_t prm[8];
+};
+
+// Exclusive prefix sum over the block (thread order); returns this thread's exclusive sum
+// and writes the block total to *total (all threads).  Contains barriers.
+__device__ __forceinline__ uint32_t block_exclusive_scan(TopkSmem& sm, uint32_t v,
+                                                         uint32_t* total) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t incl = wave_inclusive_scan(v);
+    if (lane == 63) sm.wtot[wave] = incl;
+    __syncthreads();
+    uint32_t wbase = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) {
+        const uint32_t x = sm.wtot[i];
+        wbase += (i < wave) ? x : 0u;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return wbase + incl - v;
+}
+
+// Find the bin b* holding the need-th largest candidate: count(bins > b*) < need <=
+// count(bins >= b*).  Writes b* to prm[0] and count(bins > b*) to prm[1].
+__device__ __forceinline__ void find_threshold_bin(TopkSmem& sm, uint32_t need) {
+    const int tid = threadIdx.x;
+    const int hb = kBins - 1 - 2 * tid, lb = hb - 1;
+    const uint32_t ch = sm.hist[hb], cl = sm.hist[lb];
+    if (tid == 0) {
+        sm.prm[0] = 0;
+        sm.prm[1] = 0;
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan(sm, ch + cl, &total);
+    if (before < need && before + ch >= need) {
+        sm.prm[0] = hb;
+        sm.prm[1] = before;
+    } else if (before + ch < need && before + ch + cl >= need) {
+        sm.prm[0] = lb;
+        sm.prm[1] = before + ch;
+    }
+    __syncthreads();
+}
+
+// Block-wide min/max of up to four u32 values (results broadcast to all threads).
+__device__ __forceinline__ void block_minmax(TopkSmem& sm, uint32_t& a_min, uint32_t& a_max,
+                                             uint32_t& b_min, uint32_t& b_max) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    a_min = wave_min_u32(a_min);
+    a_max = wave_max_u32(a_max);
+    b_min = wave_min_u32(b_min);
+    b_max = wave_max_u32(b_max);
+    if (lane == 0) {
+        sm.red[0][wave] = a_min;
+        sm.red[1][wave] = a_max;
+        sm.red[2][wave] = b_min;
+        sm.red[3][wave] = b_max;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) {
+        a_min = min(a_min, sm.red[0][i]);
+        a_max = max(a_max, sm.red[1][i]);
+        b_min = min(b_min, sm.red[2][i]);
+        b_max = max(b_max, sm.red[3][i]);
+    }
+    __syncthreads();
+}
+
+template <int E, bool STREAM>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
+    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
+    const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids) {
+    static_assert(E * kTopkWaves <= kTopkThreads, "per-(element, wave) counts must fit");
+    __shared__ TopkSmem sm;
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = lane_id(), wave = tid >> 6;
+
+    int64_t n;
+    if (n_valid) {
+        n = n_valid[t];
+    } else {
+        const int b = q_req[t];
+        const int64_t s_b = kv_off[b + 1] - kv_off[b];
+        n = static_cast<int64_t>(q_pos[t]) + 1;
+        n = n < s_b ? n : s_b;
+    }
+    n = n < max_n ? n : max_n;
+    n = n > 0 ? n : 0;
+    int32_t* out = ids + static_cast<int64_t>(t) * kTopK;
+    if (n <= kTopK) {
+        for (int i = tid; i < kTopK; i += kTopkThreads) out[i] = i < n ? i : -1;
+        return;
+    }
+    const float* row = scores + static_cast<int64_t>(t) * ld;
+    constexpr int64_t kChunk = static_cast<int64_t>(kTopkThreads) * E;
+    const int n_chunks = STREAM ? static_cast<int>((n + kChunk - 1) / kChunk) : 1;
+    uint32_t key[E];
+    auto load = [&](int ch) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int64_t p = ch * kChunk + static_cast<int64_t>(e) * kTopkThreads + tid;
+            key[e] = p < n ? score_key(row[p]) : 0u;
+        }
+    };
+    if (!STREAM) load(0);
+
+    // ---- row statistics: range of finite keys and of all keys
+    uint32_t fmin = ~0u, fmax = 0u, amin = ~0u, amax = 0u;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+        if (STREAM) load(ch);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t k = key[e];
+            if (k) {
+                amin = min(amin, k);
+                amax = max(amax, k);
+                if (k > kKeyNegInf && k < kKeyPosInf) {
+                    fmin = min(fmin, k);
+                    fmax = max(fmax, k);
+                }
+            }
+        }
+    }
+    block_minmax(sm, fmin, fmax, amin, amax);
+
+    bool value_mode = false;
+    float lo = 0.f, scale = 0.f;
+    if (fmin < fmax) {
+        lo = key_to_score(fmin);
+        const float span = key_to_score(fmax) - lo;
+        scale = static_cast<float>(kBins) / span;
+        value_mode = isfinite(scale) && scale > 0.f;
+    }
+
+    uint32_t rlo = amin, rhi = amax;  // candidate key range (inclusive)
+    uint32_t need = kTopK;            // candidates still to take
+    uint32_t cand;                    // candidates in the current range
+
+    // ---- level 0
+    {
+        const int sh = value_mode ? 0 : shift_for(rhi - rlo);
+        for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+        __syncthreads();
+        for (int ch = 0; ch < n_chunks; ++ch) {
+            if (STREAM) load(ch);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t k = key[e];
+                if (k) atomicAdd(&sm.hist[value_mode ? value_bin(k, lo, scale) : static_cast<int>((k - rlo) >> sh)], 1u);
+            }
+        }
+        __syncthreads();
+        find_threshold_bin(sm, need);
+        const uint32_t bstar = sm.prm[0];
+        need -= sm.prm[1];
+        cand = sm.hist[bstar];
+        if (value_mode) {
+            uint32_t mn = ~0u, mx = 0u, d0 = ~0u, d1 = 0u;
+            for (int ch = 0; ch < n_chunks; ++ch) {
+                if (STREAM) load(ch);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const uint32_t k = key[e];
+                    if (k && value_bin(k, lo, scale) == static_cast<int>(bstar)) {
+                        mn = min(mn, k);
+                        mx = max(mx, k);
+                    }
+                }
+            }
+            block_minmax(sm, mn, mx, d0, d1);
+            rlo = mn;
+            rhi = mx;
+        } else {
+            const uint64_t nlo = static_cast<uint64_t>(rlo) + (static_cast<uint64_t>(bstar) << sh);
+            const uint64_t nhi = nlo + ((1ull << sh) - 1);
+            rlo = static_cast<uint32_t>(nlo);
+            rhi = nhi < rhi ? static_cast<uint32_t>(nhi) : rhi;
+            __syncthreads();
+        }
+    }
+
+    // ---- refinement levels on the key bits (each level narrows the range by 2^11, so three
+    // levels always reach a single key; the bound only guards against a broken invariant)
+    for (int level = 0; level < 4 && cand != need && rlo != rhi; ++level) {
+        const int sh = shift_for(rhi - rlo);
+        for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+        __syncthreads();
+        for (int ch = 0; ch < n_chunks; ++ch) {
+            if (STREAM) load(ch);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t k = key[e];
+                if (k >= rlo && k <= rhi) atomicAdd(&sm.hist[(k - rlo) >> sh], 1u);
+            }
+        }
+        __syncthreads();
+        find_threshold_bin(sm, need);
+        const uint32_t bstar = sm.prm[0];
+        need -= sm.prm[1];
+        cand = sm.hist[bstar];
+        const uint64_t nlo = static_cast<uint64_t>(rlo) + (static_cast<uint64_t>(bstar) << sh);
+        const uint64_t nhi = nlo + ((1ull << sh) - 1);
+        rlo = static_cast<uint32_t>(nlo);
+        rhi = nhi < rhi ? static_cast<uint32_t>(nhi) : rhi;
+        __syncthreads();
+    }
+
+    // ---- ordered compaction.  Selected: every key above the range, plus either the whole
+    // range (cand == need) or, when the range is the single key rlo, its `need` lowest
+    // positions.
+    const bool take_all = (cand == need);
+    const uint32_t thr = rlo;
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t tie_base = 0, out_base = 0;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+        if (STREAM) load(ch);
+        uint64_t tie_ok64 = 0;  // bit e: element e is a tie at the threshold that is kept
+        if (!take_all) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint64_t m = __ballot(key[e] == thr);
+                if (lane == 0) sm.cnt[e * kTopkWaves + wave] = __popcll(m);
+            }
+            __syncthreads();
+            const uint32_t v = tid < E * kTopkWaves ? sm.cnt[tid] : 0u;
+            uint32_t total;
+            const uint32_t ex = block_exclusive_scan(sm, v, &total);
+            if (tid < E * kTopkWaves) sm.cnt[tid] = ex;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint64_t m = __ballot(key[e] == thr);
+                const uint32_t rank = tie_base + sm.cnt[e * kTopkWaves + wave] + __popcll(m & below);
+                if (key[e] == thr && rank < need) tie_ok64 |= 1ull << e;
+            }
+            tie_base += total;
+            __syncthreads();
+        }
+        auto selected = [&](int e) -> bool {
+            const uint32_t k = key[e];
+            if (take_all) return k >= thr;
+            return k > thr || ((tie_ok64 >> e) & 1ull);
+        };
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint64_t m = __ballot(selected(e));
+            if (lane == 0) sm.cnt[e * kTopkWaves + wave] = __popcll(m);
+        }
+        __syncthreads();
+        const uint32_t v = tid < E * kTopkWaves ? sm.cnt[tid] : 0u;
+        uint32_t total;
+        const uint32_t ex = block_exclusive_scan(sm, v, &total);
+        if (tid < E * kTopkWaves) sm.cnt[tid] = ex;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool s = selected(e);
+            const uint64_t m = __ballot(s);
+            const uint32_t rank = out_base + sm.cnt[e * kTopkWaves + wave] + __popcll(m & below);
+            if (s && rank < kTopK)
+                out[rank] = static_cast<int32_t>(ch * kChunk + static_cast<int64_t>(e) * kTopkThreads + tid);
+        }
+        out_base += total;
+        __syncthreads();
+    }
+}
+
+template <int E, bool STREAM>
+static void launch_topk_e(const float* scores, int64_t ld, const int32_t* n_valid,
+                          const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
+                          int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream) {
+    hipLaunchKernelGGL((topk_kernel<E, STREAM>), dim3(T), dim3(kTopkThreads), 0, stream, scores,
+                       ld, n_valid, kv_off, q_req, q_pos, max_n, ids);
+}
+
+// Either n_valid (explicit row lengths) or (kv_off, q_req, q_pos) gives each row's length.
+hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
+                       const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
+                       int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream) {
+    if (max_n <= 4 * kTopkThreads)
+        launch_topk_e<4, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
+    else if (max_n <= 8 * kTopkThreads)
+        launch_topk_e<8, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
+    else if (max_n <= 16 * kTopkThreads)
+        launch_topk_e<16, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
+    else if (max_n <= 32 * kTopkThreads)
+        launch_topk_e<32, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
+    else if (max_n <= 64 * kTopkThreads)
+        launch_topk_e<64, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
+    else
+        launch_topk_e<16, true>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

