@@ -1,0 +1,293 @@
+"""Benchmark of the MI355X DSA read path (one GPU).
+
+Headline: decode step = indexer scores + top-2048 (dsa_indexer_topk) followed by the
+restricted-softmax absorbed-MLA read (dsa_sparse_mla_attn), on a batch of 64 requests with
+32768 cached positions each (one query per request), inputs resident in HBM.  Also reported:
+the prefill indexer (indexer + top-k) on a 4096-query chunk at positions 61440..65535 of a
+65536-position request, in TFLOP/s of causal scoring work, and the index-key LayerNorm
+cache fill.  All timings use HIP events on the stream the kernels run on.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+    python bench.py --profile-kernels   # a few launches of each kernel, for rocprofv3
+
+Prints one JSON line (plus nothing else on stdout).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/s + HBM GB/s at S=32K top-2048; prefill indexer TFLOP/s"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+DECODE_WORKLOAD = "decode_b64_s32768"
+PREFILL_WORKLOAD = "prefill_t4096_s65536"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic work (what the method must move / compute; no intermediates)
+# ---------------------------------------------------------------------------------------
+def n_admissible(lay):
+    return np.maximum(0, np.minimum(lay.q_pos.astype(np.int64) + 1, lay.s_len[lay.q_req]))
+
+
+def decode_alg(lay):
+    n = n_admissible(lay)
+    sel = np.minimum(n, 2048)
+    b_idx = 256 * n + 32 * 128 * 2 + 32 * 2          # keys, q_idx, w
+    b_topk = 2048 * 4                               # IDs written
+    b_mla = 1152 * sel + 96 * 576 * 2 + 96 * 512 * 2  # gathered rows, q, out
+    f_idx = 2 * 32 * 128 * n
+    f_mla = (2 * 96 * 576 + 2 * 96 * 512) * sel
+    return {"bytes_indexer": int(b_idx.sum()), "bytes_topk": int(b_topk * lay.T),
+            "bytes_mla": int(b_mla.sum()),
+            "bytes": int((b_idx + b_topk + b_mla).sum()),
+            "flops_indexer": int(f_idx.sum()), "flops_mla": int(f_mla.sum())}
+
+
+def source_digest(name):
+    with open(os.path.join(ROOT, "dsa_indexer_top_key_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, summary_name):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
+    the current source of the kernel (else None)."""
+    path = os.path.join(PROFILES, summary_name)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != source_digest(kernel_file):
+        return None
+    return float(m_b.group(1))
+
+
+# ---------------------------------------------------------------------------------------
+def timed(fn, steps, warmup, stream, torch):
+    """Run fn warmup times, then `steps` times bracketed by events; returns ms per call."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def per_call_events(fn, steps, stream, torch):
+    """Average duration of each call, each bracketed by its own pair of events."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def cpu_baseline(lay, host, n_total, budget_s=12.0):
+    """The oracle (as it stands) on the first queries of the decode batch, cycled until about
+    budget_s seconds of host work; queries/s of indexer scores + top-2048 + sparse read."""
+    from oracle import dsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s or done < 2:
+        t = done % lay.T
+        s = O.indexer_scores(host["q_idx"], host["w"], host["keys"], lay.kv_off, lay.q_req,
+                             lay.q_pos, rows=[t])
+        ids = np.full((lay.T, 2048), -1, np.int32)
+        ids[t] = O.topk_ids(s[0])
+        O.sparse_mla(host["q"], host["latent"], host["kpe"], lay.kv_off, lay.q_req, ids,
+                     1.0 / 192 ** 0.5, rows=[t])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt, 2), "unit": "queries/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"the first {lay.T} of the {n_total} queries of {lay.name} (S=32768 each), "
+                      f"cycled: {done} query evaluations (indexer scores + top-2048 + sparse "
+                      f"read, fp64 numpy) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="launch each kernel a few times (for rocprofv3), print nothing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the DSA read path shards over requests with no "
+              "exchange (see the design notes); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dsa_indexer_top_key_amd as dsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------- decode workload
+    lay = synth.workload(DECODE_WORKLOAD)
+    d = synth.inputs_torch(lay, dev)
+    keys = dsa.index_keys_layernorm(d["raw_keys"], d["gamma"], d["beta"], synth.LN_EPS)
+    ids = torch.empty((lay.T, 2048), dtype=torch.int32, device=dev)
+    ws_idx = torch.empty(dsa.indexer_topk_workspace_size(lay.T, lay.max_s), dtype=torch.uint8,
+                         device=dev)
+    out = torch.empty((lay.T, 96, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((lay.T, 96), dtype=torch.float32, device=dev)
+    ws_mla_n = dsa.sparse_mla_workspace_size(lay.T)
+    ws_mla = torch.empty(max(ws_mla_n, 256), dtype=torch.uint8, device=dev)
+    idx_args = (d["q_idx"], d["w"], keys, d["kv_off"], d["q_req"], d["q_pos"], lay.max_s)
+    scores = ws_idx.view(torch.float32)[: lay.T * lay.max_s].view(lay.T, lay.max_s)
+    n_valid = torch.as_tensor(n_admissible(lay).astype(np.int32), device=dev)
+
+    def step_indexer():
+        dsa.indexer_topk(*idx_args, ids=ids, workspace=ws_idx)
+
+    def step_mla():
+        dsa.sparse_mla_attn(d["q"], d["latent"], d["kpe"], d["kv_off"], d["q_req"], ids,
+                            synth.ATTN_SCALE, out=out, lse=lse, workspace=ws_mla)
+
+    def step():
+        step_indexer()
+        step_mla()
+
+    def scores_only():
+        dsa.indexer_scores(*idx_args, scores=scores)
+
+    def topk_only():
+        dsa.topk(scores, n_valid, ids=ids)
+
+    def ln_fill():
+        dsa.index_keys_layernorm(d["raw_keys"], d["gamma"], d["beta"], synth.LN_EPS, keys=keys)
+
+    if args.profile_kernels:
+        for _ in range(3):
+            step()
+            scores_only()
+            topk_only()
+            ln_fill()
+        torch.cuda.synchronize()
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)  # copy kernel of known size (256 MiB read + 256 MiB written)
+        if not args.no_prefill:
+            play = synth.workload(PREFILL_WORKLOAD)
+            pd = synth.inputs_torch(play, dev, parts=("index", "ln"))
+            pkeys = dsa.index_keys_layernorm(pd["raw_keys"], pd["gamma"], pd["beta"], synth.LN_EPS)
+            for _ in range(2):
+                dsa.indexer_topk(pd["q_idx"], pd["w"], pkeys, pd["kv_off"], pd["q_req"],
+                                 pd["q_pos"], play.max_s)
+        torch.cuda.synchronize()
+        return
+
+    alg = decode_alg(lay)
+    ms_step = timed(step, args.steps, args.warmup, stream, torch)
+    ms_idx = per_call_events(step_indexer, args.steps, stream, torch)
+    ms_mla = per_call_events(step_mla, args.steps, stream, torch)
+    ms_scores = per_call_events(scores_only, args.steps, stream, torch)
+    ms_topk = per_call_events(topk_only, args.steps, stream, torch)
+    ms_ln = per_call_events(ln_fill, max(3, args.steps // 4), stream, torch)
+    qps = lay.T / (ms_step * 1e-3)
+    gbps = alg["bytes"] / (ms_step * 1e-3) / 1e9
+    scores_gbps = alg["bytes_indexer"] / (ms_scores * 1e-3) / 1e9
+    ln_bytes = lay.N * (512 + 256)
+    traffic = measured_traffic("indexer.hip", "indexer_decode_b64_s32768_counters.txt")
+
+    res = {
+        "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs of the stated shapes, generated on the GPU)",
+        "config": {"workload": DECODE_WORKLOAD, "requests": lay.T, "cached_positions": 32768,
+                   "topk": 2048, "index_heads": 32, "mla_heads": 96, "latent": 512,
+                   "companion": 64},
+        "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "alg_bytes_per_step": alg["bytes"],
+        "stages_ms": {"indexer_topk": round(ms_idx, 5), "sparse_mla": round(ms_mla, 5),
+                      "scores_kernel": round(ms_scores, 5), "topk_kernel": round(ms_topk, 5),
+                      "ln_cache_fill": round(ms_ln, 5)},
+        "ln_cache_fill_GBps": round(ln_bytes / (ms_ln * 1e-3) / 1e9, 1),
+        "sparse_mla_tflops": round(alg["flops_mla"] / (ms_mla * 1e-3) / 1e12, 1),
+        "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm",
+                     "achieved": round(scores_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(scores_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+    }
+
+    # ------------------------------------------------------------- prefill indexer
+    if not args.no_prefill:
+        del scores
+        play = synth.workload(PREFILL_WORKLOAD)
+        pd = synth.inputs_torch(play, dev, parts=("index", "ln"))
+        pkeys = dsa.index_keys_layernorm(pd["raw_keys"], pd["gamma"], pd["beta"], synth.LN_EPS)
+        pids = torch.empty((play.T, 2048), dtype=torch.int32, device=dev)
+        pws = torch.empty(dsa.indexer_topk_workspace_size(play.T, play.max_s),
+                          dtype=torch.uint8, device=dev)
+        pargs = (pd["q_idx"], pd["w"], pkeys, pd["kv_off"], pd["q_req"], pd["q_pos"], play.max_s)
+        pscores = pws.view(torch.float32)[: play.T * play.max_s].view(play.T, play.max_s)
+
+        def prefill():
+            dsa.indexer_topk(*pargs, ids=pids, workspace=pws)
+
+        def prefill_scores():
+            dsa.indexer_scores(*pargs, scores=pscores)
+
+        psteps = max(3, args.steps // 4)
+        ms_pf = timed(prefill, psteps, 2, stream, torch)
+        ms_pf_scores = per_call_events(prefill_scores, psteps, stream, torch)
+        pflops = float((n_admissible(play) * 2 * 32 * 128).sum())
+        res["prefill_indexer_tflops"] = round(pflops / (ms_pf * 1e-3) / 1e12, 1)
+        res["prefill_indexer"] = {
+            "workload": PREFILL_WORKLOAD, "ms": round(ms_pf, 4),
+            "tflops_indexer_plus_topk": res["prefill_indexer_tflops"],
+            "tflops_scores_kernel": round(pflops / (ms_pf_scores * 1e-3) / 1e12, 1),
+            "mfma_frac": round(pflops / (ms_pf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del pws, pscores
+
+    # ------------------------------------------------------------- oracle on the host
+    if not args.no_cpu_baseline:
+        from synth import to_bits_np
+        sample_req = list(range(16))
+        lo, hi = int(lay.kv_off[0]), int(lay.kv_off[len(sample_req)])
+        host = {"q_idx": to_bits_np(d["q_idx"][: len(sample_req)]),
+                "w": to_bits_np(d["w"][: len(sample_req)]),
+                "q": to_bits_np(d["q"][: len(sample_req)]),
+                "keys": to_bits_np(keys[lo:hi]),
+                "latent": to_bits_np(d["latent"][lo:hi]), "kpe": to_bits_np(d["kpe"][lo:hi])}
+        sub = synth.decode_layout(lay.name, lay.seed, lay.s_len[: len(sample_req)])
+        res["cpu_baseline"] = cpu_baseline(sub, host, lay.T)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

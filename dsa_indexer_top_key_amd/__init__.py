@@ -53,7 +53,7 @@ _SIGNATURES = {
                           _p], ctypes.c_int),
     "dsa_sparse_mla_workspace_size": ([_i32, _i32, _i32], _sz),
     "dsa_sparse_mla_attn": ([_p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p,
-                             _p, _p, _sz, _p], ctypes.c_int),
+                             _i32, _p, _p, _sz, _p], ctypes.c_int),
 }
 
 
@@ -204,8 +204,10 @@ def sparse_mla_workspace_size(t: int, n_heads: int = MLA_HEADS, k: int = TOPK) -
 
 
 def sparse_mla_attn(q, latent, kpe, kv_off, q_req, ids, scale: float, out=None, lse=None,
-                    workspace=None, stream=None):
-    """Stage 4: restricted-softmax absorbed-MLA read -> (out [T,96,512] bf16, lse [T,96])."""
+                    workspace=None, stream=None, out_dtype=None):
+    """Stage 4: restricted-softmax absorbed-MLA read -> (out [T,96,512], lse [T,96]).
+
+    out is bfloat16 unless out_dtype=torch.float32 (or a float32 `out` is passed)."""
     torch = _torch()
     _contig(_bits16(q, "q"), "q")
     _bits16(latent, "latent")
@@ -217,7 +219,10 @@ def sparse_mla_attn(q, latent, kpe, kv_off, q_req, ids, scale: float, out=None, 
         _contig(_dev(x, n), n)
     t, h = q.shape[0], q.shape[1]
     if out is None:
-        out = torch.empty((t, h, LATENT_DIM), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((t, h, LATENT_DIM), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    out_code = 1 if out.dtype == torch.float32 else 0
     if lse is None:
         lse = torch.empty((t, h), dtype=torch.float32, device=q.device)
     need = sparse_mla_workspace_size(t, h, ids.shape[1] if ids.dim() == 2 else TOPK)
@@ -226,6 +231,6 @@ def sparse_mla_attn(q, latent, kpe, kv_off, q_req, ids, scale: float, out=None, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_sparse_mla_attn", library().dsa_sparse_mla_attn(
         _ptr(q), _ptr(latent), ld_lat, _ptr(kpe), ld_kpe, _ptr(kv_off), _ptr(q_req), _ptr(ids), t,
-        b, h, ids.shape[1], float(scale), _ptr(_contig(out, "out")), _ptr(lse), _ptr(workspace),
-        ws_bytes, _stream(stream)))
+        b, h, ids.shape[1], float(scale), _ptr(_contig(out, "out")), out_code, _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse

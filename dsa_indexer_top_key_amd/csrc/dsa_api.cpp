@@ -23,7 +23,8 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t ld_lat,
                              const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
                              const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
-                             uint16_t* out, float* lse, void* workspace, hipStream_t stream);
+                             void* out, bool out_f32, float* lse, void* workspace,
+                             hipStream_t stream);
 size_t sparse_mla_workspace_bytes(int32_t T);
 }  // namespace dsa
 
@@ -194,7 +195,7 @@ dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int6
                                  const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
                                  const int32_t* q_req, const int32_t* ids, int32_t T,
                                  int32_t B, int32_t n_heads, int32_t topk, float scale,
-                                 uint16_t* out, float* lse, void* workspace,
+                                 void* out, int32_t out_dtype, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
     const char* fn = "dsa_sparse_mla_attn";
     DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
@@ -205,6 +206,8 @@ dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int6
     if (T == 0) return ok();
     DSA_REQUIRE(B >= 1, DSA_ERR_INVALID_ARG, "%s: B=%d must be >= 1", fn, B);
     DSA_REQUIRE(std::isfinite(scale), DSA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+    DSA_REQUIRE(out_dtype == DSA_OUT_BF16 || out_dtype == DSA_OUT_F32, DSA_ERR_UNSUPPORTED,
+                "%s: out_dtype=%d unsupported (DSA_OUT_BF16 or DSA_OUT_F32)", fn, out_dtype);
     DSA_REQUIRE(q && latent && kpe && kv_off && q_req && ids && out, DSA_ERR_INVALID_ARG,
                 "%s: null pointer", fn);
     DSA_REQUIRE(aligned(q, 16) && aligned(latent, 16) && aligned(kpe, 16) && aligned(out, 16),
@@ -226,8 +229,8 @@ dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int6
                     "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
     }
     return from_hip(dsa::launch_sparse_mla(q, latent, ld_latent, kpe, ld_kpe, kv_off, q_req, ids,
-                                           T, scale, out, lse, workspace,
-                                           static_cast<hipStream_t>(stream)), fn);
+                                           T, scale, out, out_dtype == DSA_OUT_F32, lse,
+                                           workspace, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

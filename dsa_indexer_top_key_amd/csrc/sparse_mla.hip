@@ -122,8 +122,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t ld_lat,
     const uint16_t* __restrict__ kpe, int64_t ld_kpe, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ ids, int32_t T,
-    int32_t nsplit, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int32_t nsplit, float scale_log2, void* __restrict__ out, int out_f32,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
     __shared__ MlaSmem sm;
     const int g = blockIdx.x;
     const int j = g >> 3;
@@ -217,10 +217,13 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
                 const int hd = 32 * hg + 8 * (r >> 2) + 4 * hh + (r & 3);
                 const float v = orest[hg][r] * sm.inv_l[hd];
                 const int col = 32 * kHelpTile + hl;
-                if (nsplit == 1)
-                    out[(static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + col] = f32_to_bf16(v);
-                else
+                const int64_t oi = (static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + col;
+                if (nsplit > 1)
                     part_o[(ps * kMlaHeads + hd) * kLatent + col] = v;
+                else if (out_f32)
+                    static_cast<float*>(out)[oi] = v;
+                else
+                    static_cast<uint16_t*>(out)[oi] = f32_to_bf16(v);
             }
         return;
     }
@@ -270,19 +273,21 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
             if (m_ref == -INFINITY) m_ref = mx;  // first tile of pass 0 (uniform per head)
             overflow |= mx > m_ref + 32.f;
             const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-            float psum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[r] = exp2f(sacc[r] - m_use);
-                psum += sacc[r];
-            }
-            l_run += psum;
+            for (int r = 0; r < 16; ++r) sacc[r] = exp2f(sacc[r] - m_use);
+            // P enters P . V in bf16; the normaliser sums the same rounded values, so the read
+            // is an exact convex combination of the rounded weights (a dominant row's rounding
+            // cancels instead of showing up as a 2^-9 relative error of the output)
             u32x4 pa0, pa1;
+            float psum = 0.f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 pa0[k] = pack_bf16x2(sacc[2 * k], sacc[2 * k + 1]);
                 pa1[k] = pack_bf16x2(sacc[8 + 2 * k], sacc[8 + 2 * k + 1]);
+                psum += (__uint_as_float(pa0[k] << 16) + __uint_as_float(pa0[k] & 0xffff0000u)) +
+                        (__uint_as_float(pa1[k] << 16) + __uint_as_float(pa1[k] & 0xffff0000u));
             }
+            l_run += psum;
             sm.pfrag[wave][lane][0] = pa0;
             sm.pfrag[wave][lane][1] = pa1;
             __syncthreads();  // B_i
@@ -324,13 +329,17 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) ir[r] = __shfl(inv, 8 * (r >> 2) + 4 * hh + (r & 3));
     if (nsplit == 1) {
-        uint16_t* ot = out + static_cast<int64_t>(t) * kMlaHeads * kLatent;
+        const int64_t ob = static_cast<int64_t>(t) * kMlaHeads * kLatent;
 #pragma unroll
         for (int nt = 0; nt < kConsTiles; ++nt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int hd = head0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                ot[hd * kLatent + 32 * nt + hl] = f32_to_bf16(o[nt][r] * ir[r]);
+                const float v = o[nt][r] * ir[r];
+                if (out_f32)
+                    static_cast<float*>(out)[ob + hd * kLatent + 32 * nt + hl] = v;
+                else
+                    static_cast<uint16_t*>(out)[ob + hd * kLatent + 32 * nt + hl] = f32_to_bf16(v);
             }
     } else {
         float* po = part_o + ps * kMlaHeads * kLatent;
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           int32_t T, int32_t nsplit,
-                                                          uint16_t* __restrict__ out,
+                                                          void* __restrict__ out, int out_f32,
                                                           float* __restrict__ lse) {
     const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (pair >= static_cast<int64_t>(T) * kMlaHeads) return;
@@ -373,12 +382,19 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    u32x4 o;
-    o[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    o[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    o[2] = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-    o[3] = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-    *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + 8 * lane) = o;
+    const int64_t oi = (static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + 8 * lane;
+    if (out_f32) {
+        f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(out) + oi);
+        dst[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        dst[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    } else {
+        u32x4 o;
+        o[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+        o[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+        o[2] = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+        o[3] = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + oi) = o;
+    }
     if (lse && lane == 0)
         lse[static_cast<int64_t>(t) * kMlaHeads + hd] = wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
 }
@@ -401,7 +417,8 @@ size_t sparse_mla_workspace_bytes(int32_t T) {
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t ld_lat,
                              const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
                              const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
-                             uint16_t* out, float* lse, void* workspace, hipStream_t stream) {
+                             void* out, bool out_f32, float* lse, void* workspace,
+                             hipStream_t stream) {
     const int ns = sparse_mla_nsplit(T);
     const int64_t groups = (static_cast<int64_t>(T) + 7) / 8;
     const int64_t blocks = groups * 8 * ns;
@@ -415,12 +432,12 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL(sparse_mla_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                        stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, ns,
-                       scale_log2, out, lse, part_o, part_lse);
+                       scale_log2, out, out_f32 ? 1 : 0, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     const int64_t cblocks = (static_cast<int64_t>(T) * kMlaHeads + 3) / 4;
     hipLaunchKernelGGL(mla_combine_kernel, dim3(static_cast<unsigned>(cblocks)), dim3(256), 0,
-                       stream, part_o, part_lse, T, ns, out, lse);
+                       stream, part_o, part_lse, T, ns, out, out_f32 ? 1 : 0, lse);
     return hipGetLastError();
 }
 

@@ -67,6 +67,9 @@ typedef enum {
 #define DSA_COMPANION_DIM 64
 #define DSA_WORKSPACE_ALIGN 256
 
+/* Element type of the sparse read's output. */
+typedef enum { DSA_OUT_BF16 = 0, DSA_OUT_F32 = 1 } dsa_out_dtype_t;
+
 /* Version of this ABI; bumped on any incompatible change. */
 int dsa_abi_version(void);
 
@@ -150,10 +153,11 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
  *          >= S_b is padding and is skipped.  Duplicate IDs are counted twice.
  * topk     must be 2048; n_heads must be 96.
  * scale    logit scale (1/sqrt(192) for K3.1), finite.
- * out      [T,96,512] bf16: o = sum_{j in I_t} p_j c_j[0:512],
+ * out      [T,96,512], element type out_dtype (DSA_OUT_BF16, rounded to nearest even, or
+ *          DSA_OUT_F32), 16-byte aligned: o = sum_{j in I_t} p_j c_j[0:512],
  *          p_j = exp(a_j - m) / sum_{i in I_t} exp(a_i - m),  a_j = scale * q . [c_j ; kpe_j].
- *          fp32 softmax, bf16 x bf16 products accumulated in fp32, rounded to bf16 (RNE).
- *          A row with no valid ID gives out = 0.
+ *          fp32 softmax; P and the latent enter the P.V product as bf16, products are
+ *          accumulated in fp32.  A row with no valid ID gives out = 0.
  * lse      [T,96] float32 out (may be NULL): log sum_{j in I_t} exp(a_j); -inf if empty.
  * workspace at least dsa_sparse_mla_workspace_size(T, 96, 2048) bytes, 256-byte aligned
  *          (may be NULL when that size is 0): split-KV partial results.
@@ -163,7 +167,7 @@ dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int6
                                  const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
                                  const int32_t* q_req, const int32_t* ids, int32_t T,
                                  int32_t B, int32_t n_heads, int32_t topk, float scale,
-                                 uint16_t* out, float* lse, void* workspace,
+                                 void* out, int32_t out_dtype, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -88,6 +88,18 @@ def layernorm_keys(raw, gamma, beta, eps) -> np.ndarray:
     return (x - mu) / np.sqrt(var + eps) * g + b
 
 
+def layernorm_term_magnitude(raw, gamma, beta, eps) -> np.ndarray:
+    """|normalised x * gamma| + |beta| per element: the size of the two terms whose sum is the
+    output, which bounds the absolute rounding error of any fp32 evaluation of it."""
+    x = np.asarray(raw, dtype=np.float32).astype(np.float64)
+    g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    b = np.asarray(beta, dtype=np.float32).astype(np.float64)
+    eps = float(np.float32(eps))
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return np.abs((x - mu) / np.sqrt(var + eps) * g) + np.abs(b)
+
+
 def layernorm_keys_bf16(raw, gamma, beta, eps) -> np.ndarray:
     """Stage-1 output as stored in the index-key cache: bf16 bit patterns [N,128]."""
     return f64_to_bf16(layernorm_keys(raw, gamma, beta, eps))

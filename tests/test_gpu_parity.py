@@ -1,8 +1,10 @@
 """GPU parity of every stage against the CPU oracle (same seeded inputs on both sides).
 
-Tolerances: LayerNorm <= 1 bf16 ulp; indexer scores |s - s_ref| <= 1e-3 * max(|s_ref|, r_t)
+Tolerances: LayerNorm <= 1 bf16 ulp (or, where its two terms cancel, 2^-16 of their size);
+indexer scores |s - s_ref| <= 1e-3 * max(|s_ref|, r_t)
 (r_t: the row's RMS score); top-k bit-exact on identical fp32 arrays; selected sets equal
-up to positions within the 1e-3 band of the k-th score; sparse read max-abs 1e-2 on out and
+up to positions within the 1e-3 band of the k-th score; sparse read max-abs 1e-2 on out (fp32
+output; a bf16 output adds half a bf16 ulp of the reference for its own rounding) and
 1e-3 * max(1, |lse|) on lse, given the same ID set.
 """
 import numpy as np
@@ -42,6 +44,21 @@ def host_bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def ln_tolerance_ok(got_bits, raw, gamma, beta, eps):
+    """LayerNorm parity: within 1 bf16 ulp of the oracle, or -- where the two terms of
+    x_hat*gamma + beta cancel -- within 2^-16 * (|x_hat*gamma| + |beta|) of the exact value
+    (fp32 evaluation leaves an absolute error of a few 2^-24 of the terms; 2^-16 is 256 of
+    them, still far below a bf16 ulp of an uncancelled output).  Returns the fraction of
+    elements that needed the second clause."""
+    ref_bits = O.layernorm_keys_bf16(raw, gamma, beta, eps)
+    one_ulp = bf16_ulp_dist(got_bits, ref_bits) <= 1
+    exact = O.layernorm_keys(raw, gamma, beta, eps)
+    mag = O.layernorm_term_magnitude(raw, gamma, beta, eps)
+    close = np.abs(O.bf16_to_f64(got_bits) - exact) <= 2.0 ** -16 * mag
+    assert np.all(one_ulp | close)
+    return float((~one_ulp).mean())
+
+
 def bf16_ulp_dist(a, b):
     def ordered(x):
         x = x.astype(np.int32)
@@ -66,9 +83,8 @@ def test_layernorm_parity(n):
     torch.cuda.synchronize()
     got = host_bits(keys)
     ref = O.layernorm_keys_bf16(raw, gamma, beta, 1e-6)
-    d = bf16_ulp_dist(got, ref)
-    assert d.max() <= 1
-    assert (d > 0).mean() < 0.01
+    assert ln_tolerance_ok(got, raw, gamma, beta, 1e-6) < 1e-3
+    assert (bf16_ulp_dist(got, ref) > 0).mean() < 0.01
     assert np.array_equal(got[0], O.f64_to_bf16(beta.astype(np.float64)))
 
 
@@ -235,7 +251,7 @@ def test_indexer_topk_prefill():
 # ---------------------------------------------------------------------------------------
 # stage 4
 # ---------------------------------------------------------------------------------------
-def run_mla(lay, d, ids, scale=synth.ATTN_SCALE, packed=False):
+def run_mla(lay, d, ids, scale=synth.ATTN_SCALE, packed=False, f32=False):
     dsa = dsa_mod()
     if packed:
         base = dev(np.concatenate([d["latent"], d["kpe"]], axis=1))
@@ -243,32 +259,46 @@ def run_mla(lay, d, ids, scale=synth.ATTN_SCALE, packed=False):
     else:
         lat, kpe = dev(d["latent"]), dev(d["kpe"])
     out, lse = dsa.sparse_mla_attn(dev(d["q"]), lat, kpe, dev(lay.kv_off), dev(lay.q_req),
-                                   dev(ids), scale)
+                                   dev(ids), scale,
+                                   out_dtype=torch.float32 if f32 else torch.bfloat16)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
 
-def check_mla(lay, d, ids, got_o, got_l, scale=synth.ATTN_SCALE):
+def bf16_half_ulp(v):
+    """Half the spacing of bf16 numbers at |v| (8 significant bits)."""
+    a = np.abs(v)
+    return np.where(a > 0, np.ldexp(1.0, np.frexp(a)[1] - 9), 0.0)
+
+
+def out_tolerance(ref_o, f32):
+    """1e-2 on the read itself; a bf16 output adds its own rounding (half an ulp)."""
+    return 1e-2 + (0.0 if f32 else bf16_half_ulp(ref_o))
+
+
+def check_mla(lay, d, ids, got_o, got_l, scale=synth.ATTN_SCALE, f32=False):
     ref_o, ref_l = O.sparse_mla(d["q"], d["latent"], d["kpe"], lay.kv_off, lay.q_req, ids, scale)
-    err = np.abs(got_o - ref_o).max()
-    assert err <= 1e-2, f"max abs err {err}"
+    err = np.abs(got_o - ref_o)
+    assert np.all(err <= out_tolerance(ref_o, f32)), f"max abs err {err.max()}"
     fin = np.isfinite(ref_l)
     assert np.array_equal(fin, np.isfinite(got_l))
     assert np.all(np.abs(got_l[fin] - ref_l[fin]) <= 1e-3 * np.maximum(1, np.abs(ref_l[fin])))
     assert np.all(got_l[~fin] == -np.inf) and np.all(got_o[~np.isfinite(ref_l)] == 0)
 
 
-@pytest.mark.parametrize("t_count,packed", [(1, False), (4, True), (64, False), (300, False)])
-def test_sparse_mla_parity(t_count, packed):
-    print(f"[mla] T={t_count} packed={packed}", flush=True)
+@pytest.mark.parametrize("t_count,packed,f32", [(1, False, False), (4, True, True),
+                                                (64, False, False), (64, False, True),
+                                                (300, False, False), (300, True, True)])
+def test_sparse_mla_parity(t_count, packed, f32):
+    print(f"[mla] T={t_count} packed={packed} f32={f32}", flush=True)
     g = np.random.default_rng(30 + t_count)
     s_len = g.integers(1, 6000, size=t_count)
     s_len[0] = 5000
     lay = synth.decode_layout("mla", 30 + t_count, s_len)
     d = synth.inputs_np(lay, parts=("mla",))
     ids = synth.random_ids_np(30 + t_count, lay)
-    got_o, got_l = run_mla(lay, d, ids, packed=packed)
-    check_mla(lay, d, ids, got_o, got_l)
+    got_o, got_l = run_mla(lay, d, ids, packed=packed, f32=f32)
+    check_mla(lay, d, ids, got_o, got_l, f32=f32)
 
 
 def test_sparse_mla_special_rows():
@@ -297,7 +327,7 @@ def test_sparse_mla_short_prefix_equals_dense():
     lay = synth.decode_layout("dense", 41, [1, 100, 2047, 2048])
     d = synth.inputs_np(lay, parts=("mla",))
     ids = O.topk_rows([np.zeros(n) for n in lay.s_len])
-    got_o, _ = run_mla(lay, d, ids)
+    got_o, _ = run_mla(lay, d, ids, f32=True)
     dr = O.dense_read(d["q"], d["latent"], d["kpe"], lay.kv_off, lay.q_req, lay.q_pos, ids,
                       synth.ATTN_SCALE)
     assert np.all(dr["eps"] == 0)
@@ -306,12 +336,14 @@ def test_sparse_mla_short_prefix_equals_dense():
 
 def test_sparse_mla_large_logits_take_the_exact_max_pass():
     print("[mla] large logit spread", flush=True)
-    lay = synth.decode_layout("big", 42, [4096])
-    d = synth.inputs_np(lay, parts=("mla",))
-    ids = synth.random_ids_np(42, lay)
-    # scale 4: logit spread far beyond 2^32 between the first tile and later ones
-    got_o, got_l = run_mla(lay, d, ids, scale=4.0)
-    check_mla(lay, d, ids, got_o, got_l, scale=4.0)
+    # scale 4: logit spread far beyond 2^32 between the first tile and later ones; the
+    # softmax is then nearly one-hot, so outputs reach |o| ~ 4 -- read in fp32
+    for t_count in (1, 300):
+        lay = synth.decode_layout("big", 42, [4096] * t_count)
+        d = synth.inputs_np(lay, parts=("mla",))
+        ids = synth.random_ids_np(42, lay)
+        got_o, got_l = run_mla(lay, d, ids, scale=4.0, f32=True)
+        check_mla(lay, d, ids, got_o, got_l, scale=4.0, f32=True)
 
 
 # ---------------------------------------------------------------------------------------
@@ -336,7 +368,7 @@ def test_end_to_end_small_workloads(name):
     torch.cuda.synchronize()
     assert torch.equal(ids, ids2) and torch.equal(out, out2), "not deterministic"
     keys_ref = O.layernorm_keys_bf16(d["raw_keys"], d["gamma"], d["beta"], synth.LN_EPS)
-    assert bf16_ulp_dist(host_bits(keys), keys_ref).max() <= 1
+    assert ln_tolerance_ok(host_bits(keys), d["raw_keys"], d["gamma"], d["beta"], synth.LN_EPS) < 1e-3
     s_ref = O.indexer_scores(d["q_idx"], d["w"], keys_ref, lay.kv_off, lay.q_req, lay.q_pos)
     got_ids = ids.cpu().numpy()
     check_selection(lay, got_ids, s_ref)
@@ -346,8 +378,9 @@ def test_end_to_end_small_workloads(name):
     o_ref, l_ref = O.sparse_mla(d["q"], d["latent"], d["kpe"], lay.kv_off, lay.q_req, ids_ref,
                                 synth.ATTN_SCALE, rows=same)
     o = out.float().cpu().numpy()[same]
-    assert np.abs(o - o_ref).max() <= 1e-2
+    assert np.all(np.abs(o - o_ref) <= out_tolerance(o_ref, False))
     # the dropped-mass bound against the oracle's full causal read
     dr = O.dense_read(d["q"], d["latent"], d["kpe"], lay.kv_off, lay.q_req, lay.q_pos, ids_ref,
                       synth.ATTN_SCALE, rows=same)
-    assert np.all(np.abs(o - dr["o_full"]) <= dr["eps"][:, :, None] * dr["v_range"][:, None, :] + 1e-2)
+    assert np.all(np.abs(o - dr["o_full"]) <= dr["eps"][:, :, None] * dr["v_range"][:, None, :]
+                  + out_tolerance(dr["o_full"], False))
