@@ -42,6 +42,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Workgroup barrier that orders LDS only: LDS writes issued before it are visible to LDS
+// reads after it, while global-memory loads (and global->LDS copies) stay in flight; where
+// a kernel hands such data across the barrier it waits on vmcnt explicitly.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

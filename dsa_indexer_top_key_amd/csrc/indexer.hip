@@ -144,7 +144,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
             s_n[tid] = 0;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // this wave's two queries
     const int qi0 = 2 * wave, qi1 = 2 * wave + 1;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
         u32x4 pre = load_chunk(0);
         *reinterpret_cast<u32x4*>(&ks[0][lrow * kKeyStride + 8 * lchunk]) = pre;
         if (n_tiles > 1) pre = load_chunk(1);
-        __syncthreads();
+        lds_barrier();
 
         for (int tile = 0; tile < n_tiles; ++tile) {
             const uint16_t* kt = ks[tile & 1];
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
             const int64_t key = key0 + col;
             if (h == 0 && key < n0) scores[static_cast<int64_t>(t0 + qi0) * ld + key] = v0;
             if (h == 1 && key < n1) scores[static_cast<int64_t>(t0 + qi1) * ld + key] = v1;
-            __syncthreads();
+            lds_barrier();
         }
         done_mask |= pass_mask;
     }

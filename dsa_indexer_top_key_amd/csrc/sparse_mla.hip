@@ -16,11 +16,15 @@
 // their 32 x 576 absorbed queries live in registers for the whole block, as the B operand
 // of  S^T = C . Q^T  (v_mfma_f32_32x32x16_bf16, M = 32 gathered rows, N = 32 heads), which
 // leaves each lane with one head and 16 rows -- exactly the A-operand layout the P . V
-// product needs, so probabilities never leave registers.  The 32 x 512 output of a head
-// group accumulates in registers across the split.  Wave 3 gathers the selected rows
-// (coalesced 16-byte loads of whole 1152-byte rows) into a three-deep LDS ring, two tiles
-// ahead of the consumers.  The V operand of P . V (rows x latent dims) is read from the
-// row-major LDS tile with the gfx950 transposing load ds_read_b64_tr_b16.
+// product needs, so probabilities never leave registers.  The 32 x 384 output of a head
+// group accumulates in its AGPRs across the split.  Wave 3 gathers the selected rows into a
+// three-deep LDS ring with gfx950's direct global->LDS copies (one 1 KB copy per latent row,
+// wave-uniform address; companion keys 8 rows per copy), issued two tiles ahead while the
+// head groups compute S^T, and
+// computes the last 128 latent columns of all 96 heads from P fragments the head groups
+// publish in LDS.  The V operand of P . V (rows x latent dims) is read from the row-major
+// LDS tile with the transposing load ds_read_b64_tr_b16.  Barriers order LDS only, so the
+// ring copies stay in flight across them (the gather wave waits on vmcnt explicitly).
 //
 // Softmax (fp32, log2 domain) uses a fixed per-head reference: the maximum logit of the
 // first tile.  Later probabilities p = 2^(x - ref) may exceed 1; that is exact after the
@@ -35,24 +39,36 @@
 
 namespace dsa {
 
-constexpr int kTile = 32;            // gathered rows per step
-constexpr int kRowStride = kQK + 8;  // padded LDS row, bf16 elements (1168 B)
-constexpr int kNBuf = 3;             // LDS ring depth
-constexpr int kChunksPerRow = kQK / 8;                      // 72 x 16 B
+constexpr int kTile = 32;                    // gathered rows per step
+constexpr int kNBuf = 3;                     // LDS ring depth
+constexpr int kLatStride = kLatent + 8;      // latent row in LDS: 1024 B + 16 B pad
+constexpr int kNTiles = kLatent / 32;        // 16 output tiles of 32 latent dims
+constexpr int kHelpTiles = 4;                // computed by the gather wave for all heads
+constexpr int kConsTiles = kNTiles - kHelpTiles;  // kept by the head-group waves
+constexpr int kKSteps = kQK / 16;            // 36 MFMA K-steps over the 576 dims
+// K order of the 576-dim dot (any order works as long as q and the rows agree): at K-step
+// s < 32 lane half hh holds latent dims 256 hh + 8s .. +8; at s >= 32 it holds companion
+// dims 32 hh + 8 (s - 32) .. +8, so both halves reach the companion block together.
+constexpr int kLatSteps = kLatent / 16;      // 32
+constexpr int kQfInAcc = 12;                 // q fragments kept in accumulation registers
+constexpr int kPrefA = 4;                    // LDS prefetch depth of S^T A fragments
+constexpr int kPrefV = 4;                    // LDS prefetch depth of P.V B fragments
+constexpr int kDmaPerTile = kTile + kTile / 8;  // 32 latent rows + 4 companion blocks
 constexpr float kLn2 = 0.69314718055994531f;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-constexpr int kNTiles = kLatent / 32;        // 16 output tiles of 32 latent dims
-constexpr int kConsTiles = kNTiles - 1;       // kept by the head-group waves
-constexpr int kHelpTile = kNTiles - 1;        // computed by the gather wave for all heads
-
+// One ring slot: 32 latent rows (1040-byte stride, so the 32 rows read by one A-operand
+// fetch fall in distinct banks) and 32 companion rows of 128 B whose 16-byte chunks are
+// XOR-swizzled by (row % 8) for the same reason.
 struct MlaSmem {
-    uint16_t c[kNBuf][kTile * kRowStride];   // ring of gathered row tiles
+    uint16_t lat[kNBuf][kTile * kLatStride];
+    uint16_t kpe[kNBuf][kTile * kCompanion];
     int32_t rows[kTopK];                     // compacted request-local IDs of the split
     u32x4 pfrag[3][64][2];                   // P (bf16) in A-operand layout, per head group
     float inv_l[kMlaHeads];                  // per-head 1/l at the end
@@ -60,46 +76,42 @@ struct MlaSmem {
     uint32_t redo;                           // some logit exceeded its reference by > 2^32
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Gather one tile of rows straight into LDS with gfx950's global_load_lds_dwordx4: each
-// instruction writes 64 consecutive 16-byte LDS slots (lane l -> slot base + l), so the tile
-// buffer is viewed as 32 rows x 73 slots (72 data chunks of a 1152-byte row -- 64 latent +
-// 8 companion -- and one padding slot).  Padding slots and rows past the split's end are
-// not loaded (their lanes are inactive).  The data bypasses registers entirely; completion
-// is tracked with vmcnt by the issuing wave.
-constexpr int kSlotsPerRow = kChunksPerRow + 1;              // 73
-constexpr int kTileSlots = kTile * kSlotsPerRow;             // 2336
-constexpr int kDmaPerTile = (kTileSlots + 63) / 64;          // 37 instructions
-static_assert(kSlotsPerRow * 8 == kRowStride, "LDS row = 73 slots of 16 bytes");
-
-__device__ __forceinline__ void gather_tile(uint16_t* buf, int tile, int n_rows,
-                                            const int32_t* rows, const uint16_t* latent,
-                                            int64_t ld_lat, const uint16_t* kpe, int64_t ld_kpe,
-                                            int64_t base, int lane) {
-    // all row IDs first (LDS reads), then the DMA stream, so the reads do not serialise it
-    int32_t rid[kDmaPerTile];
+// Gather tile `tile` of the split into one ring slot with gfx950's global_load_lds_dwordx4
+// (each instruction writes 64 x 16 consecutive LDS bytes; nothing passes through registers).
+// A latent row is one instruction -- its address is wave-uniform -- and every 8 companion
+// rows are one more.  Rows past n_rows are not loaded.  Returns the number of copies issued.
+__device__ __forceinline__ int gather_tile(uint16_t* lat_buf, uint16_t* kpe_buf, int tile,
+                                           int n_rows, const int32_t* rows,
+                                           const uint16_t* latent, int64_t ld_lat,
+                                           const uint16_t* kpe, int64_t ld_kpe, int64_t base,
+                                           int lane) {
+    const int r0 = tile * kTile;
+    const int nr = min(kTile, n_rows - r0);
+    const int my_rid = (lane < nr) ? rows[r0 + lane] : 0;
 #pragma unroll
-    for (int k = 0; k < kDmaPerTile; ++k) {
-        const int sidx = 64 * k + lane;
-        const int slot = tile * kTile + sidx / kSlotsPerRow;
-        rid[k] = (sidx < kTileSlots && slot < n_rows) ? rows[slot] : -1;
-    }
-#pragma unroll
-    for (int k = 0; k < kDmaPerTile; ++k) {
-        const int sidx = 64 * k + lane;
-        const int cc = sidx - (sidx / kSlotsPerRow) * kSlotsPerRow;
-        if (rid[k] >= 0 && cc < kChunksPerRow) {
-            const int64_t row = base + rid[k];
-            const uint16_t* src = cc < 64 ? latent + row * ld_lat + 8 * cc
-                                          : kpe + row * ld_kpe + 8 * (cc - 64);
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + 64 * 8 * k), 16, 0, 0);
+    for (int r = 0; r < kTile; ++r) {
+        if (r < nr) {
+            const int64_t row = base + __builtin_amdgcn_readlane(my_rid, r);
+            __builtin_amdgcn_global_load_lds(latent + row * ld_lat + 8 * lane,
+                                             (lds_void*)(lat_buf + r * kLatStride), 16, 0, 0);
         }
     }
+#pragma unroll
+    for (int i = 0; i < kTile / 8; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const int rid = __shfl(my_rid, r);
+        if (8 * i < nr) {  // uniform: the block of 8 rows has at least one valid row
+            const int c = (lane & 7) ^ (r & 7);  // this lane's LDS slot holds logical chunk c
+            const int64_t row = base + (r < nr ? rid : 0);
+            __builtin_amdgcn_global_load_lds(kpe + row * ld_kpe + 8 * c,
+                                             (lds_void*)(kpe_buf + i * 8 * kCompanion), 16, 0, 0);
+        }
+    }
+    return nr + (nr + 7) / 8;
 }
 
-// Wait until at most n of this wave's vector-memory operations are outstanding
-// (s_waitcnt vmcnt(n) with expcnt/lgkmcnt left at their maxima; n <= 63).
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (s_waitcnt vmcnt(N) with expcnt/lgkmcnt left at their maxima; N <= 63).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
@@ -112,9 +124,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 16-lane group, lane q points at row q/4, columns 4(q%4)..4(q%4)+3 of a 4 x 16 block; the
 // transposing load returns column q of the block's four rows.
 __device__ __forceinline__ bf16x8 v_fragment(const uint16_t* vbase, int nt, int c) {
-    const uint16_t* vp = vbase + 16 * c * kRowStride + 32 * nt;
+    const uint16_t* vp = vbase + 16 * c * kLatStride + 32 * nt;
     const bf16x4 v0 = lds_read_tr16(vp);
-    const bf16x4 v1 = lds_read_tr16(vp + 8 * kRowStride);
+    const bf16x4 v1 = lds_read_tr16(vp + 8 * kLatStride);
     return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -145,8 +157,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     if (tid == 0) sm.redo = 0;
     // rows past the end of a split are never loaded: start from a zeroed ring so the masked
     // rows of a partial tile hold finite values (their probabilities are exactly 0)
-    for (int i = tid; i < kNBuf * kTile * kRowStride / 8; i += 256)
-        reinterpret_cast<u32x4*>(&sm.c[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < static_cast<int>(kNBuf * kTile * kLatStride / 8); i += 256)
+        reinterpret_cast<u32x4*>(&sm.lat[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < static_cast<int>(kNBuf * kTile * kCompanion / 8); i += 256)
+        reinterpret_cast<u32x4*>(&sm.kpe[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
     int n_rows = 0;
     for (int i0 = 0; i0 < L; i0 += 256) {
         const int i = i0 + tid;
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         const bool ok = id >= 0 && static_cast<int64_t>(id) < s_b;
         const uint64_t m = __ballot(ok);
         if (lane == 0) sm.wcnt[wave] = __popcll(m);
-        __syncthreads();
+        lds_barrier();
         uint32_t before = 0, total = 0;
 #pragma unroll
         for (int wv = 0; wv < 4; ++wv) {
@@ -163,7 +177,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         }
         if (ok) sm.rows[n_rows + before + __popcll(m & ((1ull << lane) - 1ull))] = id;
         n_rows += total;
-        __syncthreads();
+        lds_barrier();
     }
     const int n_tiles = (n_rows + kTile - 1) / kTile;
     const int q16 = lane & 15;
@@ -175,48 +189,66 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     // groups have published P of tile i).  A second pass (rare) repeats the whole sequence.
     if (wave == 3) {
         // ================= gather wave: ring producer + last latent tile of every head
-        f32x16 orest[3];
+        f32x16 orest[3][kHelpTiles];
         for (int pass = 0; pass < 2; ++pass) {
-            orest[0] = f32x16{};
-            orest[1] = f32x16{};
-            orest[2] = f32x16{};
-            if (n_tiles > 0) gather_tile(sm.c[0], 0, n_rows, sm.rows, latent, ld_lat, kpe, ld_kpe, base, lane);
-            if (n_tiles > 1) gather_tile(sm.c[1], 1, n_rows, sm.rows, latent, ld_lat, kpe, ld_kpe, base, lane);
-            wait_vmcnt<0>();
-            __syncthreads();  // A_0
-            for (int i = 0; i < n_tiles; ++i) {
-                __syncthreads();  // B_i
-                const uint16_t* vbase = sm.c[i % kNBuf] + vrow * kRowStride + vcol;
-                const bf16x8 v0 = v_fragment(vbase, kHelpTile, 0);
-                const bf16x8 v1 = v_fragment(vbase, kHelpTile, 1);
 #pragma unroll
-                for (int hg = 0; hg < 3; ++hg) {
-                    orest[hg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][0]), v0, orest[hg], 0, 0, 0);
-                    orest[hg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][1]), v1, orest[hg], 0, 0, 0);
-                }
-                // tile i+2 -> ring slot (i+2)%3 (last read in step i-1); tile i+1, issued one
-                // step earlier, must have landed before A_{i+1} publishes it
+            for (int hg = 0; hg < 3; ++hg)
+#pragma unroll
+                for (int ht = 0; ht < kHelpTiles; ++ht) orest[hg][ht] = f32x16{};
+            // tiles 0 and 1; only tile 0 has to land before A_0
+            int in_flight = 0;  // copies of the newest tile still allowed in flight
+            for (int tl = 0; tl < 2 && tl < n_tiles; ++tl)
+                in_flight = gather_tile(sm.lat[tl], sm.kpe[tl], tl, n_rows, sm.rows, latent,
+                                        ld_lat, kpe, ld_kpe, base, lane);
+            if (n_tiles > 1 && in_flight == kDmaPerTile)
+                wait_vmcnt<kDmaPerTile>();
+            else
+                wait_vmcnt<0>();
+            lds_barrier();  // A_0
+            for (int i = 0; i < n_tiles; ++i) {
+                // While the head groups compute S^T of tile i: tile i+2 -> ring slot (i+2)%3
+                // (last read in step i-1).  Tile i+1 has to land before A_{i+1}.
+                int newest = 0;
                 if (i + 2 < n_tiles) {
-                    gather_tile(sm.c[(i + 2) % kNBuf], i + 2, n_rows, sm.rows, latent, ld_lat, kpe, ld_kpe, base, lane);
-                    wait_vmcnt<kDmaPerTile>();
-                } else {
-                    wait_vmcnt<0>();
+                    const int sl = (i + 2) % kNBuf;
+                    newest = gather_tile(sm.lat[sl], sm.kpe[sl], i + 2, n_rows, sm.rows, latent,
+                                         ld_lat, kpe, ld_kpe, base, lane);
                 }
-                __syncthreads();  // A_{i+1}
+                lds_barrier();  // B_i
+                const uint16_t* vbase = sm.lat[i % kNBuf] + vrow * kLatStride + vcol;
+#pragma unroll
+                for (int ht = 0; ht < kHelpTiles; ++ht) {
+                    const bf16x8 v0 = v_fragment(vbase, kConsTiles + ht, 0);
+                    const bf16x8 v1 = v_fragment(vbase, kConsTiles + ht, 1);
+#pragma unroll
+                    for (int hg = 0; hg < 3; ++hg) {
+                        orest[hg][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][0]), v0, orest[hg][ht], 0, 0, 0);
+                        orest[hg][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][1]), v1, orest[hg][ht], 0, 0, 0);
+                    }
+                }
+                // a full tile is exactly kDmaPerTile copies, so vmcnt <= kDmaPerTile leaves
+                // only tile i+2 in flight; after a partial (last) tile wait for everything
+                if (newest == kDmaPerTile)
+                    wait_vmcnt<kDmaPerTile>();
+                else
+                    wait_vmcnt<0>();
+                lds_barrier();  // A_{i+1}
             }
             if (pass == 0) {
-                __syncthreads();  // E: the head groups have published their overflow flags
+                lds_barrier();  // E: the head groups have published their overflow flags
                 if (sm.redo == 0) break;
             }
         }
-        __syncthreads();  // the head groups have published 1/l
+        lds_barrier();  // the head groups have published 1/l
 #pragma unroll
         for (int hg = 0; hg < 3; ++hg)
 #pragma unroll
+            for (int ht = 0; ht < kHelpTiles; ++ht)
+#pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int hd = 32 * hg + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float v = orest[hg][r] * sm.inv_l[hd];
-                const int col = 32 * kHelpTile + hl;
+                const float v = orest[hg][ht][r] * sm.inv_l[hd];
+                const int col = 32 * (kConsTiles + ht) + hl;
                 const int64_t oi = (static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + col;
                 if (nsplit > 1)
                     part_o[(ps * kMlaHeads + hd) * kLatent + col] = v;
@@ -229,34 +261,49 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     }
 
     // ================= head-group waves: heads 32*wave .. 32*wave+31
-    u32x4 qf[kQK / 16];  // 36 K-steps; lane half hh covers dims [288 hh, 288 hh + 288)
+    u32x4 qf[kKSteps];
     {
-        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK + 288 * hh;
+        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
 #pragma unroll
-        for (int s = 0; s < kQK / 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qh + 8 * s);
+        for (int s = 0; s < kKSteps; ++s) {
+            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
+            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
+            // the last kQfInAcc fragments live in accumulation registers (MFMA reads its B
+            // operand from there directly), leaving VGPRs for deep LDS prefetch
+            if (s >= kKSteps - kQfInAcc) asm volatile("" : "+a"(qf[s]));
+        }
     }
     f32x16 o[kConsTiles];
     float m_ref = -INFINITY;   // reference logit of this lane's head (log2 domain)
     float m_seen = -INFINITY;  // largest logit seen (exact maximum after a full pass)
-    float l_run = 0.f;         // this lane's partial sum of 2^(x - m_ref) over its rows
+    float l_run = 0.f;         // this lane's partial sum of the bf16-rounded 2^(x - m_ref)
+    const int sw = hl & 7;     // companion-row swizzle of this lane's A row
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int nt = 0; nt < kConsTiles; ++nt) o[nt] = f32x16{};
         l_run = 0.f;
         bool overflow = false;
-        __syncthreads();  // A_0
+        lds_barrier();  // A_0
         for (int i = 0; i < n_tiles; ++i) {
-            const uint16_t* buf = sm.c[i % kNBuf];
-            // ---- S^T tile (32 rows x 32 heads): A = gathered rows from LDS, B = q registers.
+            const uint16_t* lat_row = sm.lat[i % kNBuf] + hl * kLatStride + 256 * hh;
+            const uint16_t* kpe_row = sm.kpe[i % kNBuf] + hl * kCompanion;
+            // A fragment of K-step s (same K order as qf); companion chunks are swizzled
+            auto afrag = [&](int s) -> u32x4 {
+                const uint16_t* p = s < kLatSteps ? lat_row + 8 * s
+                                                  : kpe_row + 8 * ((4 * hh + s - kLatSteps) ^ sw);
+                return *reinterpret_cast<const u32x4*>(p);
+            };
+            // ---- S^T tile (32 rows x 32 heads): A = gathered rows (LDS, two steps ahead),
+            // B = q registers
             f32x16 sacc = {};
-            const uint16_t* arow = buf + hl * kRowStride + 288 * hh;
-            u32x4 a0 = *reinterpret_cast<const u32x4*>(arow);
+            u32x4 abuf[kPrefA];
 #pragma unroll
-            for (int s = 0; s < kQK / 16; ++s) {
-                u32x4 a1 = a0;
-                if (s + 1 < kQK / 16) a1 = *reinterpret_cast<const u32x4*>(arow + 8 * (s + 1));
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), as_bf16x8(qf[s]), sacc, 0, 0, 0);
-                a0 = a1;
+            for (int k = 0; k < kPrefA; ++k) abuf[k] = afrag(k);
+#pragma unroll
+            for (int s = 0; s < kKSteps; ++s) {
+                const u32x4 cur = abuf[s % kPrefA];
+                if (s + kPrefA < kKSteps) abuf[s % kPrefA] = afrag(s + kPrefA);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qf[s]), sacc, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- probabilities relative to the fixed per-head reference
@@ -290,27 +337,30 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
             l_run += psum;
             sm.pfrag[wave][lane][0] = pa0;
             sm.pfrag[wave][lane][1] = pa1;
-            __syncthreads();  // B_i
-            // ---- O += P . V over this wave's 15 latent tiles
-            const uint16_t* vbase = buf + vrow * kRowStride + vcol;
-            bf16x8 v0 = v_fragment(vbase, 0, 0);
+            lds_barrier();  // B_i
+            // ---- O += P . V over this wave's 15 latent tiles (V fragments two steps ahead)
+            const uint16_t* vbase = sm.lat[i % kNBuf] + vrow * kLatStride + vcol;
+            bf16x8 vbuf[kPrefV];
+#pragma unroll
+            for (int k = 0; k < kPrefV; ++k) vbuf[k] = v_fragment(vbase, k >> 1, k & 1);
 #pragma unroll
             for (int step = 0; step < 2 * kConsTiles; ++step) {
-                bf16x8 v1 = v0;
-                if (step + 1 < 2 * kConsTiles) v1 = v_fragment(vbase, (step + 1) >> 1, (step + 1) & 1);
-                o[step >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((step & 1) ? pa1 : pa0), v0, o[step >> 1], 0, 0, 0);
-                v0 = v1;
+                const bf16x8 cur = vbuf[step % kPrefV];
+                if (step + kPrefV < 2 * kConsTiles)
+                    vbuf[step % kPrefV] = v_fragment(vbase, (step + kPrefV) >> 1, (step + kPrefV) & 1);
+                o[step >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((step & 1) ? pa1 : pa0), cur, o[step >> 1], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            __syncthreads();  // A_{i+1}
+            lds_barrier();  // A_{i+1}
         }
         if (pass == 0) {
             if (__ballot(overflow) && lane == 0) sm.redo = 1;
-            __syncthreads();  // E
+            lds_barrier();  // E
             if (sm.redo == 0) break;
             m_ref = m_seen;  // second pass: the exact maximum, so every p <= 1
         }
     }
+
     // ---- epilogue: rows of O are heads 8(r/4) + 4hh + r%4 of this group
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -324,7 +374,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
             part_lse[ps * kMlaHeads + head0 + hl] = lse2;
         }
     }
-    __syncthreads();  // publish 1/l to the gather wave
+    lds_barrier();  // publish 1/l to the gather wave
     float ir[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) ir[r] = __shfl(inv, 8 * (r >> 2) + 4 * hh + (r & 3));

@@ -72,7 +72,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(TopkSmem& sm, uint32_t 
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const uint32_t incl = wave_inclusive_scan(v);
     if (lane == 63) sm.wtot[wave] = incl;
-    __syncthreads();
+    lds_barrier();
     uint32_t wbase = 0, tot = 0;
 #pragma unroll
     for (int i = 0; i < kTopkWaves; ++i) {
@@ -80,7 +80,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(TopkSmem& sm, uint32_t 
         wbase += (i < wave) ? x : 0u;
         tot += x;
     }
-    __syncthreads();
+    lds_barrier();
     *total = tot;
     return wbase + incl - v;
 }
@@ -104,7 +104,7 @@ __device__ __forceinline__ void find_threshold_bin(TopkSmem& sm, uint32_t need) 
         sm.prm[0] = lb;
         sm.prm[1] = before + ch;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Block-wide min/max of up to four u32 values (results broadcast to all threads).
@@ -121,7 +121,7 @@ __device__ __forceinline__ void block_minmax(TopkSmem& sm, uint32_t& a_min, uint
         sm.red[2][wave] = b_min;
         sm.red[3][wave] = b_max;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < kTopkWaves; ++i) {
         a_min = min(a_min, sm.red[0][i]);
@@ -129,7 +129,7 @@ __device__ __forceinline__ void block_minmax(TopkSmem& sm, uint32_t& a_min, uint
         b_min = min(b_min, sm.red[2][i]);
         b_max = max(b_max, sm.red[3][i]);
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 template <int E, bool STREAM>
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     {
         const int sh = value_mode ? 0 : shift_for(rhi - rlo);
         for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
-        __syncthreads();
+        lds_barrier();
         for (int ch = 0; ch < n_chunks; ++ch) {
             if (STREAM) load(ch);
 #pragma unroll
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
                 if (k) atomicAdd(&sm.hist[value_mode ? value_bin(k, lo, scale) : static_cast<int>((k - rlo) >> sh)], 1u);
             }
         }
-        __syncthreads();
+        lds_barrier();
         find_threshold_bin(sm, need);
         const uint32_t bstar = sm.prm[0];
         need -= sm.prm[1];
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             const uint64_t nhi = nlo + ((1ull << sh) - 1);
             rlo = static_cast<uint32_t>(nlo);
             rhi = nhi < rhi ? static_cast<uint32_t>(nhi) : rhi;
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     for (int level = 0; level < 4 && cand != need && rlo != rhi; ++level) {
         const int sh = shift_for(rhi - rlo);
         for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
-        __syncthreads();
+        lds_barrier();
         for (int ch = 0; ch < n_chunks; ++ch) {
             if (STREAM) load(ch);
 #pragma unroll
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
                 if (k >= rlo && k <= rhi) atomicAdd(&sm.hist[(k - rlo) >> sh], 1u);
             }
         }
-        __syncthreads();
+        lds_barrier();
         find_threshold_bin(sm, need);
         const uint32_t bstar = sm.prm[0];
         need -= sm.prm[1];
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         const uint64_t nhi = nlo + ((1ull << sh) - 1);
         rlo = static_cast<uint32_t>(nlo);
         rhi = nhi < rhi ? static_cast<uint32_t>(nhi) : rhi;
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- ordered compaction.  Selected: every key above the range, plus either the whole
@@ -289,12 +289,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
                 const uint64_t m = __ballot(key[e] == thr);
                 if (lane == 0) sm.cnt[e * kTopkWaves + wave] = __popcll(m);
             }
-            __syncthreads();
+            lds_barrier();
             const uint32_t v = tid < E * kTopkWaves ? sm.cnt[tid] : 0u;
             uint32_t total;
             const uint32_t ex = block_exclusive_scan(sm, v, &total);
             if (tid < E * kTopkWaves) sm.cnt[tid] = ex;
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const uint64_t m = __ballot(key[e] == thr);
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
                 if (key[e] == thr && rank < need) tie_ok64 |= 1ull << e;
             }
             tie_base += total;
-            __syncthreads();
+            lds_barrier();
         }
         auto selected = [&](int e) -> bool {
             const uint32_t k = key[e];
@@ -314,12 +314,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             const uint64_t m = __ballot(selected(e));
             if (lane == 0) sm.cnt[e * kTopkWaves + wave] = __popcll(m);
         }
-        __syncthreads();
+        lds_barrier();
         const uint32_t v = tid < E * kTopkWaves ? sm.cnt[tid] : 0u;
         uint32_t total;
         const uint32_t ex = block_exclusive_scan(sm, v, &total);
         if (tid < E * kTopkWaves) sm.cnt[tid] = ex;
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const bool s = selected(e);
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
                 out[rank] = static_cast<int32_t>(ch * kChunk + static_cast<int64_t>(e) * kTopkThreads + tid);
         }
         out_base += total;
-        __syncthreads();
+        lds_barrier();
     }
 }
 
