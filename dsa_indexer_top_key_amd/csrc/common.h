@@ -21,6 +21,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -51,33 +53,59 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
+// Cross-lane moves through DPP (data-parallel primitives on the VALU, no LDS round trip).
+// Controls: quad_perm [1,0,3,2] and [2,3,0,1] swap lanes at distance 1 and 2, row_half_mirror
+// reverses each group of 8 lanes, row_mirror each row of 16, row_shr:n shifts a row right by
+// n, row_bcast:15 / row_bcast:31 broadcast lane 15 / 31 of a row into the following rows
+// (the rows written are chosen by row_mask).  Lanes that are not written keep `old`.
+constexpr int dpp_row_shr(int n) { return 0x110 + n; }
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        static_cast<int>(old), static_cast<int>(v), Ctrl, RowMask, 0xF, false));
+}
+
+// Reduction over the 64 lanes of a wave; the result is wave-uniform.  Four DPP steps reduce
+// each row of 16 lanes, then the four row results are combined through scalar registers.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+    v = op(v, dpp_u32<kDppQuadXor1>(v, v));
+    v = op(v, dpp_u32<kDppQuadXor2>(v, v));
+    v = op(v, dpp_u32<kDppRowHalfMirror>(v, v));
+    v = op(v, dpp_u32<kDppRowMirror>(v, v));
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return op(op(r0, r1), op(r2, r3));
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m)));
-    return v;
+    return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m)));
-    return v;
+    return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane order): shifts by 1, 2, 4, 8 within
+// each row of 16, then the running totals of rows 0 and 0..1 are carried into later rows.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-    const int l = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t o = static_cast<uint32_t>(__shfl_up(static_cast<int>(v), d));
-        if (l >= d) v += o;
-    }
+    v += dpp_u32<dpp_row_shr(1)>(0u, v);
+    v += dpp_u32<dpp_row_shr(2)>(0u, v);
+    v += dpp_u32<dpp_row_shr(4)>(0u, v);
+    v += dpp_u32<dpp_row_shr(8)>(0u, v);
+    v += dpp_u32<kDppRowBcast15, 0xA>(0u, v);
+    v += dpp_u32<kDppRowBcast31, 0xC>(0u, v);
     return v;
 }
 

@@ -153,9 +153,12 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, i
                                      ids, static_cast<hipStream_t>(stream)), fn);
 }
 
+// Score rows are padded to a multiple of four floats so every row starts 16-byte aligned.
+static int64_t score_ld(int64_t max_S) { return (max_S + 3) & ~static_cast<int64_t>(3); }
+
 size_t dsa_indexer_topk_workspace_size(int32_t T, int64_t max_S) {
     if (T <= 0 || max_S <= 0) return 0;
-    return round_up(static_cast<size_t>(T) * static_cast<size_t>(max_S) * sizeof(float));
+    return round_up(static_cast<size_t>(T) * static_cast<size_t>(score_ld(max_S)) * sizeof(float));
 }
 
 dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
@@ -179,10 +182,11 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
                 "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
     hipStream_t s = static_cast<hipStream_t>(stream);
     float* scores = static_cast<float*>(workspace);
+    const int64_t ld = score_ld(max_S);
     hipError_t e = dsa::launch_indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, T, B, max_S,
-                                              scores, max_S, s);
+                                              scores, ld, s);
     if (e != hipSuccess) return from_hip(e, fn);
-    return from_hip(dsa::launch_topk(scores, max_S, nullptr, kv_off, q_req, q_pos, T, max_S, ids, s),
+    return from_hip(dsa::launch_topk(scores, ld, nullptr, kv_off, q_req, q_pos, T, max_S, ids, s),
                     fn);
 }
 

@@ -17,14 +17,14 @@
 // of  S^T = C . Q^T  (v_mfma_f32_32x32x16_bf16, M = 32 gathered rows, N = 32 heads), which
 // leaves each lane with one head and 16 rows -- exactly the A-operand layout the P . V
 // product needs, so probabilities never leave registers.  The 32 x 384 output of a head
-// group accumulates in its AGPRs across the split.  Wave 3 gathers the selected rows into a
-// three-deep LDS ring with gfx950's direct global->LDS copies (one 1 KB copy per latent row,
-// wave-uniform address; companion keys 8 rows per copy), issued two tiles ahead while the
-// head groups compute S^T, and
-// computes the last 128 latent columns of all 96 heads from P fragments the head groups
-// publish in LDS.  The V operand of P . V (rows x latent dims) is read from the row-major
-// LDS tile with the transposing load ds_read_b64_tr_b16.  Barriers order LDS only, so the
-// ring copies stay in flight across them (the gather wave waits on vmcnt explicitly).
+// group accumulates in its AGPRs across the split.  The selected rows stream into a
+// three-deep LDS ring through gfx950's direct global->LDS copies, two tiles ahead; every wave
+// issues a quarter of each tile (eight latent rows of 1 KB, one copy each with a wave-uniform
+// address, and one block of eight companion rows).  Wave 3 computes the last 128 latent
+// columns of all 96 heads from P fragments the head groups publish in LDS.  The V operand of
+// P . V (rows x latent dims) is read from the row-major LDS tile with the transposing load
+// ds_read_b64_tr_b16.  Barriers order LDS only, so the ring copies stay in flight across them
+// (each wave waits on its own vmcnt before the barrier that publishes a tile).
 //
 // Softmax (fp32, log2 domain) uses a fixed per-head reference: the maximum logit of the
 // first tile.  Later probabilities p = 2^(x - ref) may exceed 1; that is exact after the
@@ -41,10 +41,10 @@ namespace dsa {
 
 constexpr int kTile = 32;                    // gathered rows per step
 constexpr int kNBuf = 3;                     // LDS ring depth
-constexpr int kLatStride = kLatent + 8;      // latent row in LDS: 1024 B + 16 B pad
+constexpr int kLatStride = kLatent + 16;     // latent row in LDS: 1024 B + 32 B pad
 constexpr int kNTiles = kLatent / 32;        // 16 output tiles of 32 latent dims
-constexpr int kHelpTiles = 4;                // computed by the gather wave for all heads
-constexpr int kConsTiles = kNTiles - kHelpTiles;  // kept by the head-group waves
+constexpr int kHelpTiles = 5;                // computed by wave 3 for all heads
+constexpr int kConsTiles = kNTiles - kHelpTiles;  // kept by the head-group waves (11)
 constexpr int kKSteps = kQK / 16;            // 36 MFMA K-steps over the 576 dims
 // K order of the 576-dim dot (any order works as long as q and the rows agree): at K-step
 // s < 32 lane half hh holds latent dims 256 hh + 8s .. +8; at s >= 32 it holds companion
@@ -53,7 +53,6 @@ constexpr int kLatSteps = kLatent / 16;      // 32
 constexpr int kQfInAcc = 12;                 // q fragments kept in accumulation registers
 constexpr int kPrefA = 4;                    // LDS prefetch depth of S^T A fragments
 constexpr int kPrefV = 4;                    // LDS prefetch depth of P.V B fragments
-constexpr int kDmaPerTile = kTile + kTile / 8;  // 32 latent rows + 4 companion blocks
 constexpr float kLn2 = 0.69314718055994531f;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -63,51 +62,63 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// One ring slot: 32 latent rows (1040-byte stride, so the 32 rows read by one A-operand
-// fetch fall in distinct banks) and 32 companion rows of 128 B whose 16-byte chunks are
-// XOR-swizzled by (row % 8) for the same reason.
+// One ring slot: 32 latent rows (1056-byte stride: the rows read by one A-operand fetch, and
+// the four rows behind each 16-lane group of a transposing V read, fall in distinct banks)
+// and 32 companion rows of 128 B whose 16-byte chunks are XOR-swizzled by (row % 8) for the
+// same reason.
 struct MlaSmem {
     uint16_t lat[kNBuf][kTile * kLatStride];
     uint16_t kpe[kNBuf][kTile * kCompanion];
-    int32_t rows[kTopK];                     // compacted request-local IDs of the split
+    int32_t rows[kTopK];                     // the split's IDs, padding replaced by ID 0
+    uint32_t tmask[kTopK / kTile];           // per tile: bit r set if row r holds a real ID
     u32x4 pfrag[3][64][2];                   // P (bf16) in A-operand layout, per head group
     float inv_l[kMlaHeads];                  // per-head 1/l at the end
-    uint32_t wcnt[4];
+    uint32_t wend[4];                        // per wave: 1 + index of its last real ID
     uint32_t redo;                           // some logit exceeded its reference by > 2^32
 };
 
-// Gather tile `tile` of the split into one ring slot with gfx950's global_load_lds_dwordx4
-// (each instruction writes 64 x 16 consecutive LDS bytes; nothing passes through registers).
-// A latent row is one instruction -- its address is wave-uniform -- and every 8 companion
-// rows are one more.  Rows past n_rows are not loaded.  Returns the number of copies issued.
-__device__ __forceinline__ int gather_tile(uint16_t* lat_buf, uint16_t* kpe_buf, int tile,
-                                           int n_rows, const int32_t* rows,
-                                           const uint16_t* latent, int64_t ld_lat,
-                                           const uint16_t* kpe, int64_t ld_kpe, int64_t base,
-                                           int lane) {
-    const int r0 = tile * kTile;
-    const int nr = min(kTile, n_rows - r0);
-    const int my_rid = (lane < nr) ? rows[r0 + lane] : 0;
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-        if (r < nr) {
-            const int64_t row = base + __builtin_amdgcn_readlane(my_rid, r);
-            __builtin_amdgcn_global_load_lds(latent + row * ld_lat + 8 * lane,
-                                             (lds_void*)(lat_buf + r * kLatStride), 16, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kTile / 8; ++i) {
-        const int r = 8 * i + (lane >> 3);
-        const int rid = __shfl(my_rid, r);
-        if (8 * i < nr) {  // uniform: the block of 8 rows has at least one valid row
-            const int c = (lane & 7) ^ (r & 7);  // this lane's LDS slot holds logical chunk c
-            const int64_t row = base + (r < nr ? rid : 0);
-            __builtin_amdgcn_global_load_lds(kpe + row * ld_kpe + 8 * c,
-                                             (lds_void*)(kpe_buf + i * 8 * kCompanion), 16, 0, 0);
-        }
-    }
-    return nr + (nr + 7) / 8;
+// Byte offset of an LDS location, as the LDS instructions and M0 take it.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
+// One direct global->LDS copy (gfx950 global_load_lds_dwordx4): lane l moves 16 bytes from its
+// own address src to LDS bytes [lds_base + 16 l, +16); nothing passes through registers.  It is
+// issued through inline assembly so the compiler does not track it -- the compiler would
+// otherwise assume the copy may alias every later LDS read and drain the LDS queue before each
+// of them, defeating the operand prefetch.  Every wait for these copies is an explicit vmcnt
+// wait.  M0 holds the (wave-uniform) LDS base; nothing else in this kernel uses M0, and one
+// wait state separates writing M0 from the copy.
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// Ring copies of one tile (32 rows; padding rows copy row 0 of the request, so every slot
+// holds finite data and every tile is exactly 36 copies).  Each head-group wave copies six
+// latent rows (rows 6 wave .. 6 wave + 5), interleaved with its S^T MFMAs; wave 3, which is
+// idle until P is published, copies the other fourteen latent rows and the four blocks of
+// eight companion rows.  Spreading the copies over all four waves keeps enough of them in
+// flight (one wave alone reaches about half the gather rate), while most of the issue stalls
+// land on the idle wave.
+constexpr int kConsRows = 6;                      // latent rows per head-group wave
+constexpr int kHelpRows = kTile - 3 * kConsRows;  // latent rows of wave 3 (14)
+constexpr int kHelpCopies = kHelpRows + kTile / 8;  // 14 latent + 4 companion blocks
+
+__device__ __forceinline__ void copy_latent_row(int64_t row, const uint16_t* latent,
+                                                int64_t ld_lat, uint32_t lds, int lane) {
+    copy_to_lds(latent + row * ld_lat + 8 * lane, lds);
+}
+
+// Companion block kb of a tile: rows 8 kb .. 8 kb + 7, lane -> row 8 kb + lane / 8; the
+// lane's LDS slot holds logical chunk (lane % 8) ^ (row % 8).
+__device__ __forceinline__ void copy_companion_block(int64_t row, int kb, const uint16_t* kpe,
+                                                     int64_t ld_kpe, uint32_t lds, int lane) {
+    const int r = 8 * kb + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    copy_to_lds(kpe + row * ld_kpe + 8 * c, lds);
 }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding
@@ -152,86 +163,119 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     const int64_t base = kv_off[b];
     const int64_t s_b = kv_off[b + 1] - base;
 
-    // ---- ordered compaction of this split's valid IDs into sm.rows
+    // ---- head-group waves: absorbed queries into registers first (the wait for the ID loads
+    // below then covers them too)
+    u32x4 qf[kKSteps];
+    if (wave < 3) {
+        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
+            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
+            // the last kQfInAcc fragments live in accumulation registers (MFMA reads its B
+            // operand from there directly), leaving VGPRs for deep LDS prefetch
+            if (s >= kKSteps - kQfInAcc) asm volatile("" : "+a"(qf[s]));
+        }
+    }
+
+    // ---- the split's IDs into LDS: padding (ID < 0 or >= S_b) becomes row 0 of the request
+    // (real data, so every ring slot stays finite) and is masked out of the softmax through a
+    // per-tile bit mask.  Tiles after the last real ID are not processed.
     const int32_t* idr = ids + static_cast<int64_t>(t) * kTopK + static_cast<int64_t>(split) * L;
     if (tid == 0) sm.redo = 0;
-    // rows past the end of a split are never loaded: start from a zeroed ring so the masked
-    // rows of a partial tile hold finite values (their probabilities are exactly 0)
-    for (int i = tid; i < static_cast<int>(kNBuf * kTile * kLatStride / 8); i += 256)
-        reinterpret_cast<u32x4*>(&sm.lat[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
-    for (int i = tid; i < static_cast<int>(kNBuf * kTile * kCompanion / 8); i += 256)
-        reinterpret_cast<u32x4*>(&sm.kpe[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
-    int n_rows = 0;
+    uint32_t end = 0;
     for (int i0 = 0; i0 < L; i0 += 256) {
         const int i = i0 + tid;
         const int32_t id = i < L ? idr[i] : -1;
         const bool ok = id >= 0 && static_cast<int64_t>(id) < s_b;
-        const uint64_t m = __ballot(ok);
-        if (lane == 0) sm.wcnt[wave] = __popcll(m);
-        lds_barrier();
-        uint32_t before = 0, total = 0;
-#pragma unroll
-        for (int wv = 0; wv < 4; ++wv) {
-            before += wv < wave ? sm.wcnt[wv] : 0u;
-            total += sm.wcnt[wv];
+        const uint64_t m = __ballot(ok);  // lanes 0..31: one tile, lanes 32..63: the next
+        if (i < L) {
+            sm.rows[i] = ok ? id : 0;
+            if ((lane & 31) == 0) sm.tmask[i / kTile] = static_cast<uint32_t>(m >> (lane & 32));
         }
-        if (ok) sm.rows[n_rows + before + __popcll(m & ((1ull << lane) - 1ull))] = id;
-        n_rows += total;
-        lds_barrier();
+        if (ok) end = static_cast<uint32_t>(i + 1);
     }
-    const int n_tiles = (n_rows + kTile - 1) / kTile;
+    end = wave_max_u32(end);
+    if (lane == 0) sm.wend[wave] = end;
+    lds_barrier();
+    end = max(max(sm.wend[0], sm.wend[1]), max(sm.wend[2], sm.wend[3]));
+    const int n_tiles = static_cast<int>((end + kTile - 1) / kTile);
     const int q16 = lane & 15;
     const int vrow = 4 * hh + (q16 >> 2);
     const int vcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
     const int64_t ps = static_cast<int64_t>(t) * nsplit + split;
 
+    // Ring copies: wave w < 3 copies latent rows 6w .. 6w + 5 of a tile, wave 3 the other
+    // fourteen and the companion blocks; copies of a tile go to ring slot tile % 3.
+    const int my_rows = wave < 3 ? kConsRows : kHelpRows;
+    const int row0 = wave < 3 ? kConsRows * wave : 3 * kConsRows;
+    // lanes 0..31 hold the tile's 32 row IDs (the copies read them with readlane)
+    auto tile_ids = [&](int tile) -> int { return sm.rows[tile * kTile + (lane & 31)]; };
+    auto copy_row_k = [&](int tile, int rid, int k) {  // k-th latent row of this wave's share
+        const int r = row0 + k;
+        const int64_t row = base + __builtin_amdgcn_readlane(rid, r);
+        copy_latent_row(row, latent, ld_lat,
+                        lds_offset(sm.lat[tile % kNBuf] + r * kLatStride), lane);
+    };
+    auto copy_companions = [&](int tile) {  // wave 3 only
+#pragma unroll
+        for (int kb = 0; kb < kTile / 8; ++kb) {
+            const int64_t row = base + sm.rows[tile * kTile + 8 * kb + (lane >> 3)];
+            copy_companion_block(row, kb, kpe, ld_kpe,
+                                 lds_offset(sm.kpe[tile % kNBuf] + kb * 8 * kCompanion), lane);
+        }
+    };
+    auto copy_all = [&](int tile) {  // this wave's whole share of a tile, back to back
+        const int rid = tile_ids(tile);
+        for (int k = 0; k < my_rows; ++k) copy_row_k(tile, rid, k);
+        if (wave == 3) copy_companions(tile);
+    };
+    // Before the barrier that publishes tile i+1 this wave's copies of tile i+1 have landed.
+    // Only the share of tile i+2 (issued during step i, after tile i+1's) may be in flight.
+    auto wait_tile = [&](bool newer_issued) {
+        if (!newer_issued)
+            wait_vmcnt<0>();
+        else if (wave < 3)
+            wait_vmcnt<kConsRows>();
+        else
+            wait_vmcnt<kHelpCopies>();
+    };
+    // Prologue of a pass: tiles 0 and 1 in flight, tile 0 landed before A_0.
+    auto prologue = [&]() {
+        if (n_tiles > 0) copy_all(0);
+        if (n_tiles > 1) copy_all(1);
+        wait_tile(n_tiles > 1);
+        lds_barrier();  // A_0
+    };
+
     // Per step i there are two barriers: A_i (tile i is in ring slot i%3) and B_i (the head
-    // groups have published P of tile i).  A second pass (rare) repeats the whole sequence.
+    // groups have published P of tile i).  During step i every wave copies its share of tile
+    // i+2 into slot (i+2)%3, last read in step i-1.  A second pass (rare) repeats everything.
     if (wave == 3) {
-        // ================= gather wave: ring producer + last latent tile of every head
+        // ================= wave 3: the last kHelpTiles latent tiles of every head
         f32x16 orest[3][kHelpTiles];
         for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
             for (int hg = 0; hg < 3; ++hg)
 #pragma unroll
                 for (int ht = 0; ht < kHelpTiles; ++ht) orest[hg][ht] = f32x16{};
-            // tiles 0 and 1; only tile 0 has to land before A_0
-            int in_flight = 0;  // copies of the newest tile still allowed in flight
-            for (int tl = 0; tl < 2 && tl < n_tiles; ++tl)
-                in_flight = gather_tile(sm.lat[tl], sm.kpe[tl], tl, n_rows, sm.rows, latent,
-                                        ld_lat, kpe, ld_kpe, base, lane);
-            if (n_tiles > 1 && in_flight == kDmaPerTile)
-                wait_vmcnt<kDmaPerTile>();
-            else
-                wait_vmcnt<0>();
-            lds_barrier();  // A_0
+            prologue();
             for (int i = 0; i < n_tiles; ++i) {
-                // While the head groups compute S^T of tile i: tile i+2 -> ring slot (i+2)%3
-                // (last read in step i-1).  Tile i+1 has to land before A_{i+1}.
-                int newest = 0;
-                if (i + 2 < n_tiles) {
-                    const int sl = (i + 2) % kNBuf;
-                    newest = gather_tile(sm.lat[sl], sm.kpe[sl], i + 2, n_rows, sm.rows, latent,
-                                         ld_lat, kpe, ld_kpe, base, lane);
-                }
+                // idle until the head groups publish P: copy this wave's share meanwhile
+                const bool more = i + 2 < n_tiles;
+                if (more) copy_all(i + 2);
                 lds_barrier();  // B_i
                 const uint16_t* vbase = sm.lat[i % kNBuf] + vrow * kLatStride + vcol;
 #pragma unroll
-                for (int ht = 0; ht < kHelpTiles; ++ht) {
-                    const bf16x8 v0 = v_fragment(vbase, kConsTiles + ht, 0);
-                    const bf16x8 v1 = v_fragment(vbase, kConsTiles + ht, 1);
+                for (int c = 0; c < 2; ++c)
 #pragma unroll
-                    for (int hg = 0; hg < 3; ++hg) {
-                        orest[hg][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][0]), v0, orest[hg][ht], 0, 0, 0);
-                        orest[hg][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][1]), v1, orest[hg][ht], 0, 0, 0);
-                    }
+                for (int ht = 0; ht < kHelpTiles; ++ht) {
+                    const bf16x8 v = v_fragment(vbase, kConsTiles + ht, c);
+#pragma unroll
+                    for (int hg = 0; hg < 3; ++hg)
+                        orest[hg][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][c]), v, orest[hg][ht], 0, 0, 0);
                 }
-                // a full tile is exactly kDmaPerTile copies, so vmcnt <= kDmaPerTile leaves
-                // only tile i+2 in flight; after a partial (last) tile wait for everything
-                if (newest == kDmaPerTile)
-                    wait_vmcnt<kDmaPerTile>();
-                else
-                    wait_vmcnt<0>();
+                wait_tile(more);
                 lds_barrier();  // A_{i+1}
             }
             if (pass == 0) {
@@ -261,18 +305,6 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     }
 
     // ================= head-group waves: heads 32*wave .. 32*wave+31
-    u32x4 qf[kKSteps];
-    {
-        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
-#pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
-            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
-            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
-            // the last kQfInAcc fragments live in accumulation registers (MFMA reads its B
-            // operand from there directly), leaving VGPRs for deep LDS prefetch
-            if (s >= kKSteps - kQfInAcc) asm volatile("" : "+a"(qf[s]));
-        }
-    }
     f32x16 o[kConsTiles];
     float m_ref = -INFINITY;   // reference logit of this lane's head (log2 domain)
     float m_seen = -INFINITY;  // largest logit seen (exact maximum after a full pass)
@@ -283,8 +315,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         for (int nt = 0; nt < kConsTiles; ++nt) o[nt] = f32x16{};
         l_run = 0.f;
         bool overflow = false;
-        lds_barrier();  // A_0
+        prologue();
         for (int i = 0; i < n_tiles; ++i) {
+            const bool more = i + 2 < n_tiles;
+            const int rid = more ? tile_ids(i + 2) : 0;
+            const uint32_t tmask = sm.tmask[i];
             const uint16_t* lat_row = sm.lat[i % kNBuf] + hl * kLatStride + 256 * hh;
             const uint16_t* kpe_row = sm.kpe[i % kNBuf] + hl * kCompanion;
             // A fragment of K-step s (same K order as qf); companion chunks are swizzled
@@ -293,9 +328,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
                                                   : kpe_row + 8 * ((4 * hh + s - kLatSteps) ^ sw);
                 return *reinterpret_cast<const u32x4*>(p);
             };
-            // ---- S^T tile (32 rows x 32 heads): A = gathered rows (LDS, two steps ahead),
-            // B = q registers
-            f32x16 sacc = {};
+            // ---- S^T tile (32 rows x 32 heads): A = gathered rows (LDS, prefetched), B = q
+            // registers; two accumulation chains (even / odd K-steps) keep consecutive MFMAs
+            // independent.  This wave's rows of tile i+2 are copied one every four K-steps.
+            f32x16 sacc = {}, sacc1 = {};
             u32x4 abuf[kPrefA];
 #pragma unroll
             for (int k = 0; k < kPrefA; ++k) abuf[k] = afrag(k);
@@ -303,54 +339,69 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
             for (int s = 0; s < kKSteps; ++s) {
                 const u32x4 cur = abuf[s % kPrefA];
                 if (s + kPrefA < kKSteps) abuf[s % kPrefA] = afrag(s + kPrefA);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qf[s]), sacc, 0, 0, 0);
+                if ((s & 3) == 1 && (s >> 2) < kConsRows && more) copy_row_k(i + 2, rid, s >> 2);
+                if (s & 1)
+                    sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qf[s]), sacc1, 0, 0, 0);
+                else
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qf[s]), sacc, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            sacc += sacc1;
             // ---- probabilities relative to the fixed per-head reference
-            const int valid_rows = n_rows - i * kTile;
-            float mx = -INFINITY;
+            if (tmask != 0xffffffffu) {  // uniform: the tile holds padding rows
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
-                sacc[r] = row < valid_rows ? sacc[r] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, sacc[r]);
+                for (int r = 0; r < 16; ++r)
+                    if (!((tmask >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u)) sacc[r] = -INFINITY;
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            float mx = sacc[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // scale > 0 keeps the order
             m_seen = fmaxf(m_seen, mx);
             if (m_ref == -INFINITY) m_ref = mx;  // first tile of pass 0 (uniform per head)
             overflow |= mx > m_ref + 32.f;
             const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+            // p = 2^(x scale - m_ref) with one rounding before the raw v_exp_f32; results below
+            // 2^-126 flush to zero (under bf16's normal range: below 2^-100 of the sum)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[r] = exp2f(sacc[r] - m_use);
-            // P enters P . V in bf16; the normaliser sums the same rounded values, so the read
-            // is an exact convex combination of the rounded weights (a dominant row's rounding
-            // cancels instead of showing up as a 2^-9 relative error of the output)
+            for (int r = 0; r < 16; ++r)
+                sacc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, -m_use));
+            // P enters P . V in bf16 (v_cvt_pk_bf16_f32 rounds to nearest even); the normaliser
+            // sums the same rounded values (v_dot2 against 1.0), so the read is an exact convex
+            // combination of the rounded weights (a dominant row's rounding cancels instead of
+            // showing up as a 2^-9 relative error of the output)
             u32x4 pa0, pa1;
-            float psum = 0.f;
+            const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+            float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                pa0[k] = pack_bf16x2(sacc[2 * k], sacc[2 * k + 1]);
-                pa1[k] = pack_bf16x2(sacc[8 + 2 * k], sacc[8 + 2 * k + 1]);
-                psum += (__uint_as_float(pa0[k] << 16) + __uint_as_float(pa0[k] & 0xffff0000u)) +
-                        (__uint_as_float(pa1[k] << 16) + __uint_as_float(pa1[k] & 0xffff0000u));
+                const bf16x2 b0 = __builtin_convertvector((f32x2{sacc[2 * k], sacc[2 * k + 1]}), bf16x2);
+                const bf16x2 b1 = __builtin_convertvector((f32x2{sacc[8 + 2 * k], sacc[9 + 2 * k]}), bf16x2);
+                pa0[k] = __builtin_bit_cast(uint32_t, b0);
+                pa1[k] = __builtin_bit_cast(uint32_t, b1);
+                psum0 = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, psum0, false);
+                psum1 = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, psum1, false);
             }
-            l_run += psum;
+            l_run += psum0 + psum1;
             sm.pfrag[wave][lane][0] = pa0;
             sm.pfrag[wave][lane][1] = pa1;
             lds_barrier();  // B_i
-            // ---- O += P . V over this wave's 15 latent tiles (V fragments two steps ahead)
+            // ---- O += P . V over this wave's latent tiles; step = c * kConsTiles + nt, so
+            // both K-halves of a tile are kConsTiles MFMAs apart
             const uint16_t* vbase = sm.lat[i % kNBuf] + vrow * kLatStride + vcol;
             bf16x8 vbuf[kPrefV];
 #pragma unroll
-            for (int k = 0; k < kPrefV; ++k) vbuf[k] = v_fragment(vbase, k >> 1, k & 1);
+            for (int k = 0; k < kPrefV; ++k) vbuf[k] = v_fragment(vbase, k % kConsTiles, k / kConsTiles);
 #pragma unroll
             for (int step = 0; step < 2 * kConsTiles; ++step) {
                 const bf16x8 cur = vbuf[step % kPrefV];
-                if (step + kPrefV < 2 * kConsTiles)
-                    vbuf[step % kPrefV] = v_fragment(vbase, (step + kPrefV) >> 1, (step + kPrefV) & 1);
-                o[step >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8((step & 1) ? pa1 : pa0), cur, o[step >> 1], 0, 0, 0);
+                const int nx = step + kPrefV;
+                if (nx < 2 * kConsTiles) vbuf[step % kPrefV] = v_fragment(vbase, nx % kConsTiles, nx / kConsTiles);
+                const int nt = step % kConsTiles;
+                o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(step < kConsTiles ? pa0 : pa1), cur, o[nt], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            wait_tile(more);
             lds_barrier();  // A_{i+1}
         }
         if (pass == 0) {

@@ -59,9 +59,9 @@ __device__ __forceinline__ int shift_for(uint32_t span) {
 
 struct TopkSmem {
     uint32_t hist[kBins];
-    uint32_t cnt[kTopkThreads];
     uint32_t wtot[kTopkWaves];
     uint32_t red[4][kTopkWaves];
+    uint32_t cnt[2][2 * kTopkWaves];  // per-wave (above, tie) counts, double-buffered by chunk
     uint32_t prm[8];
 };
 
@@ -132,12 +132,61 @@ __device__ __forceinline__ void block_minmax(TopkSmem& sm, uint32_t& a_min, uint
     lds_barrier();
 }
 
-template <int E, bool STREAM>
+// Exact key interval of value bin `bin` among keys in [a, b]: the smallest key whose bin is
+// >= bin and the largest whose bin is <= bin (value_bin is monotone, so the keys of one bin
+// form an interval; both ends exist because some key in [a, b] falls in the bin).  One wave:
+// lanes 0..31 run a 32-ary search for the lower end, lanes 32..63 for the upper end; each
+// step keeps one of 32 sub-intervals, so seven steps cover the 32-bit key space.
+__device__ __forceinline__ void value_bin_key_range(uint32_t a, uint32_t b, int bin, float lo,
+                                                    float scale, uint32_t* r_lo, uint32_t* r_hi) {
+    const int lane = lane_id();
+    const uint32_t j = static_cast<uint32_t>(lane & 31);
+    const bool up = lane >= 32;
+    uint32_t l = a, h = b;  // the end this half-wave looks for lies in [l, h]
+    for (int step = 0; step < 10; ++step) {
+        if (!__ballot(l != h)) break;
+        const uint64_t w = static_cast<uint64_t>(h - l) + 1u;
+        auto off = [&](uint32_t i) { return static_cast<uint32_t>((w * i) >> 5); };
+        // lower end: probes ascend from l and pass once the bin reaches `bin`;
+        // upper end: probes descend from h and pass once the bin drops to `bin`
+        const uint32_t k = up ? h - off(j) : l + off(j);
+        const int vb = value_bin(k, lo, scale);
+        const uint64_t m = __ballot(up ? vb <= bin : vb >= bin);
+        const uint32_t half = static_cast<uint32_t>(up ? (m >> 32) : (m & 0xffffffffu));
+        const uint32_t j0 = half ? static_cast<uint32_t>(__builtin_ctz(half)) : 32u;
+        if (l == h) continue;
+        if (j0 == 0) {
+            if (up) l = h; else h = l;
+        } else if (up) {
+            const uint32_t nh = h - off(j0 - 1) - 1u;
+            l = j0 < 32 ? h - off(j0) : l;
+            h = nh;
+        } else {
+            const uint32_t nl = l + off(j0 - 1) + 1u;
+            h = j0 < 32 ? l + off(j0) : h;
+            l = nl;
+        }
+    }
+    *r_lo = __builtin_amdgcn_readlane(l, 0);
+    *r_hi = __builtin_amdgcn_readlane(h, 32);
+}
+
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t m, uint32_t acc) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), acc));
+}
+
+// Element e = 4g + c of a thread sits at offset 64E*wave + 256g + 4*lane + c of its chunk of
+// 1024E positions: each wave owns a contiguous span, each load instruction reads 1 KB
+// contiguous, and position order is (wave, g, lane, c) -- which the ordered compaction uses
+// to rank elements with ballots and scalar running counts instead of block scans.
+template <int E, bool STREAM, bool VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
     const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
     const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids) {
-    static_assert(E * kTopkWaves <= kTopkThreads, "per-(element, wave) counts must fit");
+    static_assert(E % 4 == 0, "elements come in groups of four consecutive positions");
+    constexpr int kGroups = E / 4;
     __shared__ TopkSmem sm;
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
@@ -162,12 +211,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* row = scores + static_cast<int64_t>(t) * ld;
     constexpr int64_t kChunk = static_cast<int64_t>(kTopkThreads) * E;
     const int n_chunks = STREAM ? static_cast<int>((n + kChunk - 1) / kChunk) : 1;
+    const int64_t tbase = static_cast<int64_t>(wave) * 64 * E + 4 * lane;
     uint32_t key[E];
     auto load = [&](int ch) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int64_t p = ch * kChunk + static_cast<int64_t>(e) * kTopkThreads + tid;
-            key[e] = p < n ? score_key(row[p]) : 0u;
+        for (int g = 0; g < kGroups; ++g) {
+            const int64_t p = ch * kChunk + tbase + 256 * g;
+            if (VEC && p + 3 < n) {
+                const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + p));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) key[4 * g + c] = score_key(v[c]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) key[4 * g + c] = p + c < n ? score_key(row[p + c]) : 0u;
+            }
         }
     };
     if (!STREAM) load(0);
@@ -189,6 +246,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             }
         }
     }
+    for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;  // ordered by the barriers below
     block_minmax(sm, fmin, fmax, amin, amax);
 
     bool value_mode = false;
@@ -207,8 +265,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     // ---- level 0
     {
         const int sh = value_mode ? 0 : shift_for(rhi - rlo);
-        for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
-        lds_barrier();
         for (int ch = 0; ch < n_chunks; ++ch) {
             if (STREAM) load(ch);
 #pragma unroll
@@ -223,21 +279,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         need -= sm.prm[1];
         cand = sm.hist[bstar];
         if (value_mode) {
-            uint32_t mn = ~0u, mx = 0u, d0 = ~0u, d1 = 0u;
-            for (int ch = 0; ch < n_chunks; ++ch) {
-                if (STREAM) load(ch);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const uint32_t k = key[e];
-                    if (k && value_bin(k, lo, scale) == static_cast<int>(bstar)) {
-                        mn = min(mn, k);
-                        mx = max(mx, k);
-                    }
+            if (wave == 0) {
+                uint32_t klo, khi;
+                value_bin_key_range(rlo, rhi, static_cast<int>(bstar), lo, scale, &klo, &khi);
+                if (lane == 0) {
+                    sm.prm[2] = klo;
+                    sm.prm[3] = khi;
                 }
             }
-            block_minmax(sm, mn, mx, d0, d1);
-            rlo = mn;
-            rhi = mx;
+            lds_barrier();
+            rlo = sm.prm[2];
+            rhi = sm.prm[3];
         } else {
             const uint64_t nlo = static_cast<uint64_t>(rlo) + (static_cast<uint64_t>(bstar) << sh);
             const uint64_t nhi = nlo + ((1ull << sh) - 1);
@@ -273,63 +325,80 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         lds_barrier();
     }
 
-    // ---- ordered compaction.  Selected: every key above the range, plus either the whole
-    // range (cand == need) or, when the range is the single key rlo, its `need` lowest
-    // positions.
+    // ---- ordered compaction.  "Above" keys are taken outright: every key above the final
+    // range, plus the whole range when it is taken whole (cand == need).  Otherwise the range
+    // is the single key rlo and its "tie" keys are taken in position order until `need` of
+    // them are in.  The output slot of a selected element is
+    //   #above before it + min(#ties before it, need).
+    // (Keys never exceed the key of +inf, so rlo + 1 does not wrap.)
     const bool take_all = (cand == need);
-    const uint32_t thr = rlo;
-    const uint64_t below = (1ull << lane) - 1ull;
-    uint32_t tie_base = 0, out_base = 0;
+    const uint32_t above_min = take_all ? rlo : rlo + 1u;  // keys >= this are "above"
+    const uint32_t tie_key = take_all ? 0xFFFFFFFFu : rlo;  // never a key when take_all
+    uint32_t above_done = 0, tie_done = 0;  // counts of earlier chunks (block-uniform)
     for (int ch = 0; ch < n_chunks; ++ch) {
         if (STREAM) load(ch);
-        uint64_t tie_ok64 = 0;  // bit e: element e is a tie at the threshold that is kept
-        if (!take_all) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const uint64_t m = __ballot(key[e] == thr);
-                if (lane == 0) sm.cnt[e * kTopkWaves + wave] = __popcll(m);
-            }
-            lds_barrier();
-            const uint32_t v = tid < E * kTopkWaves ? sm.cnt[tid] : 0u;
-            uint32_t total;
-            const uint32_t ex = block_exclusive_scan(sm, v, &total);
-            if (tid < E * kTopkWaves) sm.cnt[tid] = ex;
-            lds_barrier();
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const uint64_t m = __ballot(key[e] == thr);
-                const uint32_t rank = tie_base + sm.cnt[e * kTopkWaves + wave] + __popcll(m & below);
-                if (key[e] == thr && rank < need) tie_ok64 |= 1ull << e;
-            }
-            tie_base += total;
-            lds_barrier();
-        }
-        auto selected = [&](int e) -> bool {
-            const uint32_t k = key[e];
-            if (take_all) return k >= thr;
-            return k > thr || ((tie_ok64 >> e) & 1ull);
-        };
+        uint32_t na = 0, nt = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const uint64_t m = __ballot(selected(e));
-            if (lane == 0) sm.cnt[e * kTopkWaves + wave] = __popcll(m);
+            na += key[e] >= above_min ? 1u : 0u;
+            nt += key[e] == tie_key ? 1u : 0u;
+        }
+        na = wave_sum_u32(na);
+        nt = wave_sum_u32(nt);
+        uint32_t* cnt = sm.cnt[ch & 1];
+        if (lane == 0) {
+            cnt[wave] = na;
+            cnt[kTopkWaves + wave] = nt;
         }
         lds_barrier();
-        const uint32_t v = tid < E * kTopkWaves ? sm.cnt[tid] : 0u;
-        uint32_t total;
-        const uint32_t ex = block_exclusive_scan(sm, v, &total);
-        if (tid < E * kTopkWaves) sm.cnt[tid] = ex;
-        lds_barrier();
+        uint32_t a_run = above_done, t_run = tie_done, a_tot = 0, t_tot = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const bool s = selected(e);
-            const uint64_t m = __ballot(s);
-            const uint32_t rank = out_base + sm.cnt[e * kTopkWaves + wave] + __popcll(m & below);
-            if (s && rank < kTopK)
-                out[rank] = static_cast<int32_t>(ch * kChunk + static_cast<int64_t>(e) * kTopkThreads + tid);
+        for (int i = 0; i < kTopkWaves; ++i) {
+            const uint32_t x = cnt[i], y = cnt[kTopkWaves + i];
+            a_run += i < wave ? x : 0u;
+            t_run += i < wave ? y : 0u;
+            a_tot += x;
+            t_tot += y;
         }
-        out_base += total;
-        lds_barrier();
+        // opaque copies keep the compiler from holding the counting loop's 2E lane masks
+        // live (in scalar registers) until they are needed again below
+        uint32_t amin2 = above_min, tkey2 = tie_key;
+        asm volatile("" : "+v"(amin2), "+v"(tkey2));
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            uint64_t ma[4], mt[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ma[c] = __ballot(key[4 * g + c] >= amin2);
+                mt[c] = __ballot(key[4 * g + c] == tkey2);
+            }
+            // counts of this group's elements held by lower lanes, then by this lane's own
+            // earlier elements (position order within a group is lane, then c)
+            uint32_t ra = a_run, rt = t_run;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ra = mbcnt64(ma[c], ra);
+                rt = mbcnt64(mt[c], rt);
+            }
+            const int64_t p0 = ch * kChunk + tbase + 256 * g;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t k = key[4 * g + c];
+                const bool ia = k >= amin2, it = k == tkey2;
+                const uint32_t rank = ra + (rt < need ? rt : need);
+                if ((ia || (it && rt < need)) && rank < kTopK)
+                    out[rank] = static_cast<int32_t>(p0 + c);
+                ra += ia ? 1u : 0u;
+                rt += it ? 1u : 0u;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                a_run += static_cast<uint32_t>(__popcll(ma[c]));
+                t_run += static_cast<uint32_t>(__popcll(mt[c]));
+            }
+        }
+        above_done += a_tot;
+        tie_done += t_tot;
     }
 }
 
@@ -337,8 +406,13 @@ template <int E, bool STREAM>
 static void launch_topk_e(const float* scores, int64_t ld, const int32_t* n_valid,
                           const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
                           int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream) {
-    hipLaunchKernelGGL((topk_kernel<E, STREAM>), dim3(T), dim3(kTopkThreads), 0, stream, scores,
-                       ld, n_valid, kv_off, q_req, q_pos, max_n, ids);
+    const bool vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (ld % 4 == 0);
+    if (vec)
+        hipLaunchKernelGGL((topk_kernel<E, STREAM, true>), dim3(T), dim3(kTopkThreads), 0,
+                           stream, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids);
+    else
+        hipLaunchKernelGGL((topk_kernel<E, STREAM, false>), dim3(T), dim3(kTopkThreads), 0,
+                           stream, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids);
 }
 
 // Either n_valid (explicit row lengths) or (kv_off, q_req, q_pos) gives each row's length.

@@ -132,7 +132,8 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, i
  * ids       [T,2048] int32 out: request-local position IDs, selected set in ascending
  *           order, then -1 padding (short prefixes n_t <= 2048 select all of [0, n_t)).
  * workspace device buffer of at least dsa_indexer_topk_workspace_size(T, max_S) bytes,
- *           256-byte aligned (holds the fp32 scores of every admissible position).
+ *           256-byte aligned (holds the fp32 scores of every admissible position, rows
+ *           padded to a multiple of four floats).
  */
 size_t dsa_indexer_topk_workspace_size(int32_t T, int64_t max_S);
 dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
