@@ -39,7 +39,7 @@ __device__ __forceinline__ int64_t admissible(const int64_t* kv_off, int b, int3
 // decode
 // ---------------------------------------------------------------------------------------
 constexpr int kDecodeChunk = 2048;  // keys per block
-constexpr int kDecodeUnroll = 4;    // 16-key tiles in flight per wave
+constexpr int kDecodeUnroll = 1;    // 16-key tiles in flight per wave (more in flight measured slower)
 
 // grid: one block per (query, chunk of kDecodeChunk keys); 4 waves per block.
 // MFMA 16x16x32: A = q (rows: 16 heads), B = keys (cols: 16 keys), K = 32 dims per step.
