@@ -189,7 +189,7 @@ def main():
         dsa.index_keys_layernorm(d["raw_keys"], d["gamma"], d["beta"], synth.LN_EPS, keys=keys)
 
     if args.profile_kernels:
-        for _ in range(3):
+        for _ in range(10):
             step()
             scores_only()
             topk_only()
