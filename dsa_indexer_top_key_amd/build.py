@@ -21,6 +21,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa_amd.so")
 SOURCES = ["ln_keys.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "dsa_api.cpp"]
+# Per-file code-generation options.  sparse_mla: MFMA results in VGPRs where they fit (its
+# output accumulators then stay put; with the default AGPR form the register allocator
+# shuttled one output tile between AGPRs and VGPRs around every S^T chain).
+EXTRA_FLAGS = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 
@@ -39,7 +43,8 @@ def common_flags():
 
 def compile_one(src: str, remarks: bool) -> tuple[str, str]:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if remarks:
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

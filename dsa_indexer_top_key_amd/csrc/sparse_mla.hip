@@ -41,7 +41,7 @@ namespace dsa {
 
 constexpr int kTile = 32;                    // gathered rows per step
 constexpr int kNBuf = 3;                     // LDS ring depth
-constexpr int kLatStride = kLatent + 16;     // latent row in LDS: 1024 B + 32 B pad
+constexpr int kLatStride = kLatent + 24;     // latent row in LDS: 1024 B + 48 B pad
 constexpr int kNTiles = kLatent / 32;        // 16 output tiles of 32 latent dims
 constexpr int kHelpTiles = 5;                // computed by wave 3 for all heads
 constexpr int kConsTiles = kNTiles - kHelpTiles;  // kept by the head-group waves (11)
@@ -58,11 +58,15 @@ constexpr float kLn2 = 0.69314718055994531f;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+
+// The transposing read takes an LDS-address-space pointer: offsets added there fold into the
+// instruction's immediate (a generic pointer cast per read costs a VALU add and a VGPR each).
+__device__ __forceinline__ bf16x4 lds_read_tr16(lds_u16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// One ring slot: 32 latent rows (1056-byte stride: the rows read by one A-operand fetch, and
+// One ring slot: 32 latent rows (1072-byte stride: the rows read by one A-operand fetch, and
 // the four rows behind each 16-lane group of a transposing V read, fall in distinct banks)
 // and 32 companion rows of 128 B whose 16-byte chunks are XOR-swizzled by (row % 8) for the
 // same reason.
@@ -71,7 +75,8 @@ struct MlaSmem {
     uint16_t kpe[kNBuf][kTile * kCompanion];
     int32_t rows[kTopK];                     // the split's IDs, padding replaced by ID 0
     uint32_t tmask[kTopK / kTile];           // per tile: bit r set if row r holds a real ID
-    u32x4 pfrag[3][64][2];                   // P (bf16) in A-operand layout, per head group
+    u32x4 pfrag[2][3][64][2];                // P (bf16) in A-operand layout, per head group,
+                                             // double-buffered by tile parity
     float inv_l[kMlaHeads];                  // per-head 1/l at the end
     uint32_t wend[4];                        // per wave: 1 + index of its last real ID
     uint32_t redo;                           // some logit exceeded its reference by > 2^32
@@ -97,15 +102,13 @@ __device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_base) 
 }
 
 // Ring copies of one tile (32 rows; padding rows copy row 0 of the request, so every slot
-// holds finite data and every tile is exactly 36 copies).  Each head-group wave copies six
-// latent rows (rows 6 wave .. 6 wave + 5), interleaved with its S^T MFMAs; wave 3, which is
-// idle until P is published, copies the other fourteen latent rows and the four blocks of
-// eight companion rows.  Spreading the copies over all four waves keeps enough of them in
-// flight (one wave alone reaches about half the gather rate), while most of the issue stalls
-// land on the idle wave.
-constexpr int kConsRows = 6;                      // latent rows per head-group wave
-constexpr int kHelpRows = kTile - 3 * kConsRows;  // latent rows of wave 3 (14)
-constexpr int kHelpCopies = kHelpRows + kTile / 8;  // 14 latent + 4 companion blocks
+// holds finite data and every tile is exactly 36 copies).  Every wave copies eight latent
+// rows (rows 8 wave .. 8 wave + 7); the head-group waves interleave theirs with their S^T
+// MFMAs, wave 3 also copies the four blocks of eight companion rows.  Spreading the copies
+// over all four waves keeps enough of them in flight: one wave alone reaches about half the
+// gather rate.
+constexpr int kConsRows = kTile / 4;            // latent rows per wave (8)
+constexpr int kHelpCopies = kConsRows + kTile / 8;  // wave 3: 8 latent rows + 4 companion blocks
 
 __device__ __forceinline__ void copy_latent_row(int64_t row, const uint16_t* latent,
                                                 int64_t ld_lat, uint32_t lds, int lane) {
@@ -134,8 +137,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // 16c + 8 + 4hh + {0..3} (hh = l / 32), matching the P fragment's row order.  Within each
 // 16-lane group, lane q points at row q/4, columns 4(q%4)..4(q%4)+3 of a 4 x 16 block; the
 // transposing load returns column q of the block's four rows.
-__device__ __forceinline__ bf16x8 v_fragment(const uint16_t* vbase, int nt, int c) {
-    const uint16_t* vp = vbase + 16 * c * kLatStride + 32 * nt;
+__device__ __forceinline__ bf16x8 v_fragment(lds_u16* vbase, int nt, int c) {
+    lds_u16* vp = vbase + 16 * c * kLatStride + 32 * nt;
     const bf16x4 v0 = lds_read_tr16(vp);
     const bf16x4 v1 = lds_read_tr16(vp + 8 * kLatStride);
     return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -155,28 +158,13 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     if (t >= T) return;
     const int tid = threadIdx.x;
     const int lane = lane_id();
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
     const int hh = lane >> 5;  // lane half
     const int hl = lane & 31;  // head column (S^T) / A-operand row
     const int L = kTopK / nsplit;
     const int b = q_req[t];
     const int64_t base = kv_off[b];
     const int64_t s_b = kv_off[b + 1] - base;
-
-    // ---- head-group waves: absorbed queries into registers first (the wait for the ID loads
-    // below then covers them too)
-    u32x4 qf[kKSteps];
-    if (wave < 3) {
-        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
-#pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
-            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
-            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
-            // the last kQfInAcc fragments live in accumulation registers (MFMA reads its B
-            // operand from there directly), leaving VGPRs for deep LDS prefetch
-            if (s >= kKSteps - kQfInAcc) asm volatile("" : "+a"(qf[s]));
-        }
-    }
 
     // ---- the split's IDs into LDS: padding (ID < 0 or >= S_b) becomes row 0 of the request
     // (real data, so every ring slot stays finite) and is masked out of the softmax through a
@@ -205,10 +193,9 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     const int vcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
     const int64_t ps = static_cast<int64_t>(t) * nsplit + split;
 
-    // Ring copies: wave w < 3 copies latent rows 6w .. 6w + 5 of a tile, wave 3 the other
-    // fourteen and the companion blocks; copies of a tile go to ring slot tile % 3.
-    const int my_rows = wave < 3 ? kConsRows : kHelpRows;
-    const int row0 = wave < 3 ? kConsRows * wave : 3 * kConsRows;
+    // Ring copies: wave w < 3 copies latent rows 8w .. 8w + 7 of a tile, wave 3 rows 24 .. 31
+    // and the four companion blocks; copies of a tile go to ring slot tile % 3.
+    const int row0 = kConsRows * wave;
     // lanes 0..31 hold the tile's 32 row IDs (the copies read them with readlane)
     auto tile_ids = [&](int tile) -> int { return sm.rows[tile * kTile + (lane & 31)]; };
     auto copy_row_k = [&](int tile, int rid, int k) {  // k-th latent row of this wave's share
@@ -227,30 +214,31 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     };
     auto copy_all = [&](int tile) {  // this wave's whole share of a tile, back to back
         const int rid = tile_ids(tile);
-        for (int k = 0; k < my_rows; ++k) copy_row_k(tile, rid, k);
+#pragma unroll
+        for (int k = 0; k < kConsRows; ++k) copy_row_k(tile, rid, k);
         if (wave == 3) copy_companions(tile);
     };
-    // Before the barrier that publishes tile i+1 this wave's copies of tile i+1 have landed.
-    // Only the share of tile i+2 (issued during step i, after tile i+1's) may be in flight.
-    auto wait_tile = [&](bool newer_issued) {
-        if (!newer_issued)
-            wait_vmcnt<0>();
-        else if (wave < 3)
-            wait_vmcnt<kConsRows>();
-        else
-            wait_vmcnt<kHelpCopies>();
-    };
-    // Prologue of a pass: tiles 0 and 1 in flight, tile 0 landed before A_0.
+    // Start of a pass: tiles 0 and 1 in flight, tile 0 published by the first barrier; each
+    // wave's copies of tile 1 land before X_0.
     auto prologue = [&]() {
         if (n_tiles > 0) copy_all(0);
-        if (n_tiles > 1) copy_all(1);
-        wait_tile(n_tiles > 1);
-        lds_barrier();  // A_0
+        if (n_tiles > 1) {
+            copy_all(1);
+            if (wave < 3)
+                wait_vmcnt<kConsRows>();
+            else
+                wait_vmcnt<kHelpCopies>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();  // tile 0 published
     };
 
-    // Per step i there are two barriers: A_i (tile i is in ring slot i%3) and B_i (the head
-    // groups have published P of tile i).  During step i every wave copies its share of tile
-    // i+2 into slot (i+2)%3, last read in step i-1.  A second pass (rare) repeats everything.
+    // Software pipeline, one barrier per step.  X_i (i >= 0) publishes tile i+1 (ring slot
+    // (i+1)%3) and P(i) (pfrag[i%2]).  During step i every wave copies its share of tile i+2
+    // into slot (i+2)%3 (last read in step i-1); the head groups compute S of tile i+1 and,
+    // interleaved with its softmax, P(i) . V(i); wave 3 computes its latent columns of
+    // P(i) . V(i).  A second pass (rare) repeats everything.
     if (wave == 3) {
         // ================= wave 3: the last kHelpTiles latent tiles of every head
         f32x16 orest[3][kHelpTiles];
@@ -260,23 +248,31 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
 #pragma unroll
                 for (int ht = 0; ht < kHelpTiles; ++ht) orest[hg][ht] = f32x16{};
             prologue();
+            wait_vmcnt<0>();
+            lds_barrier();  // X_0
             for (int i = 0; i < n_tiles; ++i) {
-                // idle until the head groups publish P: copy this wave's share meanwhile
-                const bool more = i + 2 < n_tiles;
-                if (more) copy_all(i + 2);
-                lds_barrier();  // B_i
-                const uint16_t* vbase = sm.lat[i % kNBuf] + vrow * kLatStride + vcol;
+                if (i + 2 < n_tiles) copy_all(i + 2);
+                // all operands first (one LDS latency), then the 30 MFMAs back to back
+                lds_u16* vbase = (lds_u16*)sm.lat[i % kNBuf] + vrow * kLatStride + vcol;
+                u32x4 pf[3][2];
+                bf16x8 vf[2][kHelpTiles];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                    for (int hg = 0; hg < 3; ++hg) pf[hg][c] = sm.pfrag[i & 1][hg][lane][c];
+#pragma unroll
+                    for (int ht = 0; ht < kHelpTiles; ++ht) vf[c][ht] = v_fragment(vbase, kConsTiles + ht, c);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of all the MFMAs
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int ht = 0; ht < kHelpTiles; ++ht) {
-                    const bf16x8 v = v_fragment(vbase, kConsTiles + ht, c);
+                for (int ht = 0; ht < kHelpTiles; ++ht)
 #pragma unroll
                     for (int hg = 0; hg < 3; ++hg)
-                        orest[hg][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sm.pfrag[hg][lane][c]), v, orest[hg][ht], 0, 0, 0);
-                }
-                wait_tile(more);
-                lds_barrier();  // A_{i+1}
+                        orest[hg][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pf[hg][c]), vf[c][ht], orest[hg][ht], 0, 0, 0);
+                wait_vmcnt<0>();
+                lds_barrier();  // X_{i+1}
             }
             if (pass == 0) {
                 lds_barrier();  // E: the head groups have published their overflow flags
@@ -305,104 +301,144 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     }
 
     // ================= head-group waves: heads 32*wave .. 32*wave+31
+    u32x4 qf[kKSteps];
+    {
+        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
+            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
+            // the last kQfInAcc fragments live in accumulation registers (MFMA reads its B
+            // operand from there directly), leaving VGPRs for deep LDS prefetch
+            if (s >= kKSteps - kQfInAcc) asm volatile("" : "+a"(qf[s]));
+        }
+    }
     f32x16 o[kConsTiles];
     float m_ref = -INFINITY;   // reference logit of this lane's head (log2 domain)
     float m_seen = -INFINITY;  // largest logit seen (exact maximum after a full pass)
     float l_run = 0.f;         // this lane's partial sum of the bf16-rounded 2^(x - m_ref)
+    bool overflow = false;
     const int sw = hl & 7;     // companion-row swizzle of this lane's A row
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+    // S^T of tile `tile` (32 rows x 32 heads): A = gathered rows (LDS, prefetched), B = q
+    // registers (one accumulation chain: a second one measured no faster and pushed output
+    // accumulators out of the AGPRs).  When copy_tile >= 0 this wave's latent rows of that
+    // tile are copied one every four K-steps.
+    auto qk_tile = [&](int tile, int copy_tile) -> f32x16 {
+        const int rid = copy_tile >= 0 ? tile_ids(copy_tile) : 0;
+        const uint16_t* lat_row = sm.lat[tile % kNBuf] + hl * kLatStride + 256 * hh;
+        const uint16_t* kpe_row = sm.kpe[tile % kNBuf] + hl * kCompanion;
+        // A fragment of K-step s (same K order as qf); companion chunks are swizzled
+        auto afrag = [&](int s) -> u32x4 {
+            const uint16_t* p = s < kLatSteps ? lat_row + 8 * s
+                                              : kpe_row + 8 * ((4 * hh + s - kLatSteps) ^ sw);
+            return *reinterpret_cast<const u32x4*>(p);
+        };
+        f32x16 sacc = {};
+        u32x4 abuf[kPrefA];
+#pragma unroll
+        for (int k = 0; k < kPrefA; ++k) abuf[k] = afrag(k);
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+            const u32x4 cur = abuf[s % kPrefA];
+            if (s + kPrefA < kKSteps) abuf[s % kPrefA] = afrag(s + kPrefA);
+            if ((s & 3) == 1 && (s >> 2) < kConsRows && copy_tile >= 0) copy_row_k(copy_tile, rid, s >> 2);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qf[s]), sacc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint32_t tmask = __builtin_amdgcn_readfirstlane(sm.tmask[tile]);  // uniform
+        if (tmask != 0xffffffffu) {  // uniform: the tile holds padding rows
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (!((tmask >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u)) sacc[r] = -INFINITY;
+        }
+        return sacc;
+    };
+    // Probabilities of one S^T tile relative to the fixed per-head reference, packed to bf16
+    // in A-operand layout (pa0: K-half 0, pa1: K-half 1); the normaliser sums the rounded P.
+    auto softmax_tile = [&](f32x16 sacc, u32x4& pa0, u32x4& pa1) {
+        float mx = sacc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // scale > 0 keeps the order
+        m_seen = fmaxf(m_seen, mx);
+        if (m_ref == -INFINITY) m_ref = mx;  // first tile of pass 0 (uniform per head)
+        overflow |= mx > m_ref + 32.f;
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        // p = 2^(x scale - m_ref) with one rounding before the raw v_exp_f32; results below
+        // 2^-126 flush to zero (under bf16's normal range: below 2^-100 of the sum).  P enters
+        // P . V in bf16 (v_cvt_pk_bf16_f32 rounds to nearest even) and the normaliser sums the
+        // same rounded values (v_dot2 against 1.0), so the read is an exact convex combination
+        // of the rounded weights (a dominant row's rounding cancels instead of showing up as a
+        // 2^-9 relative error of the output).
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            sacc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, -m_use));
+        float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bf16x2 b0 = __builtin_convertvector((f32x2{sacc[2 * k], sacc[2 * k + 1]}), bf16x2);
+            const bf16x2 b1 = __builtin_convertvector((f32x2{sacc[8 + 2 * k], sacc[9 + 2 * k]}), bf16x2);
+            pa0[k] = __builtin_bit_cast(uint32_t, b0);
+            pa1[k] = __builtin_bit_cast(uint32_t, b1);
+            psum0 = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, psum0, false);
+            psum1 = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, psum1, false);
+        }
+        l_run += psum0 + psum1;
+    };
+    // O += P . V over this wave's latent tiles (V fragments prefetched from LDS); step =
+    // c * kConsTiles + nt, so both K-halves of an output tile are kConsTiles MFMAs apart.
+    auto pv_tile = [&](int tile) {
+        const u32x4 pa0 = sm.pfrag[tile & 1][wave][lane][0];
+        const u32x4 pa1 = sm.pfrag[tile & 1][wave][lane][1];
+        lds_u16* vbase = (lds_u16*)sm.lat[tile % kNBuf] + vrow * kLatStride + vcol;
+        bf16x8 vbuf[kPrefV];
+#pragma unroll
+        for (int k = 0; k < kPrefV; ++k) vbuf[k] = v_fragment(vbase, k % kConsTiles, k / kConsTiles);
+#pragma unroll
+        for (int step = 0; step < 2 * kConsTiles; ++step) {
+            const bf16x8 cur = vbuf[step % kPrefV];
+            const int nx = step + kPrefV;
+            if (nx < 2 * kConsTiles) vbuf[step % kPrefV] = v_fragment(vbase, nx % kConsTiles, nx / kConsTiles);
+            const int nt = step % kConsTiles;
+            o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(step < kConsTiles ? pa0 : pa1), cur, o[nt], 0, 0, 0);
+            // keeps the rotating prefetch (left alone, the compiler re-reads each fragment
+            // right before its MFMA and waits the full LDS latency every time)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int nt = 0; nt < kConsTiles; ++nt) o[nt] = f32x16{};
         l_run = 0.f;
-        bool overflow = false;
+        overflow = false;
         prologue();
+        if (n_tiles > 0) {
+            u32x4 p0, p1;
+            softmax_tile(qk_tile(0, -1), p0, p1);
+            sm.pfrag[0][wave][lane][0] = p0;
+            sm.pfrag[0][wave][lane][1] = p1;
+        }
+        wait_vmcnt<0>();
+        lds_barrier();  // X_0
         for (int i = 0; i < n_tiles; ++i) {
-            const bool more = i + 2 < n_tiles;
-            const int rid = more ? tile_ids(i + 2) : 0;
-            const uint32_t tmask = sm.tmask[i];
-            const uint16_t* lat_row = sm.lat[i % kNBuf] + hl * kLatStride + 256 * hh;
-            const uint16_t* kpe_row = sm.kpe[i % kNBuf] + hl * kCompanion;
-            // A fragment of K-step s (same K order as qf); companion chunks are swizzled
-            auto afrag = [&](int s) -> u32x4 {
-                const uint16_t* p = s < kLatSteps ? lat_row + 8 * s
-                                                  : kpe_row + 8 * ((4 * hh + s - kLatSteps) ^ sw);
-                return *reinterpret_cast<const u32x4*>(p);
-            };
-            // ---- S^T tile (32 rows x 32 heads): A = gathered rows (LDS, prefetched), B = q
-            // registers; two accumulation chains (even / odd K-steps) keep consecutive MFMAs
-            // independent.  This wave's rows of tile i+2 are copied one every four K-steps.
-            f32x16 sacc = {}, sacc1 = {};
-            u32x4 abuf[kPrefA];
-#pragma unroll
-            for (int k = 0; k < kPrefA; ++k) abuf[k] = afrag(k);
-#pragma unroll
-            for (int s = 0; s < kKSteps; ++s) {
-                const u32x4 cur = abuf[s % kPrefA];
-                if (s + kPrefA < kKSteps) abuf[s % kPrefA] = afrag(s + kPrefA);
-                if ((s & 3) == 1 && (s >> 2) < kConsRows && more) copy_row_k(i + 2, rid, s >> 2);
-                if (s & 1)
-                    sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qf[s]), sacc1, 0, 0, 0);
-                else
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qf[s]), sacc, 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+            // one copy of each part in the loop body (two code paths doubled the register
+            // footprint of the output accumulators)
+            const bool next = i + 1 < n_tiles;
+            u32x4 pn0 = {0u, 0u, 0u, 0u}, pn1 = {0u, 0u, 0u, 0u};
+            if (next) {
+                const f32x16 s_next = qk_tile(i + 1, i + 2 < n_tiles ? i + 2 : -1);
+                softmax_tile(s_next, pn0, pn1);
             }
-            sacc += sacc1;
-            // ---- probabilities relative to the fixed per-head reference
-            if (tmask != 0xffffffffu) {  // uniform: the tile holds padding rows
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (!((tmask >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u)) sacc[r] = -INFINITY;
+            pv_tile(i);
+            if (next) {
+                sm.pfrag[(i + 1) & 1][wave][lane][0] = pn0;
+                sm.pfrag[(i + 1) & 1][wave][lane][1] = pn1;
             }
-            float mx = sacc[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // scale > 0 keeps the order
-            m_seen = fmaxf(m_seen, mx);
-            if (m_ref == -INFINITY) m_ref = mx;  // first tile of pass 0 (uniform per head)
-            overflow |= mx > m_ref + 32.f;
-            const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-            // p = 2^(x scale - m_ref) with one rounding before the raw v_exp_f32; results below
-            // 2^-126 flush to zero (under bf16's normal range: below 2^-100 of the sum)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sacc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], scale_log2, -m_use));
-            // P enters P . V in bf16 (v_cvt_pk_bf16_f32 rounds to nearest even); the normaliser
-            // sums the same rounded values (v_dot2 against 1.0), so the read is an exact convex
-            // combination of the rounded weights (a dominant row's rounding cancels instead of
-            // showing up as a 2^-9 relative error of the output)
-            u32x4 pa0, pa1;
-            const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-            float psum0 = 0.f, psum1 = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const bf16x2 b0 = __builtin_convertvector((f32x2{sacc[2 * k], sacc[2 * k + 1]}), bf16x2);
-                const bf16x2 b1 = __builtin_convertvector((f32x2{sacc[8 + 2 * k], sacc[9 + 2 * k]}), bf16x2);
-                pa0[k] = __builtin_bit_cast(uint32_t, b0);
-                pa1[k] = __builtin_bit_cast(uint32_t, b1);
-                psum0 = __builtin_amdgcn_fdot2_f32_bf16(b0, ones, psum0, false);
-                psum1 = __builtin_amdgcn_fdot2_f32_bf16(b1, ones, psum1, false);
-            }
-            l_run += psum0 + psum1;
-            sm.pfrag[wave][lane][0] = pa0;
-            sm.pfrag[wave][lane][1] = pa1;
-            lds_barrier();  // B_i
-            // ---- O += P . V over this wave's latent tiles; step = c * kConsTiles + nt, so
-            // both K-halves of a tile are kConsTiles MFMAs apart
-            const uint16_t* vbase = sm.lat[i % kNBuf] + vrow * kLatStride + vcol;
-            bf16x8 vbuf[kPrefV];
-#pragma unroll
-            for (int k = 0; k < kPrefV; ++k) vbuf[k] = v_fragment(vbase, k % kConsTiles, k / kConsTiles);
-#pragma unroll
-            for (int step = 0; step < 2 * kConsTiles; ++step) {
-                const bf16x8 cur = vbuf[step % kPrefV];
-                const int nx = step + kPrefV;
-                if (nx < 2 * kConsTiles) vbuf[step % kPrefV] = v_fragment(vbase, nx % kConsTiles, nx / kConsTiles);
-                const int nt = step % kConsTiles;
-                o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(step < kConsTiles ? pa0 : pa1), cur, o[nt], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            wait_tile(more);
-            lds_barrier();  // A_{i+1}
+            wait_vmcnt<0>();
+            lds_barrier();  // X_{i+1}
         }
         if (pass == 0) {
             if (__ballot(overflow) && lane == 0) sm.redo = 1;
