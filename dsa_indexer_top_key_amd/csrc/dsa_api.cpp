@@ -19,7 +19,9 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const
                                  float* scores, int64_t ld, hipStream_t stream);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
-                       int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream);
+                       int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream,
+                       int32_t* cand_ws);
+size_t topk_workspace_bytes(int32_t T, int64_t max_n);
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t ld_lat,
                              const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
                              const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
@@ -150,15 +152,21 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, i
     DSA_REQUIRE(aligned(scores, 4) && aligned(n_valid, 4) && aligned(ids, 4),
                 DSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     return from_hip(dsa::launch_topk(scores, ld, n_valid, nullptr, nullptr, nullptr, T, max_n,
-                                     ids, static_cast<hipStream_t>(stream)), fn);
+                                     ids, static_cast<hipStream_t>(stream), nullptr), fn);
 }
 
 // Score rows are padded to a multiple of four floats so every row starts 16-byte aligned.
 static int64_t score_ld(int64_t max_S) { return (max_S + 3) & ~static_cast<int64_t>(3); }
 
+// Workspace: fp32 scores [T, score_ld] then, when rows are split for the selection, the
+// per-part candidate lists [T * parts, 2048] int32.
+static size_t score_bytes(int32_t T, int64_t max_S) {
+    return round_up(static_cast<size_t>(T) * static_cast<size_t>(score_ld(max_S)) * sizeof(float));
+}
+
 size_t dsa_indexer_topk_workspace_size(int32_t T, int64_t max_S) {
     if (T <= 0 || max_S <= 0) return 0;
-    return round_up(static_cast<size_t>(T) * static_cast<size_t>(score_ld(max_S)) * sizeof(float));
+    return score_bytes(T, max_S) + round_up(dsa::topk_workspace_bytes(T, max_S));
 }
 
 dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
@@ -186,7 +194,11 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
     hipError_t e = dsa::launch_indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, T, B, max_S,
                                               scores, ld, s);
     if (e != hipSuccess) return from_hip(e, fn);
-    return from_hip(dsa::launch_topk(scores, ld, nullptr, kv_off, q_req, q_pos, T, max_S, ids, s),
+    int32_t* cand = dsa::topk_workspace_bytes(T, max_S) > 0
+                        ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + score_bytes(T, max_S))
+                        : nullptr;
+    return from_hip(dsa::launch_topk(scores, ld, nullptr, kv_off, q_req, q_pos, T, max_S, ids, s,
+                                     cand),
                     fn);
 }
 

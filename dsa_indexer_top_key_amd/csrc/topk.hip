@@ -180,44 +180,78 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m, uint32_t acc) {
 // 1024E positions: each wave owns a contiguous span, each load instruction reads 1 KB
 // contiguous, and position order is (wave, g, lane, c) -- which the ordered compaction uses
 // to rank elements with ballots and scalar running counts instead of block scans.
-template <int E, bool STREAM, bool VEC>
+// What a launch of topk_kernel selects from:
+//  kRow   -- row t of the score matrix (positions 0 .. n_t-1); writes the positions;
+//  kParts -- part q of row t (block t*P + q): positions q*chunk .. q*chunk+chunk-1 of the
+//            row; writes the part's top-2048 as part-local positions to cand;
+//  kMerge -- the P part lists of row t (P*2048 candidates in ascending position order, the
+//            scores gathered again from the row); writes the selected positions.
+// A row's top-2048 is always inside the union of its parts' top-2048 lists (an element
+// beaten by 2048 others in its own part is beaten by them in the row), and the tie rule
+// (equal scores: lower position first) is the same at both levels, so the merge is exact.
+enum TopkMode { kRow = 0, kParts = 1, kMerge = 2 };
+
+template <int E, bool STREAM, bool VEC, int MODE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
     const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
-    const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids) {
+    const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids,
+    int32_t parts, int64_t chunk, const int32_t* __restrict__ cands) {
     static_assert(E % 4 == 0, "elements come in groups of four consecutive positions");
+    static_assert(MODE != kMerge || !STREAM, "a merge holds its candidates in registers");
     constexpr int kGroups = E / 4;
     __shared__ TopkSmem sm;
-    const int t = blockIdx.x;
+    const int t = MODE == kParts ? static_cast<int>(blockIdx.x) / parts : static_cast<int>(blockIdx.x);
+    const int part = MODE == kParts ? static_cast<int>(blockIdx.x) - t * parts : 0;
     const int tid = threadIdx.x;
     const int lane = lane_id(), wave = tid >> 6;
 
-    int64_t n;
+    int64_t n_row;
     if (n_valid) {
-        n = n_valid[t];
+        n_row = n_valid[t];
     } else {
         const int b = q_req[t];
         const int64_t s_b = kv_off[b + 1] - kv_off[b];
-        n = static_cast<int64_t>(q_pos[t]) + 1;
-        n = n < s_b ? n : s_b;
+        n_row = static_cast<int64_t>(q_pos[t]) + 1;
+        n_row = n_row < s_b ? n_row : s_b;
     }
-    n = n < max_n ? n : max_n;
-    n = n > 0 ? n : 0;
-    int32_t* out = ids + static_cast<int64_t>(t) * kTopK;
-    if (n <= kTopK) {
-        for (int i = tid; i < kTopK; i += kTopkThreads) out[i] = i < n ? i : -1;
+    n_row = n_row < max_n ? n_row : max_n;
+    n_row = n_row > 0 ? n_row : 0;
+    int64_t n = n_row;  // elements this block selects from (element index p < n)
+    if (MODE == kParts) {
+        n = n_row - part * chunk;
+        n = n < chunk ? n : chunk;
+        n = n > 0 ? n : 0;
+    } else if (MODE == kMerge) {
+        n = static_cast<int64_t>(parts) * kTopK;
+    }
+    int32_t* out = ids + static_cast<int64_t>(blockIdx.x) * kTopK;
+    const int64_t n_short = MODE == kMerge ? n_row : n;
+    if (n_short <= kTopK) {
+        for (int i = tid; i < kTopK; i += kTopkThreads) out[i] = i < n_short ? i : -1;
         return;
     }
-    const float* row = scores + static_cast<int64_t>(t) * ld;
+    const float* row = scores + static_cast<int64_t>(t) * ld + (MODE == kParts ? part * chunk : 0);
     constexpr int64_t kChunk = static_cast<int64_t>(kTopkThreads) * E;
     const int n_chunks = STREAM ? static_cast<int>((n + kChunk - 1) / kChunk) : 1;
     const int64_t tbase = static_cast<int64_t>(wave) * 64 * E + 4 * lane;
     uint32_t key[E];
+    int32_t cpos[MODE == kMerge ? E : 1];  // merge: row position of each candidate (-1: none)
     auto load = [&](int ch) {
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
             const int64_t p = ch * kChunk + tbase + 256 * g;
-            if (VEC && p + 3 < n) {
+            if constexpr (MODE == kMerge) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t pc = p + c;
+                    const int q = static_cast<int>(pc / kTopK);
+                    const int32_t local = cands[(static_cast<int64_t>(t) * parts + q) * kTopK + (pc - q * kTopK)];
+                    const int32_t pos = local >= 0 ? static_cast<int32_t>(q * chunk + local) : -1;
+                    cpos[4 * g + c] = pos;
+                    key[4 * g + c] = pos >= 0 ? score_key(row[pos]) : 0u;
+                }
+            } else if (VEC && p + 3 < n) {
                 const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + p));
 #pragma unroll
                 for (int c = 0; c < 4; ++c) key[4 * g + c] = score_key(v[c]);
@@ -386,8 +420,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
                 const uint32_t k = key[4 * g + c];
                 const bool ia = k >= amin2, it = k == tkey2;
                 const uint32_t rank = ra + (rt < need ? rt : need);
-                if ((ia || (it && rt < need)) && rank < kTopK)
-                    out[rank] = static_cast<int32_t>(p0 + c);
+                if ((ia || (it && rt < need)) && rank < kTopK) {
+                    if constexpr (MODE == kMerge)
+                        out[rank] = cpos[4 * g + c];
+                    else
+                        out[rank] = static_cast<int32_t>(p0 + c);
+                }
                 ra += ia ? 1u : 0u;
                 rt += it ? 1u : 0u;
             }
@@ -402,35 +440,86 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
 }
 
-template <int E, bool STREAM>
-static void launch_topk_e(const float* scores, int64_t ld, const int32_t* n_valid,
+template <int E, bool STREAM, int MODE>
+static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, const int32_t* n_valid,
                           const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
-                          int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream) {
-    const bool vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (ld % 4 == 0);
+                          int64_t max_n, int32_t* ids, int32_t parts, int64_t chunk,
+                          const int32_t* cands, bool vec, hipStream_t stream) {
     if (vec)
-        hipLaunchKernelGGL((topk_kernel<E, STREAM, true>), dim3(T), dim3(kTopkThreads), 0,
-                           stream, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids);
+        hipLaunchKernelGGL((topk_kernel<E, STREAM, true, MODE>), dim3(blocks), dim3(kTopkThreads),
+                           0, stream, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids,
+                           parts, chunk, cands);
     else
-        hipLaunchKernelGGL((topk_kernel<E, STREAM, false>), dim3(T), dim3(kTopkThreads), 0,
-                           stream, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids);
+        hipLaunchKernelGGL((topk_kernel<E, STREAM, false, MODE>), dim3(blocks),
+                           dim3(kTopkThreads), 0, stream, scores, ld, n_valid, kv_off, q_req,
+                           q_pos, max_n, ids, parts, chunk, cands);
+}
+
+// One selection pass over rows (or parts) of at most `len` elements each.
+template <int MODE>
+static void launch_pass(unsigned blocks, int64_t len, const float* scores, int64_t ld,
+                        const int32_t* n_valid, const int64_t* kv_off, const int32_t* q_req,
+                        const int32_t* q_pos, int64_t max_n, int32_t* ids, int32_t parts,
+                        int64_t chunk, bool vec, hipStream_t stream) {
+    if (len <= 4 * kTopkThreads)
+        launch_topk_e<4, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+    else if (len <= 8 * kTopkThreads)
+        launch_topk_e<8, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+    else if (len <= 16 * kTopkThreads)
+        launch_topk_e<16, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+    else if (len <= 32 * kTopkThreads)
+        launch_topk_e<32, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+    else if (len <= 64 * kTopkThreads)
+        launch_topk_e<64, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+    else
+        launch_topk_e<16, true, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+}
+
+// Parts per row for the two-stage selection: rows are split while fewer than 256 blocks
+// would run (one block per CU) and every part keeps at least 65536 elements; at most 16
+// parts.  A selection pass has a large fixed cost (about 25 us for a 32768-element row,
+// mostly barriers and dependent LDS round trips), so splitting shorter rows measured slower
+// (two passes of 8192 elements took longer than one pass of 32768).
+int topk_parts(int32_t T, int64_t max_n) {
+    int p = 1;
+    while (p < 16 && static_cast<int64_t>(T) * p < 256 && max_n >= static_cast<int64_t>(p) * 2 * 65536) p *= 2;
+    return p;
+}
+
+size_t topk_workspace_bytes(int32_t T, int64_t max_n) {
+    const int p = topk_parts(T, max_n);
+    return p > 1 ? static_cast<size_t>(T) * p * kTopK * sizeof(int32_t) : 0;
 }
 
 // Either n_valid (explicit row lengths) or (kv_off, q_req, q_pos) gives each row's length.
+// With a candidate workspace (topk_workspace_bytes) rows may be split into parts.
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
-                       int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream) {
-    if (max_n <= 4 * kTopkThreads)
-        launch_topk_e<4, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
-    else if (max_n <= 8 * kTopkThreads)
-        launch_topk_e<8, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
-    else if (max_n <= 16 * kTopkThreads)
-        launch_topk_e<16, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
-    else if (max_n <= 32 * kTopkThreads)
-        launch_topk_e<32, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
-    else if (max_n <= 64 * kTopkThreads)
-        launch_topk_e<64, false>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
+                       int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream,
+                       int32_t* cand_ws) {
+    const bool vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (ld % 4 == 0);
+    const int parts = cand_ws ? topk_parts(T, max_n) : 1;
+    if (parts == 1) {
+        launch_pass<kRow>(static_cast<unsigned>(T), max_n, scores, ld, n_valid, kv_off, q_req,
+                          q_pos, max_n, ids, 1, 0, vec, stream);
+        return hipGetLastError();
+    }
+    // parts start 16-byte aligned: chunk is a multiple of 4096 elements
+    int64_t chunk = (max_n + parts - 1) / parts;
+    chunk = (chunk + 4095) & ~static_cast<int64_t>(4095);
+    launch_pass<kParts>(static_cast<unsigned>(T * parts), chunk, scores, ld, n_valid, kv_off,
+                        q_req, q_pos, max_n, cand_ws, parts, chunk, vec, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned blocks = static_cast<unsigned>(T);
+    if (parts == 2)
+        launch_topk_e<4, false, kMerge>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, cand_ws, false, stream);
+    else if (parts == 4)
+        launch_topk_e<8, false, kMerge>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, cand_ws, false, stream);
+    else if (parts == 8)
+        launch_topk_e<16, false, kMerge>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, cand_ws, false, stream);
     else
-        launch_topk_e<16, true>(scores, ld, n_valid, kv_off, q_req, q_pos, T, max_n, ids, stream);
+        launch_topk_e<32, false, kMerge>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, cand_ws, false, stream);
     return hipGetLastError();
 }
 

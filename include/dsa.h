@@ -133,7 +133,8 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, i
  *           order, then -1 padding (short prefixes n_t <= 2048 select all of [0, n_t)).
  * workspace device buffer of at least dsa_indexer_topk_workspace_size(T, max_S) bytes,
  *           256-byte aligned (holds the fp32 scores of every admissible position, rows
- *           padded to a multiple of four floats).
+ *           padded to a multiple of four floats, and -- when few long rows would leave
+ *           most compute units idle -- per-part candidate lists of a two-stage selection).
  */
 size_t dsa_indexer_topk_workspace_size(int32_t T, int64_t max_S);
 dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
