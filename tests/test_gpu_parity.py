@@ -236,6 +236,29 @@ def test_indexer_topk_matches_oracle_and_standalone_topk(name, s_len):
     check_selection(lay, ids.cpu().numpy(), ref)
 
 
+def test_indexer_topk_two_stage_long_rows_bit_exact():
+    """Few long rows take the two-stage selection (parts of >= 65536 positions, then a merge
+    of the part lists).  Integer inputs make every score exact in fp32 and produce many ties,
+    so the IDs must equal the oracle's top-2048 (ties to the lower position) exactly; the
+    second request leaves parts partly and wholly empty."""
+    print("[indexer_topk] two-stage long rows", flush=True)
+    dsa = dsa_mod()
+    g = np.random.default_rng(17)
+    lay = synth.decode_layout("long2", 17, [300000, 140000])
+    q = synth.bf16_bits_from_f32(g.integers(-2, 3, size=(lay.T, 32, 128)))
+    w = synth.bf16_bits_from_f32(2.0 ** g.integers(-4, 2, size=(lay.T, 32)) *
+                                 g.choice([-1, 1], size=(lay.T, 32)))
+    keys = synth.bf16_bits_from_f32(g.integers(-2, 3, size=(lay.N, 128)))
+    args = (dev(q), dev(w), dev(keys), dev(lay.kv_off), dev(lay.q_req), dev(lay.q_pos))
+    assert dsa.indexer_topk_workspace_size(lay.T, lay.max_s) > lay.T * lay.max_s * 4  # split
+    ids = dsa.indexer_topk(*args, lay.max_s)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    ref = O.indexer_scores(q, w, keys, lay.kv_off, lay.q_req, lay.q_pos)
+    for t in range(lay.T):
+        assert np.array_equal(got[t], O.topk_ids(ref[t])), f"row {t}"
+
+
 def test_indexer_topk_prefill():
     print("[indexer_topk] prefill", flush=True)
     dsa = dsa_mod()
