@@ -53,6 +53,46 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Byte offset of an LDS location, as the LDS instructions and M0 take it.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
+// One direct global->LDS copy (gfx950 global_load_lds_dwordx4): lane l moves 16 bytes from its
+// own address src to LDS bytes [lds_base + 16 l, +16); nothing passes through registers.  It is
+// issued through inline assembly so the compiler does not track it -- the compiler would
+// otherwise assume the copy may alias every later LDS read and drain the LDS queue before each
+// of them, defeating operand prefetch.  Every wait for these copies is an explicit vmcnt wait
+// (vector-memory loads complete in issue order, so waiting until at most N operations are
+// outstanding, where N counts the loads issued after a copy, covers that copy; stores issued
+// in between only make such a wait stricter).  M0 holds the wave-uniform LDS base; one wait
+// state separates writing M0 from the copy.  With NT the copy carries the non-temporal hint:
+// data read once should not displace cached lines (a pure copy stream measured 7.2 TB/s with
+// the hint and 6.2 TB/s without it).
+template <bool NT = false>
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_base) {
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                     :
+                     : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (s_waitcnt vmcnt(N) with expcnt/lgkmcnt left at their maxima; N <= 63).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Cross-lane moves through DPP (data-parallel primitives on the VALU, no LDS round trip).
 // Controls: quad_perm [1,0,3,2] and [2,3,0,1] swap lanes at distance 1 and 2, row_half_mirror
 // reverses each group of 8 lanes, row_mirror each row of 16, row_shr:n shifts a row right by

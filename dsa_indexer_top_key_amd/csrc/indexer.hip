@@ -13,10 +13,10 @@
 //
 // Two kernels:
 //  * decode  -- one query per request.  Each query streams its S keys once from HBM
-//    (256 B per key, 32 flop/B), so the kernel is HBM-bound.  Keys go straight from global
-//    memory into the B operand of v_mfma_f32_16x16x32_bf16: the four lanes that share a key
-//    read one contiguous 64-byte quarter of the row per load, so every load instruction
-//    touches whole 64-byte segments and no LDS round trip is needed.
+//    (256 B per key, 32 flop/B), so the kernel is HBM-bound.  Keys stream through per-wave
+//    LDS rings by direct global->LDS copies of whole 1 KB spans (non-temporal), feed the B
+//    operand of v_mfma_f32_16x16x32_bf16 from there, and the scores leave in one burst per
+//    block.
 //  * prefill -- many queries of one request.  A block owns 16 consecutive queries and walks
 //    their causal key range in 32-key tiles staged through LDS (double-buffered); every key
 //    tile feeds 16 queries x 32 heads of v_mfma_f32_32x32x16_bf16, so the kernel is bound by
@@ -38,30 +38,73 @@ __device__ __forceinline__ int64_t admissible(const int64_t* kv_off, int b, int3
 // ---------------------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------------------
-constexpr int kDecodeChunk = 2048;  // keys per block
-constexpr int kDecodeUnroll = 1;    // 16-key tiles in flight per wave (more in flight measured slower)
+constexpr int kDecodeTile = 16;          // keys per wave step: 4 KB, four 1 KB copies
+constexpr int kDecodeRing = 3;           // ring slots per wave (two steps in flight)
+constexpr int kDecodeCopies = kDecodeTile / 4;
+constexpr int kDecodeMaxChunk = 4096;    // keys per block at most (their scores: 16 KB of LDS)
+constexpr int kDecodeMinChunk = 1024;
 
-// grid: one block per (query, chunk of kDecodeChunk keys); 4 waves per block.
+// Keys per block: the whole job spread over about two blocks per CU (64 KB of LDS each, so
+// two fit; all blocks then end at about the same time and the score writes leave as one
+// burst), within [1024, 4096] keys and a multiple of one block step (64 keys).  With one
+// block (four waves) per CU the MFMA and reduction latency of each tile is no longer hidden
+// (8192-key blocks measured 60% slower).
+static int64_t decode_chunk(int32_t T, int64_t max_s) {
+    int64_t c = (static_cast<int64_t>(T) * max_s + 511) / 512;
+    c = (c + 63) & ~static_cast<int64_t>(63);
+    c = c < kDecodeMinChunk ? kDecodeMinChunk : c;
+    return c > kDecodeMaxChunk ? kDecodeMaxChunk : c;
+}
+
+// grid: one block per (query, chunk of keys); 4 waves per block, each streaming its own
+// 16-key tiles (tile i of the chunk belongs to wave i % 4) through a private three-slot LDS
+// ring.  Each copy instruction moves 1 KB = 4 whole keys, so every instruction covers whole
+// 128-byte lines (key-major loads of 64 bytes per key and instruction measured 15% slower).
+// Lane l = 16 g + c of a copy loads key 4 d + g of the tile, 16-byte piece c ^ (key % 16)
+// into LDS slot c of that key's 256-byte row: the MFMA operand reads below (16 lanes, 16
+// different keys, one piece each) then fall in 16 distinct bank groups.
 // MFMA 16x16x32: A = q (rows: 16 heads), B = keys (cols: 16 keys), K = 32 dims per step.
-// Lane l = 16*g + c supplies head/key c and the dims [32s + 8g, 32s + 8g + 8) at step s;
-// the 16x16 accumulator gives lane l the key c and heads 4g + r (r = 0..3).
+// Lane l = 16 g + c supplies head/key c and the dims [32 s + 8 g, +8) at step s; the 16x16
+// accumulator gives lane l the key c and heads 4 g + r (r = 0..3).
+// Scores collect in LDS and leave at the end of the block in full 16-byte stores: writes
+// interleaved with the key stream measured about 10% slower than one burst at the end.
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ keys, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos, int32_t chunks_per_q,
-    int64_t max_s, float* __restrict__ scores, int64_t ld) {
+    int32_t chunk, int64_t max_s, float* __restrict__ scores, int64_t ld, int vec_store) {
+    __shared__ __attribute__((aligned(16))) uint16_t ring[4][kDecodeRing][kDecodeTile * kIndexDim];
+    __shared__ __attribute__((aligned(16))) float sbuf[kDecodeMaxChunk];
     const int t = blockIdx.x / chunks_per_q;
-    const int chunk = blockIdx.x - t * chunks_per_q;
+    const int ci = blockIdx.x - t * chunks_per_q;
     const int b = q_req[t];
     const int64_t n = admissible(kv_off, b, q_pos[t], max_s);
-    const int64_t k0 = static_cast<int64_t>(chunk) * kDecodeChunk;
-    if (k0 >= n) return;
-    const int64_t k_end = (k0 + kDecodeChunk < n) ? k0 + kDecodeChunk : n;
+    const int64_t k0 = static_cast<int64_t>(ci) * chunk;
+    if (k0 >= n) return;  // block-uniform
+    const int len = static_cast<int>((k0 + chunk < n ? k0 + chunk : n) - k0);
 
     const int lane = lane_id();
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int c = lane & 15;
+    const uint16_t* kb = keys + (kv_off[b] + k0) * kIndexDim;
+    const int n_tiles = (len + kDecodeTile - 1) / kDecodeTile;
+    const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
+    // copies of this wave's j-th tile into ring slot j % 3; keys past the end copy key 0
+    auto issue = [&](int j) {
+        const int kt = (wave + 4 * j) * kDecodeTile;
+        const uint16_t* slot = ring[wave][j % kDecodeRing];
+#pragma unroll
+        for (int d = 0; d < kDecodeCopies; ++d) {
+            const int r = 4 * d + g;
+            const int key = kt + r < len ? kt + r : 0;
+            copy_to_lds<true>(kb + static_cast<int64_t>(key) * kIndexDim + 8 * (c ^ r),
+                              lds_offset(slot + d * 4 * kIndexDim));
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < kDecodeRing - 1; ++j)
+        if (j < my_tiles) issue(j);
 
     bf16x8 qa[2][4];
     const uint16_t* qt = q_idx + static_cast<int64_t>(t) * kIndexHeads * kIndexDim;
@@ -76,34 +119,40 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) wr[mt][r] = bf16_to_f32(w[t * kIndexHeads + 16 * mt + 4 * g + r]);
 
-    const uint16_t* kb = keys + kv_off[b] * kIndexDim;
-    float* srow = scores + static_cast<int64_t>(t) * ld;
-    constexpr int kStep = 4 * 16 * kDecodeUnroll;  // keys per block-iteration
-    for (int64_t base = k0 + wave * 16 * kDecodeUnroll; base < k_end; base += kStep) {
-        u32x4 kf[kDecodeUnroll][4];
-#pragma unroll
-        for (int u = 0; u < kDecodeUnroll; ++u) {
-            const int64_t key = base + 16 * u + c;
-            const bool ok = key < k_end;
-            const u32x4* src = reinterpret_cast<const u32x4*>(kb + (ok ? key : k0) * kIndexDim + 8 * g);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) kf[u][s] = __builtin_nontemporal_load(src + 4 * s);
+    for (int j = 0; j < my_tiles; ++j) {
+        // tile j landed once only the copies issued after it may be outstanding
+        if (j + kDecodeRing - 1 < my_tiles) {
+            issue(j + kDecodeRing - 1);
+            wait_vmcnt<(kDecodeRing - 1) * kDecodeCopies>();
+        } else {
+            wait_vmcnt<0>();
         }
+        const uint16_t* buf = ring[wave][j % kDecodeRing] + c * kIndexDim;
+        u32x4 kf[4];
 #pragma unroll
-        for (int u = 0; u < kDecodeUnroll; ++u) {
-            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) kf[s] = *reinterpret_cast<const u32x4*>(buf + 8 * ((4 * s + g) ^ c));
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], as_bf16x8(kf[u][s]), a0, 0, 0, 0);
-                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], as_bf16x8(kf[u][s]), a1, 0, 0, 0);
-            }
-            float v = 0.f;
+        for (int s = 0; s < 4; ++s) {
+            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], as_bf16x8(kf[s]), a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], as_bf16x8(kf[s]), a1, 0, 0, 0);
+        }
+        float v = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v += wr[0][r] * fmaxf(a0[r], 0.f) + wr[1][r] * fmaxf(a1[r], 0.f);
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            const int64_t key = base + 16 * u + c;
-            if (g == 0 && key < k_end) srow[key] = v;
+        for (int r = 0; r < 4; ++r) v += wr[0][r] * fmaxf(a0[r], 0.f) + wr[1][r] * fmaxf(a1[r], 0.f);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (g == 0) sbuf[(wave + 4 * j) * kDecodeTile + c] = v;
+    }
+    __syncthreads();
+    float* srow = scores + static_cast<int64_t>(t) * ld + k0;
+    for (int i = 4 * static_cast<int>(threadIdx.x); i < len; i += 4 * 256) {
+        if (vec_store && i + 3 < len) {
+            *reinterpret_cast<f32x4*>(srow + i) = *reinterpret_cast<const f32x4*>(sbuf + i);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (i + k < len) srow[i + k] = sbuf[i + k];
         }
     }
 }
@@ -241,12 +290,15 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const
         hipLaunchKernelGGL(indexer_prefill_kernel, dim3(blocks), dim3(512), 0, stream, q_idx, w,
                            keys, kv_off, q_req, q_pos, T, max_s, scores, ld);
     } else {
-        const int64_t cpq = (max_s + kDecodeChunk - 1) / kDecodeChunk;
+        const int64_t chunk = decode_chunk(T, max_s);
+        const int64_t cpq = (max_s + chunk - 1) / chunk;
         const int64_t blocks = cpq * T;
         if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        const bool vec = reinterpret_cast<uintptr_t>(scores) % 16 == 0 && ld % 4 == 0;
         hipLaunchKernelGGL(indexer_decode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
                            0, stream, q_idx, w, keys, kv_off, q_req, q_pos,
-                           static_cast<int32_t>(cpq), max_s, scores, ld);
+                           static_cast<int32_t>(cpq), static_cast<int32_t>(chunk), max_s, scores,
+                           ld, vec ? 1 : 0);
     }
     return hipGetLastError();
 }

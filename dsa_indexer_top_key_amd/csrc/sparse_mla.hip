@@ -56,7 +56,6 @@ constexpr int kPrefV = 4;                    // LDS prefetch depth of P.V B frag
 constexpr float kLn2 = 0.69314718055994531f;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 typedef __attribute__((address_space(3))) const uint16_t lds_u16;
 
@@ -82,37 +81,19 @@ struct MlaSmem {
     uint32_t redo;                           // some logit exceeded its reference by > 2^32
 };
 
-// Byte offset of an LDS location, as the LDS instructions and M0 take it.
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
-}
-
-// One direct global->LDS copy (gfx950 global_load_lds_dwordx4): lane l moves 16 bytes from its
-// own address src to LDS bytes [lds_base + 16 l, +16); nothing passes through registers.  It is
-// issued through inline assembly so the compiler does not track it -- the compiler would
-// otherwise assume the copy may alias every later LDS read and drain the LDS queue before each
-// of them, defeating the operand prefetch.  Every wait for these copies is an explicit vmcnt
-// wait.  M0 holds the (wave-uniform) LDS base; nothing else in this kernel uses M0, and one
-// wait state separates writing M0 from the copy.
-__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
-}
-
 // Ring copies of one tile (32 rows; padding rows copy row 0 of the request, so every slot
 // holds finite data and every tile is exactly 36 copies).  Every wave copies eight latent
 // rows (rows 8 wave .. 8 wave + 7); the head-group waves interleave theirs with their S^T
 // MFMAs, wave 3 also copies the four blocks of eight companion rows.  Spreading the copies
 // over all four waves keeps enough of them in flight: one wave alone reaches about half the
 // gather rate.
+constexpr bool kGatherNt = false;  // cache hint of the ring copies (rows may repeat across queries)
 constexpr int kConsRows = kTile / 4;            // latent rows per wave (8)
 constexpr int kHelpCopies = kConsRows + kTile / 8;  // wave 3: 8 latent rows + 4 companion blocks
 
 __device__ __forceinline__ void copy_latent_row(int64_t row, const uint16_t* latent,
                                                 int64_t ld_lat, uint32_t lds, int lane) {
-    copy_to_lds(latent + row * ld_lat + 8 * lane, lds);
+    copy_to_lds<kGatherNt>(latent + row * ld_lat + 8 * lane, lds);
 }
 
 // Companion block kb of a tile: rows 8 kb .. 8 kb + 7, lane -> row 8 kb + lane / 8; the
@@ -121,15 +102,7 @@ __device__ __forceinline__ void copy_companion_block(int64_t row, int kb, const 
                                                      int64_t ld_kpe, uint32_t lds, int lane) {
     const int r = 8 * kb + (lane >> 3);
     const int c = (lane & 7) ^ (r & 7);
-    copy_to_lds(kpe + row * ld_kpe + 8 * c, lds);
-}
-
-// Wait until at most N of this wave's vector-memory operations are outstanding
-// (s_waitcnt vmcnt(N) with expcnt/lgkmcnt left at their maxima; N <= 63).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    copy_to_lds<kGatherNt>(kpe + row * ld_kpe + 8 * c, lds);
 }
 
 // V operand of P . V for latent tile nt and K-chunk c (rows 16c .. 16c+15 of the tile).
