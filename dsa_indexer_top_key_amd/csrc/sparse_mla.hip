@@ -33,8 +33,11 @@
 // recomputed once with the exact per-head maximum recorded during the first pass, so no
 // accumulator is ever rescaled in the hot loop (which would not fit the register budget:
 // the 32 x 480 accumulators of a head group already fill the 240 AGPRs it owns).
-// Splits write normalised fp32 partials and a log2-sum-exp; a small kernel merges them.  A
-// block maps to an XCD chosen by its query, so all splits of a query share one L2.
+// Splits write normalised partials (in the output's precision: bf16 or fp32) and a
+// log2-sum-exp; a small kernel over all CUs merges them (merging inside the last split of
+// each query measured slower: the agent-scope release/acquire and a merge on only one CU per
+// query cost more than the extra launch).  A block maps to an XCD chosen by its query, so all
+// splits of a query share one L2.
 #include "common.h"
 
 namespace dsa {
@@ -117,12 +120,42 @@ __device__ __forceinline__ bf16x8 v_fragment(lds_u16* vbase, int nt, int c) {
     return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Store one 32 x 32 accumulator tile of O (rows row0 + 8(r/4) + 4hh + r%4 for r = 0..15,
+// column col0 + lane % 32) into a row-major matrix with leading dimension ld.  bf16: lanes
+// 2j and 2j+1 trade one value (DPP swap of adjacent lanes) so that each lane stores two
+// adjacent columns of one row in 4 bytes -- the even lane row R, the odd lane row R + 1 --
+// half as many store instructions, each writing 64-byte runs.
+__device__ __forceinline__ void store_tile_bf16(uint16_t* dst, int64_t ld, int row0, int col0,
+                                                const float (&v)[16], int lane) {
+    const bool odd = lane & 1;
+    const int hh = (lane >> 5) & 1;
+    const int col = col0 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        const int row = row0 + 8 * (r >> 2) + 4 * hh + (r & 3);  // r % 4 is 0 or 2
+        const float send = odd ? v[r] : v[r + 1];
+        const float recv = __uint_as_float(dpp_u32<kDppQuadXor1>(0u, __float_as_uint(send)));
+        const uint32_t packed = odd ? pack_bf16x2(recv, v[r + 1]) : pack_bf16x2(v[r], recv);
+        const int64_t off = static_cast<int64_t>(row + (odd ? 1 : 0)) * ld + col - (odd ? 1 : 0);
+        *reinterpret_cast<uint32_t*>(dst + off) = packed;
+    }
+}
+
+__device__ __forceinline__ void store_tile_f32(float* dst, int64_t ld, int row0, int col0,
+                                               const float (&v)[16], int lane) {
+    const int hh = (lane >> 5) & 1;
+    const int col = col0 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        dst[static_cast<int64_t>(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * ld + col] = v[r];
+}
+
 __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t ld_lat,
     const uint16_t* __restrict__ kpe, int64_t ld_kpe, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ ids, int32_t T,
     int32_t nsplit, float scale_log2, void* __restrict__ out, int out_f32,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, void* __restrict__ part_o, float* __restrict__ part_lse) {
     __shared__ MlaSmem sm;
     const int g = blockIdx.x;
     const int j = g >> 3;
@@ -253,22 +286,20 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
             }
         }
         lds_barrier();  // the head groups have published 1/l
+        // destination: the output (one split) or this split's partial, [96][512] either way
+        const int64_t dbase = (nsplit > 1 ? ps : static_cast<int64_t>(t)) * kMlaHeads * kLatent;
+        void* dst = nsplit > 1 ? part_o : out;
 #pragma unroll
         for (int hg = 0; hg < 3; ++hg)
 #pragma unroll
-            for (int ht = 0; ht < kHelpTiles; ++ht)
+            for (int ht = 0; ht < kHelpTiles; ++ht) {
+                float v[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int hd = 32 * hg + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float v = orest[hg][ht][r] * sm.inv_l[hd];
-                const int col = 32 * (kConsTiles + ht) + hl;
-                const int64_t oi = (static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + col;
-                if (nsplit > 1)
-                    part_o[(ps * kMlaHeads + hd) * kLatent + col] = v;
-                else if (out_f32)
-                    static_cast<float*>(out)[oi] = v;
+                for (int r = 0; r < 16; ++r) v[r] = orest[hg][ht][r] * sm.inv_l[32 * hg + 8 * (r >> 2) + 4 * hh + (r & 3)];
+                if (out_f32)
+                    store_tile_f32(static_cast<float*>(dst) + dbase, kLatent, 32 * hg, 32 * (kConsTiles + ht), v, lane);
                 else
-                    static_cast<uint16_t*>(out)[oi] = f32_to_bf16(v);
+                    store_tile_bf16(static_cast<uint16_t*>(dst) + dbase, kLatent, 32 * hg, 32 * (kConsTiles + ht), v, lane);
             }
         return;
     }
@@ -438,75 +469,99 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     float ir[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) ir[r] = __shfl(inv, 8 * (r >> 2) + 4 * hh + (r & 3));
-    if (nsplit == 1) {
-        const int64_t ob = static_cast<int64_t>(t) * kMlaHeads * kLatent;
+    const int64_t dbase = (nsplit > 1 ? ps : static_cast<int64_t>(t)) * kMlaHeads * kLatent;
+    void* dst = nsplit > 1 ? part_o : out;
 #pragma unroll
-        for (int nt = 0; nt < kConsTiles; ++nt)
+    for (int nt = 0; nt < kConsTiles; ++nt) {
+        float v[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int hd = head0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float v = o[nt][r] * ir[r];
-                if (out_f32)
-                    static_cast<float*>(out)[ob + hd * kLatent + 32 * nt + hl] = v;
-                else
-                    static_cast<uint16_t*>(out)[ob + hd * kLatent + 32 * nt + hl] = f32_to_bf16(v);
-            }
-    } else {
-        float* po = part_o + ps * kMlaHeads * kLatent;
-#pragma unroll
-        for (int nt = 0; nt < kConsTiles; ++nt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int hd = head0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                po[hd * kLatent + 32 * nt + hl] = o[nt][r] * ir[r];
-            }
+        for (int r = 0; r < 16; ++r) v[r] = o[nt][r] * ir[r];
+        if (out_f32)
+            store_tile_f32(static_cast<float*>(dst) + dbase, kLatent, head0, 32 * nt, v, lane);
+        else
+            store_tile_bf16(static_cast<uint16_t*>(dst) + dbase, kLatent, head0, 32 * nt, v, lane);
     }
 }
 
-// Merge split partials: one wave per (query, head), 8 latent dims per lane.
-__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ part_o,
+// Merge split partials: one wave per (query, head), 8 latent columns per lane.
+//   O = sum_s 2^(l_s - m) O_s / sum_s 2^(l_s - m),  m = max_s l_s
+// (partials in bf16 for a bf16 output, else fp32).  The split count is a template argument so
+// every load of a wave is issued before the first one is needed (one memory round trip for
+// the log-sum-exps, one for the partials).
+template <bool F32, int NS>
+__global__ __launch_bounds__(256) void mla_combine_kernel(const void* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
-                                                          int32_t T, int32_t nsplit,
-                                                          void* __restrict__ out, int out_f32,
+                                                          int32_t T, void* __restrict__ out,
                                                           float* __restrict__ lse) {
     const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (pair >= static_cast<int64_t>(T) * kMlaHeads) return;
     const int t = static_cast<int>(pair / kMlaHeads), hd = static_cast<int>(pair % kMlaHeads);
     const int lane = lane_id();
+    float ls[NS];
+    u32x4 x[NS][F32 ? 2 : 1];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int64_t ps = static_cast<int64_t>(t) * NS + s;
+        ls[s] = part_lse[ps * kMlaHeads + hd];
+        const int64_t pi = (ps * kMlaHeads + hd) * kLatent + 8 * lane;
+        if constexpr (F32) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(part_o) + pi);
+            x[s][0] = src[0];
+            x[s][1] = src[1];
+        } else {
+            x[s][0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(part_o) + pi);
+        }
+    }
     float m = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-        m = fmaxf(m, part_lse[(static_cast<int64_t>(t) * nsplit + s) * kMlaHeads + hd]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) m = fmaxf(m, ls[s]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    if (m != -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
-            const int64_t ps = static_cast<int64_t>(t) * nsplit + s;
-            const float ls = part_lse[ps * kMlaHeads + hd];
-            if (ls == -INFINITY) continue;
-            const float wgt = exp2f(ls - m);
-            wsum += wgt;
-            const float4* src = reinterpret_cast<const float4*>(part_o + (ps * kMlaHeads + hd) * kLatent + 8 * lane);
-            const float4 a = src[0], bq = src[1];
-            acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
-            acc[4] += wgt * bq.x; acc[5] += wgt * bq.y; acc[6] += wgt * bq.z; acc[7] += wgt * bq.w;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        // a split without valid IDs has l_s = -inf and weight 0 (its partial is all zeros)
+        const float wgt = ls[s] == -INFINITY ? 0.f : exp2f(ls[s] - m);
+        wsum += wgt;
+        if constexpr (F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] += wgt * __uint_as_float(x[s][0][e]);
+                acc[4 + e] += wgt * __uint_as_float(x[s][1][e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += wgt * __uint_as_float(x[s][0][e] << 16);
+                acc[2 * e + 1] += wgt * __uint_as_float(x[s][0][e] & 0xffff0000u);
+            }
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     const int64_t oi = (static_cast<int64_t>(t) * kMlaHeads + hd) * kLatent + 8 * lane;
-    if (out_f32) {
+    if constexpr (F32) {
         f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(out) + oi);
         dst[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
         dst[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
     } else {
         u32x4 o;
-        o[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-        o[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-        o[2] = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-        o[3] = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
         *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + oi) = o;
     }
     if (lse && lane == 0)
         lse[static_cast<int64_t>(t) * kMlaHeads + hd] = wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+template <int NS>
+static void launch_combine(bool out_f32, unsigned blocks, const void* part_o,
+                           const float* part_lse, int32_t T, void* out, float* lse,
+                           hipStream_t stream) {
+    if (out_f32)
+        hipLaunchKernelGGL((mla_combine_kernel<true, NS>), dim3(blocks), dim3(256), 0, stream,
+                           part_o, part_lse, T, out, lse);
+    else
+        hipLaunchKernelGGL((mla_combine_kernel<false, NS>), dim3(blocks), dim3(256), 0, stream,
+                           part_o, part_lse, T, out, lse);
 }
 
 int sparse_mla_nsplit(int32_t T) {
@@ -515,13 +570,14 @@ int sparse_mla_nsplit(int32_t T) {
     return ns;
 }
 
+// Split workspace: per-split partial outputs (sized for fp32), then per-split log2-sum-exp.
+static size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
 size_t sparse_mla_workspace_bytes(int32_t T) {
     const int ns = sparse_mla_nsplit(T);
     if (ns == 1 || T <= 0) return 0;
     const size_t parts = static_cast<size_t>(T) * ns;
-    const size_t o_bytes = parts * kMlaHeads * kLatent * sizeof(float);
-    const size_t l_bytes = parts * kMlaHeads * sizeof(float);
-    return o_bytes + ((l_bytes + 255) & ~static_cast<size_t>(255));
+    return round256(parts * kMlaHeads * kLatent * sizeof(float)) + round256(parts * kMlaHeads * sizeof(float));
 }
 
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t ld_lat,
@@ -533,11 +589,12 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
     const int64_t groups = (static_cast<int64_t>(T) + 7) / 8;
     const int64_t blocks = groups * 8 * ns;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    float* part_o = nullptr;
+    void* part_o = nullptr;
     float* part_lse = nullptr;
     if (ns > 1) {
-        part_o = static_cast<float*>(workspace);
-        part_lse = part_o + static_cast<size_t>(T) * ns * kMlaHeads * kLatent;
+        part_o = workspace;
+        part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            round256(static_cast<size_t>(T) * ns * kMlaHeads * kLatent * sizeof(float)));
     }
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL(sparse_mla_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
@@ -545,9 +602,13 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
                        scale_log2, out, out_f32 ? 1 : 0, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
-    const int64_t cblocks = (static_cast<int64_t>(T) * kMlaHeads + 3) / 4;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(static_cast<unsigned>(cblocks)), dim3(256), 0,
-                       stream, part_o, part_lse, T, ns, out, out_f32 ? 1 : 0, lse);
+    const unsigned cblocks = static_cast<unsigned>((static_cast<int64_t>(T) * kMlaHeads + 3) / 4);
+    switch (ns) {  // sparse_mla_nsplit gives a power of two up to 16
+        case 2: launch_combine<2>(out_f32, cblocks, part_o, part_lse, T, out, lse, stream); break;
+        case 4: launch_combine<4>(out_f32, cblocks, part_o, part_lse, T, out, lse, stream); break;
+        case 8: launch_combine<8>(out_f32, cblocks, part_o, part_lse, T, out, lse, stream); break;
+        default: launch_combine<16>(out_f32, cblocks, part_o, part_lse, T, out, lse, stream); break;
+    }
     return hipGetLastError();
 }
 

@@ -162,7 +162,10 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
  *          accumulated in fp32.  A row with no valid ID gives out = 0.
  * lse      [T,96] float32 out (may be NULL): log sum_{j in I_t} exp(a_j); -inf if empty.
  * workspace at least dsa_sparse_mla_workspace_size(T, 96, 2048) bytes, 256-byte aligned
- *          (may be NULL when that size is 0): split-KV partial results.
+ *          (may be NULL when that size is 0): split-KV partial results (small T splits each
+ *          ID row over several blocks and merges their normalised partials afterwards).
+ *          With bf16 output the partials are kept in bf16 (each split's normalised partial
+ *          is rounded once more, by at most half a bf16 ulp), with fp32 output in fp32.
  */
 size_t dsa_sparse_mla_workspace_size(int32_t T, int32_t n_heads, int32_t topk);
 dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int64_t ld_latent,

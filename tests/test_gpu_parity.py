@@ -324,6 +324,28 @@ def test_sparse_mla_parity(t_count, packed, f32):
     check_mla(lay, d, ids, got_o, got_l, f32=f32)
 
 
+@pytest.mark.parametrize("f32", [False, True])
+def test_sparse_mla_split_workspace_reuse(f32):
+    """Small T splits each ID row over several blocks and merges their partials (bf16 partials
+    for a bf16 output); one caller-owned workspace, filled with garbage first, serves several
+    calls in a row, and every result matches the oracle."""
+    print(f"[mla] split workspace reuse f32={f32}", flush=True)
+    dsa = dsa_mod()
+    lay = synth.decode_layout("reuse", 77, [5000, 4000, 2500])
+    d = synth.inputs_np(lay, parts=("mla",))
+    need = dsa.sparse_mla_workspace_size(lay.T)
+    assert need > 0  # three queries: split path
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    for call in range(3):
+        ids = synth.random_ids_np(100 + call, lay)
+        out, lse = dsa.sparse_mla_attn(dev(d["q"]), dev(d["latent"]), dev(d["kpe"]),
+                                       dev(lay.kv_off), dev(lay.q_req), dev(ids),
+                                       synth.ATTN_SCALE, workspace=ws,
+                                       out_dtype=torch.float32 if f32 else torch.bfloat16)
+        torch.cuda.synchronize()
+        check_mla(lay, d, ids, out.float().cpu().numpy(), lse.cpu().numpy(), f32=f32)
+
+
 def test_sparse_mla_special_rows():
     print("[mla] special rows", flush=True)
     lay = synth.decode_layout("sp", 40, [3000, 3000, 3000, 2000, 50])
