@@ -108,6 +108,17 @@ __device__ __forceinline__ void copy_companion_block(int64_t row, int kb, const 
     copy_to_lds<kGatherNt>(kpe + row * ld_kpe + 8 * c, lds);
 }
 
+// The per-step base of the transposing V reads, made opaque to the compiler.  Left visible,
+// the compiler splits base + constant into a loop-invariant register per read and re-adds
+// it with a VALU op before every read (44 per step per wave) instead of folding the constant
+// into the instruction's 16-bit offset field; behind an empty asm the base is a fresh value
+// each step and every constant folds.
+__device__ __forceinline__ lds_u16* opaque_lds(lds_u16* p) {
+    uint32_t v = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+    asm volatile("" : "+v"(v));
+    return reinterpret_cast<lds_u16*>(static_cast<uintptr_t>(v));
+}
+
 // V operand of P . V for latent tile nt and K-chunk c (rows 16c .. 16c+15 of the tile).
 // Lane l needs latent column 32 nt + (l % 32) at rows 16c + 4hh + {0..3} and
 // 16c + 8 + 4hh + {0..3} (hh = l / 32), matching the P fragment's row order.  Within each
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
             for (int i = 0; i < n_tiles; ++i) {
                 if (i + 2 < n_tiles) copy_all(i + 2);
                 // all operands first (one LDS latency), then the 30 MFMAs back to back
-                lds_u16* vbase = (lds_u16*)sm.lat[i % kNBuf] + vrow * kLatStride + vcol;
+                lds_u16* vbase = opaque_lds((lds_u16*)sm.lat[i % kNBuf] + vrow * kLatStride + vcol);
                 u32x4 pf[3][2];
                 bf16x8 vf[2][kHelpTiles];
 #pragma unroll
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     auto pv_tile = [&](int tile) {
         const u32x4 pa0 = sm.pfrag[tile & 1][wave][lane][0];
         const u32x4 pa1 = sm.pfrag[tile & 1][wave][lane][1];
-        lds_u16* vbase = (lds_u16*)sm.lat[tile % kNBuf] + vrow * kLatStride + vcol;
+        lds_u16* vbase = opaque_lds((lds_u16*)sm.lat[tile % kNBuf] + vrow * kLatStride + vcol);
         bf16x8 vbuf[kPrefV];
 #pragma unroll
         for (int k = 0; k < kPrefV; ++k) vbuf[k] = v_fragment(vbase, k % kConsTiles, k / kConsTiles);
