@@ -58,7 +58,8 @@ __device__ __forceinline__ int shift_for(uint32_t span) {
 }
 
 struct TopkSmem {
-    uint32_t hist[kBins];
+    uint32_t hist[kBins];             // histogram; at the end the output row being staged
+    uint32_t bm[2][kBins];            // selection bitmaps (above, tie) of a register-resident row
     uint32_t wtot[kTopkWaves];
     uint32_t red[4][kTopkWaves];
     uint32_t cnt[2][2 * kTopkWaves];  // per-wave (above, tie) counts, double-buffered by chunk
@@ -369,75 +370,159 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const bool take_all = (cand == need);
     const uint32_t above_min = take_all ? rlo : rlo + 1u;  // keys >= this are "above"
     const uint32_t tie_key = take_all ? 0xFFFFFFFFu : rlo;  // never a key when take_all
-    uint32_t above_done = 0, tie_done = 0;  // counts of earlier chunks (block-uniform)
-    for (int ch = 0; ch < n_chunks; ++ch) {
-        if (STREAM) load(ch);
-        uint32_t na = 0, nt = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            na += key[e] >= above_min ? 1u : 0u;
-            nt += key[e] == tie_key ? 1u : 0u;
-        }
-        na = wave_sum_u32(na);
-        nt = wave_sum_u32(nt);
-        uint32_t* cnt = sm.cnt[ch & 1];
-        if (lane == 0) {
-            cnt[wave] = na;
-            cnt[kTopkWaves + wave] = nt;
-        }
-        lds_barrier();
-        uint32_t a_run = above_done, t_run = tie_done, a_tot = 0, t_tot = 0;
-#pragma unroll
-        for (int i = 0; i < kTopkWaves; ++i) {
-            const uint32_t x = cnt[i], y = cnt[kTopkWaves + i];
-            a_run += i < wave ? x : 0u;
-            t_run += i < wave ? y : 0u;
-            a_tot += x;
-            t_tot += y;
-        }
-        // opaque copies keep the compiler from holding the counting loop's 2E lane masks
-        // live (in scalar registers) until they are needed again below
-        uint32_t amin2 = above_min, tkey2 = tie_key;
-        asm volatile("" : "+v"(amin2), "+v"(tkey2));
+    if constexpr (!STREAM) {
+        // Register-resident row: selection bitmaps in LDS, one bit per position (word p / 32,
+        // bit p % 32).  A lane's four consecutive positions of group g form a 4-bit mask; the
+        // eight lanes of an octet cover one 32-bit word, which three DPP ORs assemble.  A
+        // popcount scan over the words (in position order) then ranks every selected position:
+        // first the tie bitmap keeps its first `need` bits, then the union is ranked.
+        constexpr int kWords = 32 * E;                       // words of the row
+        constexpr int kWpt = kWords >= kTopkThreads ? kWords / kTopkThreads : 1;  // words per thread
+        const bool ties = !take_all;                          // block-uniform
+        const uint32_t amin2 = above_min, tkey2 = tie_key;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-            uint64_t ma[4], mt[4];
+            uint32_t ma = 0u, mt = 0u;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                ma[c] = __ballot(key[4 * g + c] >= amin2);
-                mt[c] = __ballot(key[4 * g + c] == tkey2);
+                ma |= (key[4 * g + c] >= amin2 ? 1u : 0u) << c;
+                mt |= (key[4 * g + c] == tkey2 ? 1u : 0u) << c;
             }
-            // counts of this group's elements held by lower lanes, then by this lane's own
-            // earlier elements (position order within a group is lane, then c)
-            uint32_t ra = a_run, rt = t_run;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                ra = mbcnt64(ma[c], ra);
-                rt = mbcnt64(mt[c], rt);
-            }
-            const int64_t p0 = ch * kChunk + tbase + 256 * g;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t k = key[4 * g + c];
-                const bool ia = k >= amin2, it = k == tkey2;
-                const uint32_t rank = ra + (rt < need ? rt : need);
-                if ((ia || (it && rt < need)) && rank < kTopK) {
-                    if constexpr (MODE == kMerge)
-                        sm.hist[rank] = static_cast<uint32_t>(cpos[4 * g + c]);
-                    else
-                        sm.hist[rank] = static_cast<uint32_t>(p0 + c);
-                }
-                ra += ia ? 1u : 0u;
-                rt += it ? 1u : 0u;
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                a_run += static_cast<uint32_t>(__popcll(ma[c]));
-                t_run += static_cast<uint32_t>(__popcll(mt[c]));
+            const int sh = 4 * (lane & 7);
+            uint32_t wa = ma << sh, wt = mt << sh;
+            wa |= dpp_u32<kDppQuadXor1>(0u, wa);
+            wa |= dpp_u32<kDppQuadXor2>(0u, wa);
+            wa |= dpp_u32<kDppRowHalfMirror>(0u, wa);
+            const int widx = 2 * E * wave + 8 * g + (lane >> 3);
+            if ((lane & 7) == 0) sm.bm[0][widx] = wa;
+            if (ties) {
+                wt |= dpp_u32<kDppQuadXor1>(0u, wt);
+                wt |= dpp_u32<kDppQuadXor2>(0u, wt);
+                wt |= dpp_u32<kDppRowHalfMirror>(0u, wt);
+                if ((lane & 7) == 0) sm.bm[1][widx] = wt;
             }
         }
-        above_done += a_tot;
-        tie_done += t_tot;
+        lds_barrier();
+        // this thread's words, in position order
+        const int w0 = tid * kWpt;
+        const bool owns = w0 < kWords;
+        uint32_t sel[kWpt];
+#pragma unroll
+        for (int k = 0; k < kWpt; ++k) sel[k] = owns ? sm.bm[0][w0 + k] : 0u;
+        if (ties) {  // keep the first `need` tie bits in position order
+            uint32_t tw[kWpt];
+            uint32_t tc = 0;
+#pragma unroll
+            for (int k = 0; k < kWpt; ++k) {
+                tw[k] = owns ? sm.bm[1][w0 + k] : 0u;
+                tc += static_cast<uint32_t>(__popc(tw[k]));
+            }
+            uint32_t ttot;
+            uint32_t before = block_exclusive_scan(sm, tc, &ttot);
+#pragma unroll
+            for (int k = 0; k < kWpt; ++k) {
+                uint32_t x = tw[k];
+                while (x) {  // drop bits from the lowest once `need` ties are in
+                    const uint32_t bit = x & (0u - x);
+                    if (before >= need) tw[k] &= ~bit;
+                    ++before;
+                    x &= x - 1u;
+                }
+                sel[k] |= tw[k];
+            }
+        }
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int k = 0; k < kWpt; ++k) cnt += static_cast<uint32_t>(__popc(sel[k]));
+        uint32_t stot;
+        uint32_t rank = block_exclusive_scan(sm, cnt, &stot);
+#pragma unroll
+        for (int k = 0; k < kWpt; ++k) {
+            uint32_t x = sel[k];
+            while (x) {
+                const int p = 32 * (w0 + k) + __builtin_ctz(x);
+                int32_t v = p;
+                if constexpr (MODE == kMerge) {
+                    const int q = p / kTopK;
+                    const int32_t local = cands[(static_cast<int64_t>(t) * parts + q) * kTopK + (p - q * kTopK)];
+                    v = static_cast<int32_t>(q * chunk + local);
+                }
+                if (rank < kTopK) sm.hist[rank] = static_cast<uint32_t>(v);
+                ++rank;
+                x &= x - 1u;
+            }
+        }
+    } else {
+        uint32_t above_done = 0, tie_done = 0;  // counts of earlier chunks (block-uniform)
+        for (int ch = 0; ch < n_chunks; ++ch) {
+            if (STREAM) load(ch);
+            uint32_t na = 0, nt = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                na += key[e] >= above_min ? 1u : 0u;
+                nt += key[e] == tie_key ? 1u : 0u;
+            }
+            na = wave_sum_u32(na);
+            nt = wave_sum_u32(nt);
+            uint32_t* cnt = sm.cnt[ch & 1];
+            if (lane == 0) {
+                cnt[wave] = na;
+                cnt[kTopkWaves + wave] = nt;
+            }
+            lds_barrier();
+            uint32_t a_run = above_done, t_run = tie_done, a_tot = 0, t_tot = 0;
+#pragma unroll
+            for (int i = 0; i < kTopkWaves; ++i) {
+                const uint32_t x = cnt[i], y = cnt[kTopkWaves + i];
+                a_run += i < wave ? x : 0u;
+                t_run += i < wave ? y : 0u;
+                a_tot += x;
+                t_tot += y;
+            }
+            // opaque copies keep the compiler from holding the counting loop's 2E lane masks
+            // live (in scalar registers) until they are needed again below
+            uint32_t amin2 = above_min, tkey2 = tie_key;
+            asm volatile("" : "+v"(amin2), "+v"(tkey2));
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) {
+                uint64_t ma[4], mt[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    ma[c] = __ballot(key[4 * g + c] >= amin2);
+                    mt[c] = __ballot(key[4 * g + c] == tkey2);
+                }
+                // counts of this group's elements held by lower lanes, then by this lane's own
+                // earlier elements (position order within a group is lane, then c)
+                uint32_t ra = a_run, rt = t_run;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    ra = mbcnt64(ma[c], ra);
+                    rt = mbcnt64(mt[c], rt);
+                }
+                const int64_t p0 = ch * kChunk + tbase + 256 * g;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t k = key[4 * g + c];
+                    const bool ia = k >= amin2, it = k == tkey2;
+                    const uint32_t rank = ra + (rt < need ? rt : need);
+                    if ((ia || (it && rt < need)) && rank < kTopK) {
+                        if constexpr (MODE == kMerge)
+                            sm.hist[rank] = static_cast<uint32_t>(cpos[4 * g + c]);
+                        else
+                            sm.hist[rank] = static_cast<uint32_t>(p0 + c);
+                    }
+                    ra += ia ? 1u : 0u;
+                    rt += it ? 1u : 0u;
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    a_run += static_cast<uint32_t>(__popcll(ma[c]));
+                    t_run += static_cast<uint32_t>(__popcll(mt[c]));
+                }
+            }
+            above_done += a_tot;
+            tie_done += t_tot;
+        }
     }
     // the ranks fill the staging row once each; it leaves in two coalesced stores per thread
     // (scattered 4-byte stores straight to global memory measured slightly slower)
