@@ -40,16 +40,20 @@ __device__ __forceinline__ uint32_t score_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Score of a key: keys with the top bit set are non-negative scores (their sign bit was set),
+// the others negative ones (all bits were flipped).  Key 1 (NaN) gives a NaN pattern.
 __device__ __forceinline__ float key_to_score(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+    const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(k) >> 31);  // ~0 if top bit set
+    return __uint_as_float(k ^ (~m | 0x80000000u));
 }
 
-// Value-linear bin of a key (monotone non-decreasing in the key).
-__device__ __forceinline__ int value_bin(uint32_t k, float lo, float scale) {
-    if (k <= kKeyNegInf) return 0;
-    if (k >= kKeyPosInf) return kBins - 1;
-    const float f = (key_to_score(k) - lo) * scale;
-    return f < static_cast<float>(kBins) ? static_cast<int>(f) : kBins - 1;
+// Value-linear bin of a key: trunc(clamp(x * scale + off, 0, 2047)) with x its score and
+// off = -lo * scale.  fma, the clamps and truncation are each monotone non-decreasing, so the
+// map is; NaN lands in bin 0 (the max with 0 drops it), -inf in bin 0, +inf in bin 2047.
+__device__ __forceinline__ int value_bin(uint32_t k, float scale, float off) {
+    const float f = fminf(fmaxf(__builtin_fmaf(key_to_score(k), scale, off), 0.f),
+                          static_cast<float>(kBins - 1));
+    return static_cast<int>(f);
 }
 
 __device__ __forceinline__ int shift_for(uint32_t span) {
@@ -138,8 +142,8 @@ __device__ __forceinline__ void block_minmax(TopkSmem& sm, uint32_t& a_min, uint
 // form an interval; both ends exist because some key in [a, b] falls in the bin).  One wave:
 // lanes 0..31 run a 32-ary search for the lower end, lanes 32..63 for the upper end; each
 // step keeps one of 32 sub-intervals, so seven steps cover the 32-bit key space.
-__device__ __forceinline__ void value_bin_key_range(uint32_t a, uint32_t b, int bin, float lo,
-                                                    float scale, uint32_t* r_lo, uint32_t* r_hi) {
+__device__ __forceinline__ void value_bin_key_range(uint32_t a, uint32_t b, int bin, float scale,
+                                                    float bias, uint32_t* r_lo, uint32_t* r_hi) {
     const int lane = lane_id();
     const uint32_t j = static_cast<uint32_t>(lane & 31);
     const bool up = lane >= 32;
@@ -151,7 +155,7 @@ __device__ __forceinline__ void value_bin_key_range(uint32_t a, uint32_t b, int 
         // lower end: probes ascend from l and pass once the bin reaches `bin`;
         // upper end: probes descend from h and pass once the bin drops to `bin`
         const uint32_t k = up ? h - off(j) : l + off(j);
-        const int vb = value_bin(k, lo, scale);
+        const int vb = value_bin(k, scale, bias);
         const uint64_t m = __ballot(up ? vb <= bin : vb >= bin);
         const uint32_t half = static_cast<uint32_t>(up ? (m >> 32) : (m & 0xffffffffu));
         const uint32_t j0 = half ? static_cast<uint32_t>(__builtin_ctz(half)) : 32u;
@@ -264,33 +268,50 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     };
     if (!STREAM) load(0);
 
-    // ---- row statistics: range of finite keys and of all keys
-    uint32_t fmin = ~0u, fmax = 0u, amin = ~0u, amax = 0u;
+    // ---- row statistics: range of all keys, and of the finite ones (a second pass only when
+    // the row holds +-inf or NaN).  Absent elements (key 0) wrap to the top in k - 1.
+    uint32_t amin = ~0u, amax = 0u;
     for (int ch = 0; ch < n_chunks; ++ch) {
         if (STREAM) load(ch);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const uint32_t k = key[e];
-            if (k) {
-                amin = min(amin, k);
-                amax = max(amax, k);
+            amin = min(amin, key[e] - 1u);
+            amax = max(amax, key[e]);
+        }
+    }
+    for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;  // ordered by the barriers below
+    {
+        uint32_t d0 = ~0u, d1 = 0u;
+        block_minmax(sm, amin, amax, d0, d1);
+    }
+    amin += 1u;
+    uint32_t fmin = amin, fmax = amax;
+    if (amin <= kKeyNegInf || amax >= kKeyPosInf) {  // block-uniform
+        fmin = ~0u;
+        fmax = 0u;
+        for (int ch = 0; ch < n_chunks; ++ch) {
+            if (STREAM) load(ch);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t k = key[e];
                 if (k > kKeyNegInf && k < kKeyPosInf) {
                     fmin = min(fmin, k);
                     fmax = max(fmax, k);
                 }
             }
         }
+        uint32_t d0 = ~0u, d1 = 0u;
+        block_minmax(sm, fmin, fmax, d0, d1);
     }
-    for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;  // ordered by the barriers below
-    block_minmax(sm, fmin, fmax, amin, amax);
 
     bool value_mode = false;
-    float lo = 0.f, scale = 0.f;
+    float scale = 0.f, off = 0.f;
     if (fmin < fmax) {
-        lo = key_to_score(fmin);
+        const float lo = key_to_score(fmin);
         const float span = key_to_score(fmax) - lo;
         scale = static_cast<float>(kBins) / span;
-        value_mode = isfinite(scale) && scale > 0.f;
+        off = -lo * scale;
+        value_mode = isfinite(scale) && scale > 0.f && isfinite(off);
     }
 
     uint32_t rlo = amin, rhi = amax;  // candidate key range (inclusive)
@@ -305,7 +326,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const uint32_t k = key[e];
-                if (k) atomicAdd(&sm.hist[value_mode ? value_bin(k, lo, scale) : static_cast<int>((k - rlo) >> sh)], 1u);
+                if (k) atomicAdd(&sm.hist[value_mode ? value_bin(k, scale, off) : static_cast<int>((k - rlo) >> sh)], 1u);
             }
         }
         lds_barrier();
@@ -316,7 +337,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         if (value_mode) {
             if (wave == 0) {
                 uint32_t klo, khi;
-                value_bin_key_range(rlo, rhi, static_cast<int>(bstar), lo, scale, &klo, &khi);
+                value_bin_key_range(rlo, rhi, static_cast<int>(bstar), scale, off, &klo, &khi);
                 if (lane == 0) {
                     sm.prm[2] = klo;
                     sm.prm[3] = khi;
@@ -345,7 +366,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const uint32_t k = key[e];
-                if (k >= rlo && k <= rhi) atomicAdd(&sm.hist[(k - rlo) >> sh], 1u);
+                if (k - rlo <= rhi - rlo) atomicAdd(&sm.hist[(k - rlo) >> sh], 1u);  // k in [rlo, rhi]
             }
         }
         lds_barrier();
