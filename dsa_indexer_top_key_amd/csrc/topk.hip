@@ -68,7 +68,10 @@ struct TopkSmem {
     uint32_t red[4][kTopkWaves];
     uint32_t cnt[2][2 * kTopkWaves];  // per-wave (above, tie) counts, double-buffered by chunk
     uint32_t prm[8];
+    uint32_t cbuf[64];                // keys of a small threshold bin
 };
+
+constexpr uint32_t kFastCand = 64;  // threshold bins up to this size are resolved by one wave
 
 // Exclusive prefix sum over the block (thread order); returns this thread's exclusive sum
 // and writes the block total to *total (all threads).  Contains barriers.
@@ -280,6 +283,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         }
     }
     for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;  // ordered by the barriers below
+    if (tid == 0) sm.prm[4] = 0u;  // fill count of cbuf
     {
         uint32_t d0 = ~0u, d1 = 0u;
         block_minmax(sm, amin, amax, d0, d1);
@@ -320,13 +324,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 
     // ---- level 0
     {
+        // rows held in registers with up to 32 elements per thread keep each element's bin
+        constexpr bool kSaveBins = E <= 32 && !STREAM;
+        uint32_t kbin[kSaveBins ? E : 1];
         const int sh = value_mode ? 0 : shift_for(rhi - rlo);
         for (int ch = 0; ch < n_chunks; ++ch) {
             if (STREAM) load(ch);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const uint32_t k = key[e];
-                if (k) atomicAdd(&sm.hist[value_mode ? value_bin(k, scale, off) : static_cast<int>((k - rlo) >> sh)], 1u);
+                const int bin = value_mode ? value_bin(k, scale, off) : static_cast<int>((k - rlo) >> sh);
+                if (k) atomicAdd(&sm.hist[bin], 1u);
+                if constexpr (kSaveBins) kbin[e] = k ? static_cast<uint32_t>(bin) : 0xFFFFu;
             }
         }
         lds_barrier();
@@ -334,7 +343,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         const uint32_t bstar = sm.prm[0];
         need -= sm.prm[1];
         cand = sm.hist[bstar];
-        if (value_mode) {
+        if (kSaveBins && value_mode && cand <= kFastCand) {  // block-uniform
+            // Small threshold bin: its keys go to LDS and one wave finds the need-th largest
+            // key theta by counting (#keys > theta < need <= #keys >= theta); the final range
+            // is then the single key theta.  (Rows without saved bins would recompute every
+            // element's bin for this, which measured slower than the range search below.)
+#pragma unroll
+            for (int e = 0; e < E; ++e)  // (saved bins imply one register-resident chunk)
+                if (kbin[kSaveBins ? e : 0] == bstar) sm.cbuf[atomicAdd(&sm.prm[4], 1u)] = key[e];
+            lds_barrier();
+            if (wave == 0) {
+                const uint32_t nc = __builtin_amdgcn_readfirstlane(cand);  // uniform loop bound
+                const uint32_t mine = static_cast<uint32_t>(lane) < nc ? sm.cbuf[lane] : 0u;
+                uint32_t gt = 0, ge = 0;
+                for (uint32_t j = 0; j < nc; ++j) {
+                    const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine), static_cast<int>(j)));
+                    gt += o > mine ? 1u : 0u;
+                    ge += o >= mine ? 1u : 0u;
+                }
+                const bool thr = static_cast<uint32_t>(lane) < nc && gt < need && need <= ge;
+                const uint64_t m = __ballot(thr);
+                if (m && lane == static_cast<int>(__builtin_ctzll(m))) {
+                    sm.prm[2] = mine;
+                    sm.prm[3] = gt;
+                    sm.prm[5] = ge - gt;
+                }
+            }
+            lds_barrier();
+            rlo = rhi = sm.prm[2];
+            need -= sm.prm[3];
+            cand = sm.prm[5];
+        } else if (value_mode) {
             if (wave == 0) {
                 uint32_t klo, khi;
                 value_bin_key_range(rlo, rhi, static_cast<int>(bstar), scale, off, &klo, &khi);
