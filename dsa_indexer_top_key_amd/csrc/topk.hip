@@ -328,16 +328,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         constexpr bool kSaveBins = E <= 32 && !STREAM;
         uint32_t kbin[kSaveBins ? E : 1];
         const int sh = value_mode ? 0 : shift_for(rhi - rlo);
-        for (int ch = 0; ch < n_chunks; ++ch) {
-            if (STREAM) load(ch);
+        // one loop per binning (a per-element select on the block-uniform mode compiled into
+        // a branch per element)
+        auto count = [&](auto bin_of) {
+            for (int ch = 0; ch < n_chunks; ++ch) {
+                if (STREAM) load(ch);
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const uint32_t k = key[e];
-                const int bin = value_mode ? value_bin(k, scale, off) : static_cast<int>((k - rlo) >> sh);
-                if (k) atomicAdd(&sm.hist[bin], 1u);
-                if constexpr (kSaveBins) kbin[e] = k ? static_cast<uint32_t>(bin) : 0xFFFFu;
+                for (int e = 0; e < E; ++e) {
+                    const uint32_t k = key[e];
+                    const int bin = bin_of(k);
+                    if (k) atomicAdd(&sm.hist[bin], 1u);
+                    if constexpr (kSaveBins) kbin[e] = k ? static_cast<uint32_t>(bin) : 0xFFFFu;
+                }
             }
-        }
+        };
+        if (value_mode)
+            count([&](uint32_t k) { return value_bin(k, scale, off); });
+        else
+            count([&](uint32_t k) { return static_cast<int>((k - rlo) >> sh); });
         lds_barrier();
         find_threshold_bin(sm, need);
         const uint32_t bstar = sm.prm[0];
