@@ -92,9 +92,17 @@ def timed(fn, steps, warmup, stream, torch):
 
 
 def per_call_events(fn, steps, stream, torch):
-    """Average duration of each call, each bracketed by its own pair of events."""
+    """Average duration of each call, each bracketed by its own pair of events.  A short GPU
+    spin queued first keeps the GPU behind the host while all calls are enqueued, so a call
+    shorter than its host-side launch cost is still timed by the GPU alone."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
+    torch.cuda.synchronize()
+    try:
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(2e6) * max(1, steps // 10))  # about 1 ms per 10 calls
+    except (AttributeError, RuntimeError):
+        pass
     for a, b in evs:
         a.record(stream)
         fn()
