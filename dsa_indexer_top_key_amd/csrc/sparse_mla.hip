@@ -170,28 +170,53 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     __shared__ MlaSmem sm;
     const int g = blockIdx.x;
     const int j = g >> 3;
-    const int t = (g & 7) + 8 * (j / nsplit);
-    const int split = j - (j / nsplit) * nsplit;
+    const int lsplit = __builtin_ctz(static_cast<unsigned>(nsplit));  // nsplit: a power of two
+    const int t = (g & 7) + 8 * (j >> lsplit);
+    const int split = j & (nsplit - 1);
     if (t >= T) return;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
     const int hh = lane >> 5;  // lane half
     const int hl = lane & 31;  // head column (S^T) / A-operand row
-    const int L = kTopK / nsplit;
-    const int b = q_req[t];
-    const int64_t base = kv_off[b];
-    const int64_t s_b = kv_off[b + 1] - base;
+    const int L = kTopK >> lsplit;
+    // Head-group waves load their 32 absorbed queries first, so the loads overlap the ID phase.
+    u32x4 qf[kKSteps];
+    if (wave < 3) {
+        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
+            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
+            // the last kQfInAcc fragments live in accumulation registers (MFMA reads its B
+            // operand from there directly), leaving VGPRs for deep LDS prefetch
+            if (s >= kKSteps - kQfInAcc) asm volatile("" : "+a"(qf[s]));
+        }
+    }
 
     // ---- the split's IDs into LDS: padding (ID < 0 or >= S_b) becomes row 0 of the request
     // (real data, so every ring slot stays finite) and is masked out of the softmax through a
-    // per-tile bit mask.  Tiles after the last real ID are not processed.
+    // per-tile bit mask.  Tiles after the last real ID are not processed.  The ID loads are
+    // issued before the request lookups (q_req, then kv_off) they do not depend on.
+    constexpr int kIdPerThread = kTopK / 256;
     const int32_t* idr = ids + static_cast<int64_t>(t) * kTopK + static_cast<int64_t>(split) * L;
+    int32_t idv[kIdPerThread];
+#pragma unroll
+    for (int k = 0; k < kIdPerThread; ++k) {
+        const int i = 256 * k + tid;
+        idv[k] = i < L ? idr[i] : -1;
+    }
+    const int b = q_req[t];
+    const int64_t base = kv_off[b];
+    const int64_t s_b = kv_off[b + 1] - base;
     if (tid == 0) sm.redo = 0;
     uint32_t end = 0;
-    for (int i0 = 0; i0 < L; i0 += 256) {
+#pragma unroll
+    for (int k = 0; k < kIdPerThread; ++k) {
+        const int i0 = 256 * k;
+        if (i0 >= L) break;  // block-uniform
         const int i = i0 + tid;
-        const int32_t id = i < L ? idr[i] : -1;
+        const int32_t id = idv[k];
         const bool ok = id >= 0 && static_cast<int64_t>(id) < s_b;
         const uint64_t m = __ballot(ok);  // lanes 0..31: one tile, lanes 32..63: the next
         if (i < L) {
@@ -315,19 +340,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         return;
     }
 
-    // ================= head-group waves: heads 32*wave .. 32*wave+31
-    u32x4 qf[kKSteps];
-    {
-        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
-#pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
-            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
-            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
-            // the last kQfInAcc fragments live in accumulation registers (MFMA reads its B
-            // operand from there directly), leaving VGPRs for deep LDS prefetch
-            if (s >= kKSteps - kQfInAcc) asm volatile("" : "+a"(qf[s]));
-        }
-    }
+    // ================= head-group waves: heads 32*wave .. 32*wave+31 (qf loaded above)
     f32x16 o[kConsTiles];
     float m_ref = -INFINITY;   // reference logit of this lane's head (log2 domain)
     float m_seen = -INFINITY;  // largest logit seen (exact maximum after a full pass)
