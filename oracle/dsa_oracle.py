@@ -293,6 +293,45 @@ def sparse_mla(q, latent, kpe, kv_off, q_req, ids, scale, rows=None):
 
 
 # ----------------------------------------------------------------------------------------
+# Post-read epilogue (the row after stage 4).  Section "Was ändert sich – und was nicht?":
+# 96 main-attention heads with 128-wide value heads; the read above stays in the shared
+# 512-wide latent (absorbed MLA), so each head's value comes from its own up-projection of
+# that read.  The paragraph after the Gated-MLA one: after the sparse attention and before
+# the output projection a learned, coordinatewise sigmoid output gate is applied; the K3
+# guide's MLA section adds that the gate is input-dependent and acts on the attention
+# output.  Reading (the pages give no formula): per query t and head h
+#   v_th = W_UV[h] o_th            (128 x 512 times 512)
+#   u_th = v_th * sigmoid(g_th)    (elementwise over the 128 coordinates)
+# with W_UV [96,128,512] the learned up-projection and g [T,96,128] the gate logits that an
+# upstream projection of the token's hidden state produces (both inputs here).
+# ----------------------------------------------------------------------------------------
+def sigmoid(x) -> np.ndarray:
+    """1 / (1 + exp(-x)) in float64, written in the form that does not overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def value_gate(o, w_uv, gate) -> np.ndarray:
+    """u [T,96,128] = (W_UV[h] o_th) * sigmoid(g_th); o is the read (bf16 bits or float),
+    w_uv [96,128,512] and gate [T,96,128] are bf16 bits."""
+    o = np.asarray(o)
+    o64 = bf16_to_f64(o) if o.dtype == np.uint16 else o.astype(np.float64)
+    w = bf16_to_f64(w_uv)
+    g = bf16_to_f64(gate)
+    v = np.einsum("hck,thk->thc", w, o64)  # one contraction per (t, h): W_UV[h] @ o_th
+    return v * sigmoid(g)
+
+
+def value_gate_magnitude(o, w_uv, gate) -> np.ndarray:
+    """sum_k |W_UV[h,c,k] o_thk| * sigmoid(g_thc): the scale of the rounding error of any
+    finite-precision evaluation of value_gate."""
+    o = np.asarray(o)
+    o64 = bf16_to_f64(o) if o.dtype == np.uint16 else o.astype(np.float64)
+    return np.einsum("hck,thk->thc", np.abs(bf16_to_f64(w_uv)), np.abs(o64)) * sigmoid(bf16_to_f64(gate))
+
+
+# ----------------------------------------------------------------------------------------
 # Dense reference and dropped mass (oracle only, never timed).
 # Section "Die Mathematik ...": compared with a hypothetical full read at fixed logits and
 # values, with eps the full softmax mass outside I_t, the retained and dropped reads are
