@@ -11,13 +11,13 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["DsaError", "library", "index_keys_layernorm", "indexer_scores", "topk",
+__all__ = ["DsaError", "library", "index_keys_layernorm", "indexer_scores", "topk", "value_gate",
            "indexer_topk", "indexer_topk_workspace_size", "sparse_mla_attn",
            "sparse_mla_workspace_size", "INDEX_HEADS", "INDEX_DIM", "TOPK", "MLA_HEADS",
-           "LATENT_DIM", "COMPANION_DIM"]
+           "LATENT_DIM", "COMPANION_DIM", "VALUE_DIM"]
 
 INDEX_HEADS, INDEX_DIM, TOPK = 32, 128, 2048
-MLA_HEADS, LATENT_DIM, COMPANION_DIM = 96, 512, 64
+MLA_HEADS, LATENT_DIM, COMPANION_DIM, VALUE_DIM = 96, 512, 64, 128
 QK_DIM = LATENT_DIM + COMPANION_DIM
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_amd.so")
@@ -54,6 +54,7 @@ _SIGNATURES = {
     "dsa_sparse_mla_workspace_size": ([_i32, _i32, _i32], _sz),
     "dsa_sparse_mla_attn": ([_p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p,
                              _i32, _p, _p, _sz, _p], ctypes.c_int),
+    "dsa_value_gate": ([_p, _p, _p, _i32, _i32, _p, _p], ctypes.c_int),
 }
 
 
@@ -234,3 +235,21 @@ def sparse_mla_attn(q, latent, kpe, kv_off, q_req, ids, scale: float, out=None, 
         b, h, ids.shape[1], float(scale), _ptr(_contig(out, "out")), out_code, _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
+
+
+def value_gate(o, w_uv, gate, out=None, stream=None):
+    """Value up-projection and sigmoid output gate of the read: o [T,96,512] bf16,
+    w_uv [96,128,512] bf16, gate [T,96,128] bf16 logits -> out [T,96,128] bf16 with
+    out[t,h] = (w_uv[h] @ o[t,h]) * sigmoid(gate[t,h])."""
+    torch = _torch()
+    for x, n in ((o, "o"), (w_uv, "w_uv"), (gate, "gate")):
+        _contig(_bits16(_dev(x, n), n), n)
+    t, h = o.shape[0], o.shape[1]
+    if tuple(o.shape[1:]) != (h, LATENT_DIM) or tuple(w_uv.shape) != (h, VALUE_DIM, LATENT_DIM) \
+            or tuple(gate.shape) != (t, h, VALUE_DIM):
+        raise ValueError("value_gate expects o [T,H,512], w_uv [H,128,512], gate [T,H,128]")
+    if out is None:
+        out = torch.empty((t, h, VALUE_DIM), dtype=torch.bfloat16, device=o.device)
+    _check("dsa_value_gate", library().dsa_value_gate(
+        _ptr(o), _ptr(w_uv), _ptr(gate), t, h, _ptr(_contig(out, "out")), _stream(stream)))
+    return out

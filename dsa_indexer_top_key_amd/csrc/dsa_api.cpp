@@ -28,6 +28,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
                              void* out, bool out_f32, float* lse, void* workspace,
                              hipStream_t stream);
 size_t sparse_mla_workspace_bytes(int32_t T);
+hipError_t launch_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
+                             int32_t T, uint16_t* out, hipStream_t stream);
 }  // namespace dsa
 
 namespace {
@@ -250,3 +252,16 @@ dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int6
 }
 
 }  // extern "C"
+
+dsa_status_t dsa_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
+                            int32_t T, int32_t n_heads, uint16_t* out, void* stream) {
+    const char* fn = "dsa_value_gate";
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    DSA_REQUIRE(n_heads == DSA_MLA_HEADS, DSA_ERR_UNSUPPORTED, "%s: n_heads=%d unsupported (only %d)",
+                fn, n_heads, DSA_MLA_HEADS);
+    if (T == 0) return DSA_OK;
+    DSA_REQUIRE(o && w_uv && gate && out, DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+    DSA_REQUIRE(aligned(o, 16) && aligned(w_uv, 16) && aligned(gate, 2) && aligned(out, 4),
+                DSA_ERR_INVALID_ARG, "%s: o and w_uv must be 16-byte, gate 2-byte, out 4-byte aligned", fn);
+    return from_hip(dsa::launch_value_gate(o, w_uv, gate, T, out, static_cast<hipStream_t>(stream)), fn);
+}

@@ -131,27 +131,6 @@ __device__ __forceinline__ bf16x8 v_fragment(lds_u16* vbase, int nt, int c) {
     return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Store one 32 x 32 accumulator tile of O (rows row0 + 8(r/4) + 4hh + r%4 for r = 0..15,
-// column col0 + lane % 32) into a row-major matrix with leading dimension ld.  bf16: lanes
-// 2j and 2j+1 trade one value (DPP swap of adjacent lanes) so that each lane stores two
-// adjacent columns of one row in 4 bytes -- the even lane row R, the odd lane row R + 1 --
-// half as many store instructions, each writing 64-byte runs.
-__device__ __forceinline__ void store_tile_bf16(uint16_t* dst, int64_t ld, int row0, int col0,
-                                                const float (&v)[16], int lane) {
-    const bool odd = lane & 1;
-    const int hh = (lane >> 5) & 1;
-    const int col = col0 + (lane & 31);
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        const int row = row0 + 8 * (r >> 2) + 4 * hh + (r & 3);  // r % 4 is 0 or 2
-        const float send = odd ? v[r] : v[r + 1];
-        const float recv = __uint_as_float(dpp_u32<kDppQuadXor1>(0u, __float_as_uint(send)));
-        const uint32_t packed = odd ? pack_bf16x2(recv, v[r + 1]) : pack_bf16x2(v[r], recv);
-        const int64_t off = static_cast<int64_t>(row + (odd ? 1 : 0)) * ld + col - (odd ? 1 : 0);
-        *reinterpret_cast<uint32_t*>(dst + off) = packed;
-    }
-}
-
 __device__ __forceinline__ void store_tile_f32(float* dst, int64_t ld, int row0, int col0,
                                                const float (&v)[16], int lane) {
     const int hh = (lane >> 5) & 1;

@@ -64,6 +64,7 @@ typedef enum {
 #define DSA_TOPK 2048
 #define DSA_MLA_HEADS 96
 #define DSA_LATENT_DIM 512
+#define DSA_VALUE_DIM 128
 #define DSA_COMPANION_DIM 64
 #define DSA_WORKSPACE_ALIGN 256
 
@@ -174,6 +175,25 @@ dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int6
                                  int32_t B, int32_t n_heads, int32_t topk, float scale,
                                  void* out, int32_t out_dtype, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * After stage 4 -- value up-projection and sigmoid output gate of the read.
+ * Page "Kimi K3.1 Pro: Sparse-Zugriffe, keine kleinere Historie": 96 heads with 128-wide
+ * value heads (section "Was ändert sich – und was nicht?"); a learned, coordinatewise,
+ * input-dependent sigmoid output gate after the sparse attention and before the output
+ * projection (the paragraph after the Gated-MLA one).
+ * o        [T,96,512] bf16, 16-byte aligned: the read (dsa_sparse_mla_attn's bf16 output).
+ * w_uv     [96,128,512] bf16, 16-byte aligned: per-head up-projection, row c of head h maps
+ *          the latent to value coordinate c.
+ * gate     [T,96,128] bf16 gate logits (2-byte aligned), produced upstream from the token.
+ * n_heads  must be 96 (else UNSUPPORTED).
+ * out      [T,96,128] bf16 out, 4-byte aligned:
+ *          out[t][h][c] = (sum_k w_uv[h][c][k] * o[t][h][k]) * 1 / (1 + exp(-gate[t][h][c])),
+ *          products and sums in fp32, the sigmoid in fp32, rounded to bf16 (nearest even).
+ * Errors: INVALID_ARG for T < 0 or null/misaligned pointers when T > 0.
+ */
+dsa_status_t dsa_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
+                            int32_t T, int32_t n_heads, uint16_t* out, void* stream);
 
 #ifdef __cplusplus
 }

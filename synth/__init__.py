@@ -9,9 +9,12 @@ sharing code with each other.  Every array is seeded separately with
     3 raw index keys [N,128] fp32 (bf16 for the long-context workload)
     4 LayerNorm gamma [128]   5 LayerNorm beta [128]   6 latent [N,512] (or [N,576])
     7 companion keys [N,64]   8 absorbed main queries [T,96,576] bf16
+    10 value up-projection W_UV [96,128,512] bf16   11 output-gate logits [T,96,128] bf16
+    12 a stand-in read o [T,96,512] bf16 (for the epilogue alone)
 
 Distributions: index queries, raw keys, latents and main queries N(0,1); head weights
-N(0, 1/32); gamma 1 + N(0, 0.1); beta N(0, 0.1).  The second argument of N is read as
+N(0, 1/32); gamma 1 + N(0, 0.1); beta N(0, 0.1); W_UV N(0, 1/512) (unit gain); gate logits
+N(0, 1); stand-in reads N(0, 0.1) (a read is a convex combination of N(0,1) rows).  The second argument of N is read as
 the variance.  BF16 values are rounded from float32 with round-to-nearest-even.
 
 CPU generation uses numpy's PCG64; large workloads are generated on the GPU with torch's
@@ -31,6 +34,9 @@ W_STD = (1.0 / 32.0) ** 0.5
 AFFINE_STD = 0.1 ** 0.5
 LN_EPS = 1e-6
 ATTN_SCALE = 1.0 / 192.0 ** 0.5
+VALUE_DIM = 128
+WUV_STD = (1.0 / 512.0) ** 0.5
+READ_STD = 0.1 ** 0.5
 
 
 def bf16_bits_from_f32(x) -> np.ndarray:
@@ -146,6 +152,10 @@ def inputs_np(lay: Layout, parts=("index", "ln", "mla")) -> dict:
             d["latent"] = bf16_bits_from_f32(_normal(s, 6, (n, LATENT_DIM)))
             d["kpe"] = bf16_bits_from_f32(_normal(s, 7, (n, COMPANION_DIM)))
         d["q"] = bf16_bits_from_f32(_normal(s, 8, (t, MLA_HEADS, QK_DIM)))
+    if "gate" in parts:
+        d["w_uv"] = bf16_bits_from_f32(_normal(s, 10, (MLA_HEADS, VALUE_DIM, LATENT_DIM), std=WUV_STD))
+        d["gate"] = bf16_bits_from_f32(_normal(s, 11, (t, MLA_HEADS, VALUE_DIM)))
+        d["o"] = bf16_bits_from_f32(_normal(s, 12, (t, MLA_HEADS, LATENT_DIM), std=READ_STD))
     return d
 
 
@@ -234,6 +244,10 @@ def inputs_torch(lay: Layout, device, parts=("index", "ln", "mla")) -> dict:
             d["latent"] = normal(6, (n, LATENT_DIM))
             d["kpe"] = normal(7, (n, COMPANION_DIM))
         d["q"] = normal(8, (t, MLA_HEADS, QK_DIM))
+    if "gate" in parts:
+        d["w_uv"] = normal(10, (MLA_HEADS, VALUE_DIM, LATENT_DIM), std=WUV_STD)
+        d["gate"] = normal(11, (t, MLA_HEADS, VALUE_DIM))
+        d["o"] = normal(12, (t, MLA_HEADS, LATENT_DIM), std=READ_STD)
     return d
 
 

@@ -155,3 +155,17 @@ def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
         dsa.index_keys_layernorm(torch.zeros(4, 128), torch.ones(128), torch.zeros(128))
+
+
+def test_value_gate_validation():
+    lib = dsa.library()
+    vg = lambda o=fake(), w=fake(), g=fake(), T=2, H=96, out=fake(): lib.dsa_value_gate(o, w, g, T, H, out, P(0))
+    assert vg(T=0, o=P(0), w=P(0), g=P(0), out=P(0)) == OK  # nothing to do, no pointer touched
+    assert vg(T=-1) == INVALID
+    assert vg(H=128) == UNSUPPORTED
+    assert vg(o=P(0)) == INVALID
+    assert vg(out=P(0)) == INVALID
+    assert vg(o=fake(0x10008)) == INVALID   # o must be 16-byte aligned
+    assert vg(w=fake(0x10004)) == INVALID   # w_uv must be 16-byte aligned
+    assert vg(out=fake(0x10002)) == INVALID  # out must be 4-byte aligned
+    assert vg(g=fake(0x10001)) == INVALID   # gate must be 2-byte aligned

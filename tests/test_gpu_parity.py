@@ -430,3 +430,76 @@ def test_end_to_end_small_workloads(name):
                       synth.ATTN_SCALE, rows=same)
     assert np.all(np.abs(o - dr["o_full"]) <= dr["eps"][:, :, None] * dr["v_range"][:, None, :]
                   + out_tolerance(dr["o_full"], False))
+
+
+# ---------------------------------------------------------------------------------------
+# after stage 4: value up-projection and sigmoid output gate
+# ---------------------------------------------------------------------------------------
+def bf16_ulp(v):
+    """Spacing of bf16 numbers at |v| (8 significant bits; subnormal floor 2^-133)."""
+    a = np.abs(v)
+    return np.where(a > 0, np.ldexp(1.0, np.maximum(np.frexp(a)[1] - 8, -133)), np.ldexp(1.0, -133))
+
+
+def vg_tolerance(ref, mag):
+    """One bf16 ulp of the result (its rounding, with room for the fp32 value to sit across a
+    binade boundary) plus the fp32 error of a 512-term dot product and the fp32 sigmoid:
+    <= 512 * 2^-24 of the sum of |terms| (2^-15), doubled."""
+    return bf16_ulp(ref) + 2.0 ** -14 * mag
+
+
+def run_vg(o, w_uv, gate):
+    dsa = dsa_mod()
+    out = dsa.value_gate(dev(o), dev(w_uv), dev(gate))
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("t_count", [1, 33, 64, 300])
+def test_value_gate_parity(t_count):
+    print(f"[value_gate] T={t_count}", flush=True)
+    lay = synth.decode_layout("vg", 50 + t_count, [100] * t_count)
+    d = synth.inputs_np(lay, parts=("gate",))
+    got = run_vg(d["o"], d["w_uv"], d["gate"])
+    ref = O.value_gate(d["o"], d["w_uv"], d["gate"])
+    mag = O.value_gate_magnitude(d["o"], d["w_uv"], d["gate"])
+    err = np.abs(got - ref)
+    assert np.all(err <= vg_tolerance(ref, mag)), f"max err {err.max()}"
+
+
+def test_value_gate_exact_on_integer_inputs_and_gate_extremes():
+    """Small integers make the fp32 contraction exact; logits of +-2^100 and +-inf give gates
+    of exactly 1 and 0, NaN logits give NaN: the output must equal the oracle bit for bit."""
+    print("[value_gate] exact", flush=True)
+    g = np.random.default_rng(61)
+    t = 40
+    o = synth.bf16_bits_from_f32(g.integers(-2, 3, size=(t, 96, 512)))
+    w = synth.bf16_bits_from_f32(g.integers(-1, 2, size=(96, 128, 512)) * (g.random((96, 128, 512)) < 0.1))
+    lg = np.where(g.random((t, 96, 128)) < 0.5, 2.0 ** 100, -(2.0 ** 100)).astype(np.float32)
+    lg[0, 0, :4] = [np.inf, -np.inf, np.nan, 0.0]
+    gate = synth.bf16_bits_from_f32(lg)
+    got = run_vg(o, w, gate)
+    ref = O.value_gate(o, w, gate)
+    assert np.all(np.abs(ref[np.isfinite(ref)]) < 256)  # every result is a bf16 integer
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.isnan(got[0, 0, 2])
+
+
+def test_value_gate_on_the_sparse_read():
+    """End to end after stage 4: the epilogue applied to the GPU read equals the oracle's
+    epilogue of the same (bf16) read."""
+    print("[value_gate] after the read", flush=True)
+    lay = synth.decode_layout("vgr", 62, [3000, 2500, 40])
+    d = synth.inputs_np(lay, parts=("mla", "gate"))
+    ids = synth.random_ids_np(62, lay)
+    dsa = dsa_mod()
+    o, _ = dsa.sparse_mla_attn(dev(d["q"]), dev(d["latent"]), dev(d["kpe"]), dev(lay.kv_off),
+                               dev(lay.q_req), dev(ids), synth.ATTN_SCALE)
+    u = dsa.value_gate(o, dev(d["w_uv"]), dev(d["gate"]))
+    torch.cuda.synchronize()
+    o_bits = host_bits(o)
+    ref = O.value_gate(o_bits, d["w_uv"], d["gate"])
+    mag = O.value_gate_magnitude(o_bits, d["w_uv"], d["gate"])
+    assert np.all(np.abs(u.float().cpu().numpy() - ref) <= vg_tolerance(ref, mag))
