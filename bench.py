@@ -196,12 +196,21 @@ def main():
     def ln_fill():
         dsa.index_keys_layernorm(d["raw_keys"], d["gamma"], d["beta"], synth.LN_EPS, keys=keys)
 
+    # post-read epilogue (value up-projection + sigmoid gate) on the read of this batch;
+    # measured beside the step, which covers the four stages of the read path
+    dg = synth.inputs_torch(lay, dev, parts=("gate",))
+    u_out = torch.empty((lay.T, 96, 128), dtype=torch.bfloat16, device=dev)
+
+    def value_gate():
+        dsa.value_gate(out, dg["w_uv"], dg["gate"], out=u_out)
+
     if args.profile_kernels:
         for _ in range(10):
             step()
             scores_only()
             topk_only()
             ln_fill()
+            value_gate()
         torch.cuda.synchronize()
         n = 256 << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -225,6 +234,9 @@ def main():
     ms_scores = per_call_events(scores_only, args.steps, stream, torch)
     ms_topk = per_call_events(topk_only, args.steps, stream, torch)
     ms_ln = per_call_events(ln_fill, max(3, args.steps // 4), stream, torch)
+    ms_vg = per_call_events(value_gate, args.steps, stream, torch)
+    vg_bytes = 96 * 128 * 512 * 2 + lay.T * 96 * (512 + 2 * 128) * 2  # W_UV, o, gate, out
+    vg_flops = 2 * lay.T * 96 * 128 * 512
     qps = lay.T / (ms_step * 1e-3)
     gbps = alg["bytes"] / (ms_step * 1e-3) / 1e9
     scores_gbps = alg["bytes_indexer"] / (ms_scores * 1e-3) / 1e9
@@ -245,6 +257,9 @@ def main():
                       "scores_kernel": round(ms_scores, 5), "topk_kernel": round(ms_topk, 5),
                       "ln_cache_fill": round(ms_ln, 5)},
         "ln_cache_fill_GBps": round(ln_bytes / (ms_ln * 1e-3) / 1e9, 1),
+        "post_read_value_gate": {"ms": round(ms_vg, 5), "bytes": vg_bytes,
+                                 "GBps": round(vg_bytes / (ms_vg * 1e-3) / 1e9, 1),
+                                 "tflops": round(vg_flops / (ms_vg * 1e-3) / 1e12, 1)},
         "sparse_mla_tflops": round(alg["flops_mla"] / (ms_mla * 1e-3) / 1e12, 1),
         "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm",
                      "achieved": round(scores_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
