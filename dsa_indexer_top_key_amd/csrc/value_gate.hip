@@ -12,86 +12,110 @@
 // Bytes per call: T x (96 x 512 + 2 x 96 x 128) bf16 plus the 12.6 MB of W_UV; 128 MACs per
 // byte of W_UV when T is large, 1 MAC per byte of o -- HBM-bound at every batch size.
 //
-// One block per (32 queries, head h); block index = query tile x 96 + h, so every block of a
-// head lands on the same XCD (96 is a multiple of 8) and W_UV[h] (128 KB) stays in that
-// XCD's L2 across query tiles.  Eight waves: wave w computes value columns 32 (w % 4) ..
-// +31 over latent half w / 4 (256 dims) with v_mfma_f32_32x32x16_bf16 (A = 32 query rows of
-// o, B = 32 rows of W_UV[h], K = latent dims), issuing all of its 32 loads before the first
-// MFMA -- the call is small and latency-bound at decode sizes, so every byte a wave needs is
-// requested at once.  The upper-half waves hand their partial sums to the lower-half waves
-// through LDS.  K order: in each 64-dim slab a lane (row r, half hh) loads 64 contiguous
-// bytes, dims 32 hh .. 32 hh + 31 of the slab, and K-step j of the slab takes its j-th 16
-// bytes; A and B use the same order, so the contraction is unchanged.  The gate is applied to
-// the fp32 sums (sigmoid in fp32) and the result is stored as bf16 (round to nearest even).
+// One block per (head h, range of 32-query tiles); the four waves own the four groups of 32
+// value columns.  Each wave keeps its 32 rows of W_UV[h] -- all 512 latent dims, as the B
+// operands of the 32 K-steps -- in registers for the whole block, so the weights are read
+// once per block.  The query tiles stream through a two-slot LDS ring by direct
+// global->LDS copies: the 32 rows of o (one 1 KB row per copy instruction, whole 128-byte
+// lines) and the 32 gate rows of head h (four 256-byte rows per copy), one tile ahead.  Per
+// tile a wave runs 32 v_mfma_f32_32x32x16_bf16 (A = query rows of o from LDS at a 1040-byte
+// row stride, bank-conflict-free), applies the gate to the fp32 sums (sigmoid in fp32) and
+// stores bf16 (round to nearest even).  Block index = split x 96 + h, so all blocks of a head
+// run on one XCD (96 is a multiple of 8) and share W_UV[h] in its L2.
 #include "common.h"
 
 namespace dsa {
 
-constexpr int kValueDim = 128;        // value head width
-constexpr int kVgRows = 32;           // queries per block
-constexpr int kVgSlabs = kLatent / 64 / 2;  // 64-dim slabs per latent half
+constexpr int kValueDim = 128;          // value head width
+constexpr int kVgRows = 32;             // queries per tile
+constexpr int kVgStride = kLatent + 8;  // LDS row stride of o in bf16 elements (1040 bytes)
+constexpr int kVgCopies = 8 + 2;        // copies per wave and tile: 8 rows of o, 2 x 4 gate rows
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
-__global__ __launch_bounds__(512) void value_gate_kernel(const uint16_t* __restrict__ o,
-                                                         const uint16_t* __restrict__ w_uv,
-                                                         const uint16_t* __restrict__ gate,
-                                                         int32_t T, uint16_t* __restrict__ out) {
-    __shared__ f32x16 part[4][64];  // upper-half partial sums, per column group and lane
+__global__ __launch_bounds__(256, 1) void value_gate_kernel(const uint16_t* __restrict__ o,
+                                                            const uint16_t* __restrict__ w_uv,
+                                                            const uint16_t* __restrict__ gate,
+                                                            int32_t T, int32_t n_tiles,
+                                                            int32_t n_split,
+                                                            uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][kVgRows * kVgStride];
+    __shared__ __attribute__((aligned(16))) uint16_t g_lds[2][kVgRows * kValueDim];
     const int h = static_cast<int>(blockIdx.x) % kMlaHeads;
-    const int t0 = (static_cast<int>(blockIdx.x) / kMlaHeads) * kVgRows;
+    const int split = static_cast<int>(blockIdx.x) / kMlaHeads;
+    const int tt0 = static_cast<int>(static_cast<int64_t>(n_tiles) * split / n_split);
+    const int tt1 = static_cast<int>(static_cast<int64_t>(n_tiles) * (split + 1) / n_split);
     const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int cg = wave & 3;   // value columns 32 cg .. 32 cg + 31
-    const int kh = wave >> 2;  // latent dims 256 kh .. 256 kh + 255
+    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave = column group
     const int r = lane & 31;
     const int hh = lane >> 5;
-    // A row: query t0 + r (rows past T read the last query; their results are not stored)
-    const int tq = t0 + r < T ? t0 + r : T - 1;
-    const u32x4* arow = reinterpret_cast<const u32x4*>(o + (static_cast<int64_t>(tq) * kMlaHeads + h) * kLatent + 256 * kh + 32 * hh);
-    const u32x4* brow = reinterpret_cast<const u32x4*>(w_uv + (static_cast<int64_t>(h) * kValueDim + 32 * cg + r) * kLatent + 256 * kh + 32 * hh);
-    u32x4 a[kVgSlabs][4], b[kVgSlabs][4];
+    // this wave's W_UV rows: B operand of K-step s is dims 16 s + 8 hh .. +8 of row 32 cg + r
+    u32x4 bw[kLatent / 16];
+    {
+        const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kValueDim + 32 * cg + r) * kLatent + 8 * hh;
 #pragma unroll
-    for (int s2 = 0; s2 < kVgSlabs; ++s2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {  // a slab is 64 dims = 8 u32x4 further along the row
-            a[s2][j] = arow[8 * s2 + j];
-            b[s2][j] = brow[8 * s2 + j];
-        }
-    // keep every load ahead of the MFMAs (left alone, the scheduler sinks each load next to
-    // its MFMA and leaves about three in flight)
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 acc = {};
-#pragma unroll
-    for (int s2 = 0; s2 < kVgSlabs; ++s2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[s2][j]), as_bf16x8(b[s2][j]), acc, 0, 0, 0);
-    if (kh == 1) part[cg][lane] = acc;
-    __syncthreads();
-    if (kh == 1) return;  // block-uniform per wave; no barrier follows
-    acc += part[cg][lane];
-    // epilogue: acc[i] is query row 8(i/4) + 4hh + i%4, value column 32 cg + r
-    const int col = 32 * cg + r;
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = t0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const int rr = row < T ? row : T - 1;
-        const float g = bf16_to_f32(gate[(static_cast<int64_t>(rr) * kMlaHeads + h) * kValueDim + col]);
-        v[i] = acc[i] * sigmoidf_(g);
+        for (int s = 0; s < kLatent / 16; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
     }
-    store_tile_bf16(out + (static_cast<int64_t>(t0) * kMlaHeads + h) * kValueDim, kMlaHeads * kValueDim,
-                    0, 32 * cg, v, lane, T - t0);
+    // copies of tile tt into slot b: rows 8 cg .. 8 cg + 7 of o, gate rows 8 cg .. 8 cg + 7
+    // (lane l of a gate copy moves bytes 16 (l % 16) .. of gate row 4 k + l / 16); rows past T
+    // copy the last query
+    auto stage = [&](int tt, int b) {
+        const int t0 = tt * kVgRows;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int row = 8 * cg + k;
+            const int tq = t0 + row < T ? t0 + row : T - 1;
+            copy_to_lds(o + (static_cast<int64_t>(tq) * kMlaHeads + h) * kLatent + 8 * lane,
+                        lds_offset(a_lds[b] + row * kVgStride));
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int row = 8 * cg + 4 * k + (lane >> 4);
+            const int tq = t0 + row < T ? t0 + row : T - 1;
+            copy_to_lds(gate + (static_cast<int64_t>(tq) * kMlaHeads + h) * kValueDim + 8 * (lane & 15),
+                        lds_offset(g_lds[b] + (8 * cg + 4 * k) * kValueDim));
+        }
+    };
+    if (tt0 < tt1) stage(tt0, 0);
+    for (int tt = tt0; tt < tt1; ++tt) {
+        const int b = (tt - tt0) & 1;
+        // tile tt landed once only the copies issued after it may be outstanding
+        if (tt + 1 < tt1) {
+            stage(tt + 1, b ^ 1);
+            wait_vmcnt<kVgCopies>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();  // every wave's copies of tile tt are in
+        const uint16_t* ap = a_lds[b] + r * kVgStride + 8 * hh;
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < kLatent / 16; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(*reinterpret_cast<const u32x4*>(ap + 16 * s)), as_bf16x8(bw[s]), acc, 0, 0, 0);
+        // epilogue: acc[e] is query row 8(e/4) + 4hh + e%4 of the tile, value column 32 cg + r
+        const int t0 = tt * kVgRows;
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = 8 * (e >> 2) + 4 * hh + (e & 3);
+            v[e] = acc[e] * sigmoidf_(bf16_to_f32(g_lds[b][row * kValueDim + 32 * cg + r]));
+        }
+        store_tile_bf16(out + (static_cast<int64_t>(t0) * kMlaHeads + h) * kValueDim,
+                        kMlaHeads * kValueDim, 0, 32 * cg, v, lane, T - t0);
+        __syncthreads();  // slot b is refilled by the next iteration's copies
+    }
 }
 
 hipError_t launch_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
                              int32_t T, uint16_t* out, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    const int64_t blocks = static_cast<int64_t>((T + kVgRows - 1) / kVgRows) * kMlaHeads;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(value_gate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(512), 0,
-                       stream, o, w_uv, gate, T, out);
+    const int n_tiles = (T + kVgRows - 1) / kVgRows;
+    // splits per head: up to 8 (768 blocks: three rounds of one block per CU), at most one
+    // per tile
+    const int n_split = n_tiles < 8 ? n_tiles : 8;
+    hipLaunchKernelGGL(value_gate_kernel, dim3(static_cast<unsigned>(kMlaHeads * n_split)), dim3(256),
+                       0, stream, o, w_uv, gate, T, n_tiles, n_split, out);
     return hipGetLastError();
 }
 
