@@ -20,11 +20,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa_amd.so")
-SOURCES = ["ln_keys.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "value_gate.hip", "dsa_api.cpp"]
+SOURCES = ["ln_keys.hip", "indexer.hip", "indexer_prefill.hip", "topk.hip", "sparse_mla.hip", "value_gate.hip", "dsa_api.cpp"]
 # Per-file code-generation options.  sparse_mla: MFMA results in VGPRs where they fit (its
 # output accumulators then stay put; with the default AGPR form the register allocator
 # shuttled one output tile between AGPRs and VGPRs around every S^T chain).
-EXTRA_FLAGS = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# indexer_prefill: same reason -- its VALU epilogue reads every accumulator, which from AGPRs
+# would cost one extra move per value.
+EXTRA_FLAGS = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "indexer_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 

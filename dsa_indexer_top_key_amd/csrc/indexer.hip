@@ -17,10 +17,9 @@
 //    LDS rings by direct global->LDS copies of whole 1 KB spans (non-temporal), feed the B
 //    operand of v_mfma_f32_16x16x32_bf16 from there, and the scores leave in one burst per
 //    block.
-//  * prefill -- many queries of one request.  A block owns 16 consecutive queries and walks
-//    their causal key range in 32-key tiles staged through LDS (double-buffered); every key
-//    tile feeds 16 queries x 32 heads of v_mfma_f32_32x32x16_bf16, so the kernel is bound by
-//    MFMA throughput rather than HBM.
+//  * prefill -- many queries of one request (indexer_prefill.hip): every key tile feeds
+//    16 queries x 32 heads of v_mfma_f32_32x32x16_bf16, so that kernel is bound by MFMA
+//    throughput rather than HBM.
 #include "common.h"
 
 namespace dsa {
@@ -157,127 +156,10 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------------------
-// prefill
-// ---------------------------------------------------------------------------------------
-constexpr int kPrefillQ = 16;        // queries per block (2 per wave, 8 waves)
-constexpr int kPrefillTile = 32;     // keys per LDS tile
-constexpr int kKeyStride = kIndexDim + 8;  // padded LDS row (bf16 elements): 272 bytes
-
-// MFMA 32x32x16: A = q (rows: the 32 heads of one query), B = key tile (cols: 32 keys).
-// Lane l (h = l/32) supplies head/key l%32 and dims [64h + 8s, 64h + 8s + 8) at step s.
-// The accumulator gives lane l the key l%32 and the heads 8(r/4) + 4h + r%4, r = 0..15.
-__global__ __launch_bounds__(512) void indexer_prefill_kernel(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ keys, const int64_t* __restrict__ kv_off,
-    const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos, int32_t T,
-    int64_t max_s, float* __restrict__ scores, int64_t ld) {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[2][kPrefillTile * kKeyStride];
-    __shared__ int64_t s_n[kPrefillQ];
-    __shared__ int32_t s_req[kPrefillQ];
-
-    const int t0 = blockIdx.x * kPrefillQ;
-    const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int wave = tid >> 6;
-    const int h = lane >> 5;
-    const int col = lane & 31;
-
-    if (tid < kPrefillQ) {
-        const int t = t0 + tid;
-        if (t < T) {
-            s_req[tid] = q_req[t];
-            s_n[tid] = admissible(kv_off, q_req[t], q_pos[t], max_s);
-        } else {
-            s_req[tid] = -1;
-            s_n[tid] = 0;
-        }
-    }
-    lds_barrier();
-
-    // this wave's two queries
-    const int qi0 = 2 * wave, qi1 = 2 * wave + 1;
-    bf16x8 qa[2][8];
-    float wr[2][16];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int t = t0 + 2 * wave + j;
-        const int tt = t < T ? t : 0;
-        const uint16_t* qt = q_idx + static_cast<int64_t>(tt) * kIndexHeads * kIndexDim;
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            qa[j][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + col * kIndexDim + 64 * h + 8 * s));
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            wr[j][r] = bf16_to_f32(w[tt * kIndexHeads + 8 * (r >> 2) + 4 * h + (r & 3)]);
-    }
-
-    // The queries of a block normally share one request.  If they do not, the block makes
-    // one pass per distinct request, each pass scoring only that request's queries.
-    int done_mask = 0;  // bit i: query i of the block handled (uniform across the block)
-    for (int qi = 0; qi < kPrefillQ; ++qi)
-        if (s_req[qi] < 0 || s_n[qi] == 0) done_mask |= 1 << qi;
-    while (done_mask != (1 << kPrefillQ) - 1) {
-        int req = -1;
-        for (int qi = 0; qi < kPrefillQ; ++qi)
-            if (!(done_mask & (1 << qi))) { req = s_req[qi]; break; }
-        int64_t n_max = 0;
-        int pass_mask = 0;
-        for (int qi = 0; qi < kPrefillQ; ++qi)
-            if (!(done_mask & (1 << qi)) && s_req[qi] == req) {
-                pass_mask |= 1 << qi;
-                n_max = s_n[qi] > n_max ? s_n[qi] : n_max;
-            }
-        const bool act0 = pass_mask & (1 << qi0), act1 = pass_mask & (1 << qi1);
-        const int64_t n0 = act0 ? s_n[qi0] : 0, n1 = act1 ? s_n[qi1] : 0;
-        const uint16_t* kb = keys + kv_off[req] * kIndexDim;
-        const int n_tiles = static_cast<int>((n_max + kPrefillTile - 1) / kPrefillTile);
-
-        // each thread moves one 16-byte chunk of a 32-key tile (32 keys x 16 chunks = 512)
-        const int lrow = tid >> 4, lchunk = tid & 15;
-        auto load_chunk = [&](int tile) -> u32x4 {
-            int64_t key = static_cast<int64_t>(tile) * kPrefillTile + lrow;
-            key = key < n_max ? key : n_max - 1;
-            return *reinterpret_cast<const u32x4*>(kb + key * kIndexDim + 8 * lchunk);
-        };
-        u32x4 pre = load_chunk(0);
-        *reinterpret_cast<u32x4*>(&ks[0][lrow * kKeyStride + 8 * lchunk]) = pre;
-        if (n_tiles > 1) pre = load_chunk(1);
-        lds_barrier();
-
-        for (int tile = 0; tile < n_tiles; ++tile) {
-            const uint16_t* kt = ks[tile & 1];
-            const int64_t key0 = static_cast<int64_t>(tile) * kPrefillTile;
-            f32x16 acc0 = {}, acc1 = {};
-            if (key0 < n0 || key0 < n1) {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + col * kKeyStride + 64 * h + 8 * s));
-                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kf, acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kf, acc1, 0, 0, 0);
-                }
-            }
-            // stage the next tile into the other buffer while the epilogue runs
-            if (tile + 1 < n_tiles) {
-                *reinterpret_cast<u32x4*>(&ks[(tile + 1) & 1][lrow * kKeyStride + 8 * lchunk]) = pre;
-                if (tile + 2 < n_tiles) pre = load_chunk(tile + 2);
-            }
-            float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                v0 += wr[0][r] * fmaxf(acc0[r], 0.f);
-                v1 += wr[1][r] * fmaxf(acc1[r], 0.f);
-            }
-            v0 += __shfl_xor(v0, 32);
-            v1 += __shfl_xor(v1, 32);
-            const int64_t key = key0 + col;
-            if (h == 0 && key < n0) scores[static_cast<int64_t>(t0 + qi0) * ld + key] = v0;
-            if (h == 1 && key < n1) scores[static_cast<int64_t>(t0 + qi1) * ld + key] = v1;
-            lds_barrier();
-        }
-        done_mask |= pass_mask;
-    }
-}
+hipError_t launch_indexer_prefill(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
+                                  const int64_t* kv_off, const int32_t* q_req,
+                                  const int32_t* q_pos, int32_t T, int64_t max_s, float* scores,
+                                  int64_t ld, hipStream_t stream);
 
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
                                  const int64_t* kv_off, const int32_t* q_req,
@@ -286,9 +168,8 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const
     // Prefill kernel when queries come in runs of one request (on average >= 8 per
     // request); per-query streaming otherwise.  Both are exact for any layout.
     if (static_cast<int64_t>(T) >= 8 * static_cast<int64_t>(B)) {
-        const int blocks = (T + kPrefillQ - 1) / kPrefillQ;
-        hipLaunchKernelGGL(indexer_prefill_kernel, dim3(blocks), dim3(512), 0, stream, q_idx, w,
-                           keys, kv_off, q_req, q_pos, T, max_s, scores, ld);
+        return launch_indexer_prefill(q_idx, w, keys, kv_off, q_req, q_pos, T, max_s, scores,
+                                      ld, stream);
     } else {
         const int64_t chunk = decode_chunk(T, max_s);
         const int64_t cpq = (max_s + chunk - 1) / chunk;
