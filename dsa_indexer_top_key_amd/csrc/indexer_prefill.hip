@@ -11,21 +11,30 @@
 // N and the 128 dims as K (8 steps).  The ReLU, the head weights and the head sum are a VALU
 // epilogue of 2 instructions per (head, key) -- half the VALU issue rate at full MFMA rate,
 // so it must overlap the MFMAs rather than follow them.  Each wave therefore runs a
-// two-stage pipeline over half tiles of 32 keys: while the MFMAs of one half tile execute,
-// the epilogue of the previous half tile (other accumulator set) issues in between.
+// two-stage pipeline over sub-tiles of 32 keys: while the MFMAs of one sub-tile execute,
+// the epilogue of the previous sub-tile (other accumulator set) issues in between.
 //
 // Keys reach LDS by direct global->LDS copies (no register staging) into a four-slot ring of
-// 64-key tiles, three tiles ahead of the MFMAs; one barrier per tile.
+// 128-key tiles, three tiles ahead of the MFMAs; one barrier per tile.  Within a tile the key
+// operands roll: the register holding step s of one sub-tile is refilled with step s of the
+// next sub-tile as soon as both MFMAs of step s have issued.
+//
+// Measured on the 4096-query chunk at 61440..65535 (2.13 TFLOP of causal scoring): the
+// sustained clock under this load is about 1.7 GHz, at which the matrix cores are busy about
+// 62% of cycles.  Without the epilogue the loop reached 1.68 ms, without the score stores
+// 1.86 ms, against 2.01 ms for the whole kernel; 64-key tiles, an eight-slot ring and
+// non-temporal score stores were all within 1% of this shape, and one wave per SIMD with four
+// queries each (512 registers) was 20% slower.
 #include "common.h"
 
 namespace dsa {
 
 namespace {
 
-constexpr int kPQ = 16;          // queries per block: 2 per wave, 8 waves
-constexpr int kPTile = 64;       // keys per LDS tile (16 KB)
+constexpr int kPQ = 16;          // queries per block
+constexpr int kQPW = 2;          // queries per wave: 8 waves, 2 per SIMD
+constexpr int kPTile = 128;      // keys per LDS tile (32 KB)
 constexpr int kPRing = 4;        // ring slots: tiles i..i+3 (i+3 being copied)
-constexpr int kPCopies = kPTile / 4 / 8;  // 1 KB copies (4 keys each) per wave per tile: 2
 
 __device__ __forceinline__ int64_t admissible_n(const int64_t* kv_off, int b, int32_t pos,
                                                 int64_t max_s) {
@@ -38,8 +47,8 @@ __device__ __forceinline__ int64_t admissible_n(const int64_t* kv_off, int b, in
 
 }  // namespace
 
-// grid: one block per 16 consecutive queries; 512 threads (8 waves, 2 per SIMD), each wave
-// owning two queries (query 2w + j of the block, j = 0, 1).
+// grid: one block per 16 consecutive queries; 512 threads (8 waves), wave w owning queries
+// 2w and 2w + 1 of the block.
 // LDS tile layout: key r of the tile occupies 256 bytes; its 16-byte piece p (dims 8p..8p+7)
 // sits at position p ^ (r % 16).  Copy d (0..15) of a tile moves keys 4d..4d+3: lane 16g + c
 // loads piece c ^ (r % 16) of key r = 4d + g to position c, so one copy fills 1 KB of LDS
@@ -48,11 +57,15 @@ __device__ __forceinline__ int64_t admissible_n(const int64_t* kv_off, int b, in
 // MFMA 32x32x16: lane l (hh = l / 32) supplies head / key l % 32 and dims [64 hh + 8 s, +8)
 // at step s; the accumulator gives lane l the key l % 32 and the heads
 // 8 (r / 4) + 4 hh + r % 4, r = 0..15.
-__global__ __launch_bounds__(512) void indexer_prefill_kernel(
+__global__ __launch_bounds__(64 * (kPQ / kQPW)) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ keys, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos, int32_t T,
     int64_t max_s, float* __restrict__ scores, int64_t ld) {
+    constexpr int QPW = kQPW;
+    constexpr int kWaves = kPQ / QPW;
+    constexpr int kCopies = kPTile / 4 / kWaves;  // 1 KB copies (4 keys each) per wave per tile
+    constexpr int kPairs = QPW / 2;
     __shared__ __attribute__((aligned(1024))) uint16_t ring[kPRing][kPTile * kIndexDim];
     __shared__ int64_t s_n[kPQ];
     __shared__ int32_t s_req[kPQ];
@@ -78,12 +91,12 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
     }
     lds_barrier();
 
-    // the wave's two queries: A operands (8 K-steps each) and head weights in accumulator order
-    bf16x8 qa[2][8];
-    float wr[2][16];
+    // the wave's queries: A operands (8 K-steps each) and head weights in accumulator order
+    bf16x8 qa[QPW][8];
+    float wr[QPW][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int t = t0 + 2 * wave + j;
+    for (int j = 0; j < QPW; ++j) {
+        const int t = t0 + QPW * wave + j;
         const int tt = t < T ? t : 0;
         const uint16_t* qt = q_idx + static_cast<int64_t>(tt) * kIndexHeads * kIndexDim;
 #pragma unroll
@@ -93,9 +106,15 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
         for (int r = 0; r < 16; ++r)
             wr[j][r] = bf16_to_f32(w[tt * kIndexHeads + 8 * (r >> 2) + 4 * hh + (r & 3)]);
     }
-    // After the epilogue's half swap, lanes 0..31 hold query 2w and lanes 32..63 query 2w+1.
-    const int my_q = 2 * wave + hh;
-    float* my_row = scores + static_cast<int64_t>(t0 + my_q) * ld;
+    // After the epilogue's half swap of pair p, lanes 0..31 hold query QPW w + 2p and lanes
+    // 32..63 query QPW w + 2p + 1.
+    int my_q[kPairs];
+    float* my_row[kPairs];
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) {
+        my_q[p] = QPW * wave + 2 * p + hh;
+        my_row[p] = scores + static_cast<int64_t>(t0 + my_q[p]) * ld;
+    }
 
     // The queries of a block normally share one request.  If they do not, the block makes
     // one pass per distinct request, each pass scoring only that request's queries.
@@ -113,19 +132,21 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
                 pass_mask |= 1 << qi;
                 n_max = s_n[qi] > n_max ? s_n[qi] : n_max;
             }
-        // this lane's store limit: its query's count if the query is in this pass, else 0
-        const int64_t my_n = (pass_mask >> my_q) & 1 ? s_n[my_q] : 0;
+        // this lane's store limits: its queries' counts if they are in this pass, else 0
+        int64_t my_n[kPairs];
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) my_n[p] = (pass_mask >> my_q[p]) & 1 ? s_n[my_q[p]] : 0;
         const uint16_t* kb = keys + kv_off[req] * kIndexDim;
         const int n_tiles = static_cast<int>((n_max + kPTile - 1) / kPTile);
 
-        // This wave's two copies of `tile` into its ring slot.  Keys past n_max (the tail of
-        // the last tile, and the tiles past the end that keep the copy count uniform) copy an
+        // This wave's copies of `tile` into its ring slot.  Keys past n_max (the tail of the
+        // last tile, and the tiles past the end that keep the copy count uniform) copy an
         // in-bounds key of the request instead; their scores are never stored.
         auto issue = [&](int tile) {
-            const uint16_t* slot = ring[tile & (kPRing - 1)];
+            const uint16_t* slot = ring[tile % kPRing];
 #pragma unroll
-            for (int d = 0; d < kPCopies; ++d) {
-                const int cp = kPCopies * wave + d;
+            for (int d = 0; d < kCopies; ++d) {
+                const int cp = kCopies * wave + d;
                 const int r = 4 * cp + g;
                 int64_t key = static_cast<int64_t>(tile) * kPTile + r;
                 key = key < n_max ? key : n_max - 1;
@@ -134,60 +155,66 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(
             }
         };
 
-        // MFMAs of half tile `half` (keys 32 half .. +31) of the tile in `kt`
-        auto mfma_half = [&](const uint16_t* kt, int half, f32x16 (&acc)[2]) {
-            const uint16_t* krow = kt + (32 * half + col) * kIndexDim;
+        // epilogue of a sub-tile whose first key is key0 (negative: nothing to store)
+        auto epilogue = [&](const f32x16 (&acc)[QPW], int64_t key0) {
+            const int64_t key = key0 + col;
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) {
+                float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    v0 = __builtin_fmaf(wr[2 * p][r], fmaxf(acc[2 * p][r], 0.f), v0);
+                    v1 = __builtin_fmaf(wr[2 * p + 1][r], fmaxf(acc[2 * p + 1][r], 0.f), v1);
+                }
+                // v_permlane32_swap: the upper half of v0 trades places with the lower half
+                // of v1, so lane l < 32 gets v0 of lane l + 32 and lane l + 32 gets v1 of lane
+                // l; the sum is query 2p's score in lanes 0..31 and query 2p+1's in 32..63.
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0),
+                                                                 __float_as_uint(v1), false, false);
+                const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                if (key >= 0 && key < my_n[p]) my_row[p][key] = v;
+            }
+        };
+
+#pragma unroll
+        for (int j = 0; j < kPRing - 1; ++j) issue(j);
+        f32x16 acc_a[QPW], acc_b[QPW];
+#pragma unroll
+        for (int j = 0; j < QPW; ++j) acc_b[j] = f32x16{};
+        for (int i = 0; i < n_tiles; ++i) {
+            // this wave's copies of tile i are done once at most the copies of the kPRing - 2
+            // tiles after it remain outstanding (loads complete in issue order; score stores
+            // in between only make the wait stricter); the barrier then covers every wave's
+            // copies, and every wave is done reading tile i-1, whose slot is refilled below
+            wait_vmcnt<(kPRing - 2) * kCopies>();
+            lds_barrier();
+            const uint16_t* kt = ring[i % kPRing];
+            const int64_t key0 = static_cast<int64_t>(i) * kPTile;
+            // B operands of sub-tile h (keys 32 h .. 32 h + 31 of the tile), step s
+            auto operand = [&](int h, int s) {
+                const uint16_t* krow = kt + (32 * h + col) * kIndexDim;
+                return as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * ((8 * hh + s) ^ (col & 15))));
+            };
             bf16x8 kf[8];
 #pragma unroll
-            for (int s = 0; s < 8; ++s)
-                kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * ((8 * hh + s) ^ (col & 15))));
-            acc[0] = f32x16{};
-            acc[1] = f32x16{};
+            for (int s = 0; s < 8; ++s) kf[s] = operand(0, s);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], kf[s], acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], kf[s], acc[1], 0, 0, 0);
-            }
-        };
-
-        // epilogue of a half tile whose first key is key0 (negative: nothing to store)
-        auto epilogue = [&](const f32x16 (&acc)[2], int64_t key0) {
-            float v0 = 0.f, v1 = 0.f;
+            for (int h = 0; h < kPTile / 32; ++h) {
+                // even sub-tiles accumulate into acc_a, odd ones into acc_b; the epilogue of
+                // the previous sub-tile (the other set) issues between these MFMAs
+                f32x16 (&acc)[QPW] = (h & 1) ? acc_b : acc_a;
+                f32x16 (&prev)[QPW] = (h & 1) ? acc_a : acc_b;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                v0 = __builtin_fmaf(wr[0][r], fmaxf(acc[0][r], 0.f), v0);
-                v1 = __builtin_fmaf(wr[1][r], fmaxf(acc[1][r], 0.f), v1);
+                for (int j = 0; j < QPW; ++j) acc[j] = f32x16{};
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+#pragma unroll
+                    for (int j = 0; j < QPW; ++j)
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j][s], kf[s], acc[j], 0, 0, 0);
+                    if (h + 1 < kPTile / 32) kf[s] = operand(h + 1, s);
+                }
+                epilogue(prev, key0 + 32 * h - 32);   // none before key 0
             }
-            // v_permlane32_swap: the upper half of v0 trades places with the lower half of v1,
-            // so lane l < 32 gets v0 of lane l + 32 and lane l + 32 gets v1 of lane l; the sum
-            // is query 2w's score in lanes 0..31 and query 2w+1's in lanes 32..63.
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0),
-                                                             __float_as_uint(v1), false, false);
-            const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            const int64_t key = key0 + col;
-            if (key >= 0 && key < my_n) my_row[key] = v;
-        };
-
-        issue(0);
-        issue(1);
-        issue(2);
-        f32x16 acc_a[2], acc_b[2];
-        acc_b[0] = f32x16{};
-        acc_b[1] = f32x16{};
-        for (int i = 0; i < n_tiles; ++i) {
-            // this wave's copies of tile i are done once at most the 2 x kPCopies copies of
-            // tiles i+1 and i+2 remain outstanding (loads complete in issue order; score
-            // stores in between only make the wait stricter); the barrier then covers every
-            // wave's copies, and every wave is done reading tile i-1, whose slot is refilled
-            // below
-            wait_vmcnt<2 * kPCopies>();
-            lds_barrier();
-            const uint16_t* kt = ring[i & (kPRing - 1)];
-            const int64_t key0 = static_cast<int64_t>(i) * kPTile;
-            mfma_half(kt, 0, acc_a);
-            epilogue(acc_b, key0 - 32);   // second half of tile i-1 (none before tile 0)
-            mfma_half(kt, 1, acc_b);
-            epilogue(acc_a, key0);        // first half of tile i
             issue(i + kPRing - 1);
         }
         epilogue(acc_b, static_cast<int64_t>(n_tiles) * kPTile - 32);
@@ -204,8 +231,8 @@ hipError_t launch_indexer_prefill(const uint16_t* q_idx, const uint16_t* w, cons
                                   const int32_t* q_pos, int32_t T, int64_t max_s, float* scores,
                                   int64_t ld, hipStream_t stream) {
     const int blocks = (T + kPQ - 1) / kPQ;
-    hipLaunchKernelGGL(indexer_prefill_kernel, dim3(blocks), dim3(512), 0, stream, q_idx, w, keys,
-                       kv_off, q_req, q_pos, T, max_s, scores, ld);
+    hipLaunchKernelGGL(indexer_prefill_kernel, dim3(blocks), dim3(64 * (kPQ / kQPW)), 0, stream,
+                       q_idx, w, keys, kv_off, q_req, q_pos, T, max_s, scores, ld);
     return hipGetLastError();
 }
 
