@@ -77,9 +77,10 @@ def f64_to_bf16(x) -> np.ndarray:
 # (no rotation of the keys).  Reading: biased variance, affine gamma/beta in fp32, an eps
 # passed by the caller, result stored as bf16 (round to nearest even).
 # ----------------------------------------------------------------------------------------
-def layernorm_keys(raw, gamma, beta, eps) -> np.ndarray:
-    """Exact-as-fp64 LayerNorm of each 128-wide row; returns float64 [N,128]."""
-    x = np.asarray(raw, dtype=np.float32).astype(np.float64)
+def layernorm64(x, gamma, beta, eps) -> np.ndarray:
+    """LayerNorm of each 128-wide row of float64 x, evaluated in fp64 (gamma, beta and eps are
+    taken at their fp32 values)."""
+    x = np.asarray(x, dtype=np.float64)
     g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
     b = np.asarray(beta, dtype=np.float32).astype(np.float64)
     eps = float(np.float32(eps))
@@ -88,10 +89,17 @@ def layernorm_keys(raw, gamma, beta, eps) -> np.ndarray:
     return (x - mu) / np.sqrt(var + eps) * g + b
 
 
+def layernorm_keys(raw, gamma, beta, eps) -> np.ndarray:
+    """Exact-as-fp64 LayerNorm of each 128-wide row of fp32 raw keys; returns float64 [N,128]."""
+    return layernorm64(np.asarray(raw, dtype=np.float32).astype(np.float64), gamma, beta, eps)
+
+
 def layernorm_term_magnitude(raw, gamma, beta, eps) -> np.ndarray:
     """|normalised x * gamma| + |beta| per element: the size of the two terms whose sum is the
-    output, which bounds the absolute rounding error of any fp32 evaluation of it."""
-    x = np.asarray(raw, dtype=np.float32).astype(np.float64)
+    output, which bounds the absolute rounding error of any fp32 evaluation of it.  fp32 raw
+    keys are used as given; float64 rows (an exact projection) are used unrounded."""
+    x = np.asarray(raw)
+    x = x.astype(np.float64) if x.dtype == np.float64 else x.astype(np.float32).astype(np.float64)
     g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
     b = np.asarray(beta, dtype=np.float32).astype(np.float64)
     eps = float(np.float32(eps))
@@ -329,6 +337,46 @@ def value_gate_magnitude(o, w_uv, gate) -> np.ndarray:
     o = np.asarray(o)
     o64 = bf16_to_f64(o) if o.dtype == np.uint16 else o.astype(np.float64)
     return np.einsum("hck,thk->thc", np.abs(bf16_to_f64(w_uv)), np.abs(o64)) * sigmoid(bf16_to_f64(gate))
+
+
+# ----------------------------------------------------------------------------------------
+# Indexer-side projections (the steps before the key LayerNorm and the scoring).
+# Section "Eine Query durch den Indexer verfolgen": the indexer projects the query latent to
+# [T,32,128]; another projection maps residual states to [S,128] keys, followed by the key
+# LayerNorm; a further one makes 32 head weights from each query's residual state.  Section
+# "Was ändert sich – und was nicht?": query latent rank 1536, residual width 7168.  The
+# adapter paragraph: FP32 key normalisation, BF16 head-gate path.
+# Reading (the page gives no formula): plain linear maps, weights stored [out, in]; no bias,
+# scale or activation; q_idx and w are rounded to bf16 once, the key is normalised from the
+# exact projection and then rounded (as layernorm_keys_bf16 does for a given raw key).
+# ----------------------------------------------------------------------------------------
+def linear(x, weight) -> np.ndarray:
+    """x [T, K] (bf16 bits or float) times weight [N, K] (bf16 bits) transposed -> [T, N] fp64."""
+    x = np.asarray(x)
+    x64 = bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    return x64 @ bf16_to_f64(weight).T
+
+
+def linear_magnitude(x, weight) -> np.ndarray:
+    """sum_k |x_tk w_nk|: the scale of the rounding error of any finite-precision evaluation."""
+    x = np.asarray(x)
+    x64 = bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    return np.abs(x64) @ np.abs(bf16_to_f64(weight)).T
+
+
+def indexer_projections(c_q, h, w_qi, w_k, w_w, gamma, beta, eps) -> dict:
+    """The indexer's inputs for T new tokens.
+
+    c_q [T,1536] query latent and h [T,7168] residual states (bf16 bits); w_qi [4096,1536],
+    w_k [128,7168], w_w [32,7168] (bf16 bits, [out, in]); gamma, beta [128] fp32.
+    Returns q_idx [T,32,128] and w [T,32] as bf16 bits, the exact raw key k_raw [T,128]
+    (fp64), its LayerNorm key [T,128] (fp64) and that key as bf16 bits (the cache rows)."""
+    t = np.asarray(c_q).shape[0]
+    q = linear(c_q, w_qi).reshape(t, INDEX_HEADS, INDEX_DIM)  # output j = 128 head + dim
+    k_raw = linear(h, w_k)
+    key = layernorm64(k_raw, gamma, beta, eps)
+    return {"q_idx": f64_to_bf16(q), "w": f64_to_bf16(linear(h, w_w)), "k_raw": k_raw,
+            "key": key, "key_bf16": f64_to_bf16(key)}
 
 
 # ----------------------------------------------------------------------------------------

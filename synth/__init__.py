@@ -11,10 +11,15 @@ sharing code with each other.  Every array is seeded separately with
     7 companion keys [N,64]   8 absorbed main queries [T,96,576] bf16
     10 value up-projection W_UV [96,128,512] bf16   11 output-gate logits [T,96,128] bf16
     12 a stand-in read o [T,96,512] bf16 (for the epilogue alone)
+    13 query latent c_q [T,1536] bf16   14 residual states h [T,7168] bf16
+    15 W_qi [4096,1536] bf16   16 W_k [128,7168] bf16   17 W_w [32,7168] bf16 (weights [out, in])
 
 Distributions: index queries, raw keys, latents and main queries N(0,1); head weights
 N(0, 1/32); gamma 1 + N(0, 0.1); beta N(0, 0.1); W_UV N(0, 1/512) (unit gain); gate logits
-N(0, 1); stand-in reads N(0, 0.1) (a read is a convex combination of N(0,1) rows).  The second argument of N is read as
+N(0, 1); stand-in reads N(0, 0.1) (a read is a convex combination of N(0,1) rows); query
+latents and residual states N(0,1); W_qi N(0, 1/1536) and W_k N(0, 1/7168) (unit gain, so
+projected queries are N(0,1) like the given ones); W_w N(0, 1/(32*7168)) (projected head
+weights N(0, 1/32) like the given ones).  The second argument of N is read as
 the variance.  BF16 values are rounded from float32 with round-to-nearest-even.
 
 CPU generation uses numpy's PCG64; large workloads are generated on the GPU with torch's
@@ -37,6 +42,10 @@ ATTN_SCALE = 1.0 / 192.0 ** 0.5
 VALUE_DIM = 128
 WUV_STD = (1.0 / 512.0) ** 0.5
 READ_STD = 0.1 ** 0.5
+Q_LATENT, RESIDUAL = 1536, 7168
+WQI_STD = (1.0 / Q_LATENT) ** 0.5
+WK_STD = (1.0 / RESIDUAL) ** 0.5
+WW_STD = (1.0 / (INDEX_HEADS * RESIDUAL)) ** 0.5
 
 
 def bf16_bits_from_f32(x) -> np.ndarray:
@@ -156,6 +165,14 @@ def inputs_np(lay: Layout, parts=("index", "ln", "mla")) -> dict:
         d["w_uv"] = bf16_bits_from_f32(_normal(s, 10, (MLA_HEADS, VALUE_DIM, LATENT_DIM), std=WUV_STD))
         d["gate"] = bf16_bits_from_f32(_normal(s, 11, (t, MLA_HEADS, VALUE_DIM)))
         d["o"] = bf16_bits_from_f32(_normal(s, 12, (t, MLA_HEADS, LATENT_DIM), std=READ_STD))
+    if "proj" in parts:
+        d["c_q"] = bf16_bits_from_f32(_normal(s, 13, (t, Q_LATENT)))
+        d["h"] = bf16_bits_from_f32(_normal(s, 14, (t, RESIDUAL)))
+        d["w_qi"] = bf16_bits_from_f32(_normal(s, 15, (INDEX_HEADS * INDEX_DIM, Q_LATENT), std=WQI_STD))
+        d["w_k"] = bf16_bits_from_f32(_normal(s, 16, (INDEX_DIM, RESIDUAL), std=WK_STD))
+        d["w_w"] = bf16_bits_from_f32(_normal(s, 17, (INDEX_HEADS, RESIDUAL), std=WW_STD))
+        d["gamma"] = _normal(s, 4, (INDEX_DIM,), std=AFFINE_STD, mean=1.0).astype(np.float32)
+        d["beta"] = _normal(s, 5, (INDEX_DIM,), std=AFFINE_STD).astype(np.float32)
     return d
 
 
@@ -248,6 +265,14 @@ def inputs_torch(lay: Layout, device, parts=("index", "ln", "mla")) -> dict:
         d["w_uv"] = normal(10, (MLA_HEADS, VALUE_DIM, LATENT_DIM), std=WUV_STD)
         d["gate"] = normal(11, (t, MLA_HEADS, VALUE_DIM))
         d["o"] = normal(12, (t, MLA_HEADS, LATENT_DIM), std=READ_STD)
+    if "proj" in parts:
+        d["c_q"] = normal(13, (t, Q_LATENT))
+        d["h"] = normal(14, (t, RESIDUAL))
+        d["w_qi"] = normal(15, (INDEX_HEADS * INDEX_DIM, Q_LATENT), std=WQI_STD)
+        d["w_k"] = normal(16, (INDEX_DIM, RESIDUAL), std=WK_STD)
+        d["w_w"] = normal(17, (INDEX_HEADS, RESIDUAL), std=WW_STD)
+        d["gamma"] = normal(4, (INDEX_DIM,), std=AFFINE_STD, mean=1.0, dtype=torch.float32)
+        d["beta"] = normal(5, (INDEX_DIM,), std=AFFINE_STD, dtype=torch.float32)
     return d
 
 
