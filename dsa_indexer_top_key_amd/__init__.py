@@ -12,6 +12,7 @@ import ctypes
 import os
 
 __all__ = ["DsaError", "library", "index_keys_layernorm", "indexer_scores", "topk", "value_gate",
+           "indexer_project", "indexer_project_workspace_size", "Q_LATENT", "RESIDUAL",
            "indexer_topk", "indexer_topk_workspace_size", "sparse_mla_attn",
            "sparse_mla_workspace_size", "INDEX_HEADS", "INDEX_DIM", "TOPK", "MLA_HEADS",
            "LATENT_DIM", "COMPANION_DIM", "VALUE_DIM"]
@@ -19,6 +20,7 @@ __all__ = ["DsaError", "library", "index_keys_layernorm", "indexer_scores", "top
 INDEX_HEADS, INDEX_DIM, TOPK = 32, 128, 2048
 MLA_HEADS, LATENT_DIM, COMPANION_DIM, VALUE_DIM = 96, 512, 64, 128
 QK_DIM = LATENT_DIM + COMPANION_DIM
+Q_LATENT, RESIDUAL = 1536, 7168
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_amd.so")
 
@@ -55,6 +57,9 @@ _SIGNATURES = {
     "dsa_sparse_mla_attn": ([_p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p,
                              _i32, _p, _p, _sz, _p], ctypes.c_int),
     "dsa_value_gate": ([_p, _p, _p, _i32, _i32, _p, _p], ctypes.c_int),
+    "dsa_indexer_project_workspace_size": ([_i32], _sz),
+    "dsa_indexer_project": ([_p, _p, _p, _p, _p, _p, _p, _f32, _i32, _p, _p, _p, _p, _p, _sz, _p],
+                            ctypes.c_int),
 }
 
 
@@ -253,3 +258,43 @@ def value_gate(o, w_uv, gate, out=None, stream=None):
     _check("dsa_value_gate", library().dsa_value_gate(
         _ptr(o), _ptr(w_uv), _ptr(gate), t, h, _ptr(_contig(out, "out")), _stream(stream)))
     return out
+
+
+def indexer_project_workspace_size(t: int) -> int:
+    return int(library().dsa_indexer_project_workspace_size(t))
+
+
+def indexer_project(c_q, h, w_qi, w_k, w_w, gamma, beta, eps: float, keys, key_rows, q_idx=None,
+                    w=None, workspace=None, stream=None):
+    """Indexer-side projections of T new tokens: c_q [T,1536] and h [T,7168] bf16, weights
+    w_qi [4096,1536], w_k [128,7168], w_w [32,7168] bf16 ([out, in]), gamma/beta [128] fp32.
+    Returns (q_idx [T,32,128], w [T,32]) bf16 and writes LayerNorm(w_k h[t]) as bf16 into row
+    key_rows[t] (int64, absolute) of the index-key cache `keys` [rows,128]."""
+    torch = _torch()
+    for x, n in ((c_q, "c_q"), (h, "h"), (w_qi, "w_qi"), (w_k, "w_k"), (w_w, "w_w"),
+                 (keys, "keys")):
+        _contig(_bits16(_dev(x, n), n), n)
+    for x, n in ((gamma, "gamma"), (beta, "beta"), (key_rows, "key_rows")):
+        _contig(_dev(x, n), n)
+    t = c_q.shape[0]
+    if tuple(c_q.shape) != (t, Q_LATENT) or tuple(h.shape) != (t, RESIDUAL) \
+            or tuple(w_qi.shape) != (INDEX_HEADS * INDEX_DIM, Q_LATENT) \
+            or tuple(w_k.shape) != (INDEX_DIM, RESIDUAL) or tuple(w_w.shape) != (INDEX_HEADS, RESIDUAL) \
+            or keys.dim() != 2 or keys.shape[1] != INDEX_DIM or tuple(key_rows.shape) != (t,):
+        raise ValueError("indexer_project expects c_q [T,1536], h [T,7168], w_qi [4096,1536], "
+                         "w_k [128,7168], w_w [32,7168], keys [rows,128], key_rows [T]")
+    if key_rows.dtype != torch.int64 or gamma.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("key_rows must be int64, gamma and beta float32")
+    if q_idx is None:
+        q_idx = torch.empty((t, INDEX_HEADS, INDEX_DIM), dtype=torch.bfloat16, device=c_q.device)
+    if w is None:
+        w = torch.empty((t, INDEX_HEADS), dtype=torch.bfloat16, device=c_q.device)
+    need = indexer_project_workspace_size(t)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=c_q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_indexer_project", library().dsa_indexer_project(
+        _ptr(c_q), _ptr(h), _ptr(w_qi), _ptr(w_k), _ptr(w_w), _ptr(gamma), _ptr(beta), float(eps), t,
+        _ptr(_contig(q_idx, "q_idx")), _ptr(_contig(w, "w")), _ptr(keys), _ptr(key_rows),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return q_idx, w

@@ -30,6 +30,12 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
 size_t sparse_mla_workspace_bytes(int32_t T);
 hipError_t launch_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
                              int32_t T, uint16_t* out, hipStream_t stream);
+size_t proj_workspace_bytes(int32_t T);
+hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uint16_t* w_qi,
+                               const uint16_t* w_k, const uint16_t* w_w, const float* gamma,
+                               const float* beta, float eps, int32_t T, uint16_t* q_idx,
+                               uint16_t* w, uint16_t* keys, const int64_t* key_rows,
+                               void* workspace, hipStream_t stream);
 }  // namespace dsa
 
 namespace {
@@ -264,4 +270,34 @@ dsa_status_t dsa_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint1
     DSA_REQUIRE(aligned(o, 16) && aligned(w_uv, 16) && aligned(gate, 2) && aligned(out, 4),
                 DSA_ERR_INVALID_ARG, "%s: o and w_uv must be 16-byte, gate 2-byte, out 4-byte aligned", fn);
     return from_hip(dsa::launch_value_gate(o, w_uv, gate, T, out, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t dsa_indexer_project_workspace_size(int32_t T) {
+    return T > 0 ? round_up(dsa::proj_workspace_bytes(T)) : 0;
+}
+
+dsa_status_t dsa_indexer_project(const uint16_t* c_q, const uint16_t* h, const uint16_t* w_qi,
+                                 const uint16_t* w_k, const uint16_t* w_w, const float* gamma,
+                                 const float* beta, float eps, int32_t T, uint16_t* q_idx,
+                                 uint16_t* w, uint16_t* keys, const int64_t* key_rows,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "dsa_indexer_project";
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    DSA_REQUIRE(std::isfinite(eps) && eps >= 0.f, DSA_ERR_INVALID_ARG,
+                "%s: eps must be finite and >= 0", fn);
+    if (T == 0) return ok();
+    DSA_REQUIRE(c_q && h && w_qi && w_k && w_w && gamma && beta && q_idx && w && keys && key_rows,
+                DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+    DSA_REQUIRE(aligned(c_q, 16) && aligned(h, 16) && aligned(w_qi, 16) && aligned(w_k, 16) &&
+                aligned(w_w, 16) && aligned(q_idx, 16) && aligned(keys, 16),
+                DSA_ERR_INVALID_ARG, "%s: c_q, h, w_qi, w_k, w_w, q_idx and keys must be 16-byte aligned", fn);
+    DSA_REQUIRE(aligned(gamma, 4) && aligned(beta, 4) && aligned(w, 2) && aligned(key_rows, 8),
+                DSA_ERR_INVALID_ARG, "%s: misaligned gamma/beta/w/key_rows", fn);
+    const size_t need = dsa_indexer_project_workspace_size(T);
+    DSA_REQUIRE(workspace && aligned(workspace, kAlign) && workspace_bytes >= need,
+                DSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) needed, got %zu",
+                fn, need, workspace_bytes);
+    return from_hip(dsa::launch_indexer_proj(c_q, h, w_qi, w_k, w_w, gamma, beta, eps, T, q_idx,
+                                             w, keys, key_rows, workspace,
+                                             static_cast<hipStream_t>(stream)), fn);
 }

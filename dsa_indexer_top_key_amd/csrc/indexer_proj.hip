@@ -1,0 +1,215 @@
+// Before stages 1 and 2: the indexer-side projections of T new tokens, fused with the key
+// LayerNorm and the append of the keys to the index-key cache.
+//
+// Page "Kimi K3.1 Pro: Sparse-Zugriffe, keine kleinere Historie", section "Eine Query durch
+// den Indexer verfolgen": the indexer projects the query latent to [T,32,128]; another
+// projection maps residual states to [S,128] keys, followed by LayerNorm; a further one makes
+// 32 head weights from the residual state of each query.  Section "Was ändert sich – und was
+// nicht?": query latent rank 1536, residual width 7168.  The adapter paragraph: FP32 key
+// normalisation, BF16 head-gate path.
+//
+//   q_idx[t] = W_qi c_q[t]            [4096] -> [32,128] bf16   (W_qi [4096,1536])
+//   key[t]   = LN(W_k h[t]) -> bf16, written to cache row key_rows[t]   (W_k [128,7168])
+//   w[t]     = W_w h[t]               [32] bf16                 (W_w [32,7168])
+//
+// Two products X W^T with bf16 operands and fp32 sums on the matrix cores
+// (v_mfma_f32_32x32x16_bf16): the query product (K = 1536, N = 4096) and the residual
+// product (K = 7168, N = 160: the key's 128 columns followed by the 32 head weights).  Each
+// wave owns a 64 x 32 output tile (two accumulators sharing every weight operand) and loads
+// its operands straight from global memory in MFMA layout: at K step s of a 128-wide chunk,
+// lane l supplies row l % 32 and the dims [64 (l / 32) + 8 s, +8) -- the K order inside a
+// chunk is permuted identically for both operands, so each lane reads 128 contiguous bytes per
+// chunk and every row is read as whole 256-byte spans.  The K range is split so that small T
+// (decode: one token per request) still spreads the weight stream over hundreds of waves;
+// each split writes fp32 partial sums, and one epilogue block per token adds the splits in a
+// fixed order (deterministic), rounds q_idx and w to bf16, and normalises the key in fp32
+// (mean, biased variance, rsqrt(var + eps), gamma, beta) before rounding it into the cache.
+//
+// Roofline: decode (T = 64) streams 15 MB of weights once -- HBM-bound; a prefill chunk
+// (T = 4096) is 61 GFLOP of contraction -- bound by the matrix cores.
+#include "common.h"
+
+namespace dsa {
+
+constexpr int kQLatent = 1536;
+constexpr int kResidual = 7168;
+constexpr int kQOut = kIndexHeads * kIndexDim;   // 4096 query outputs
+constexpr int kKWOut = kIndexDim + kIndexHeads;  // 160: key columns, then head-weight columns
+constexpr int kProjChunk = 128;                  // K per chunk: 8 MFMA steps
+constexpr int kProjBM = 64;                      // rows per wave tile (two 32-row MFMA tiles)
+constexpr int kProjBN = 128;                     // columns per block (four waves x 32)
+constexpr int kProjTargetBlocks = 128;           // split K until about this many blocks
+
+struct ProjSplits {
+    int q_splits, q_cps;    // query product: splits, chunks per split
+    int kw_splits, kw_cps;  // residual product
+};
+
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+static void split_k(int blocks_mn, int chunks, int* splits, int* cps) {
+    int s = ceil_div(kProjTargetBlocks, blocks_mn);
+    s = s < 1 ? 1 : (s > chunks ? chunks : s);
+    *cps = ceil_div(chunks, s);
+    *splits = ceil_div(chunks, *cps);
+}
+
+static ProjSplits proj_splits(int32_t T) {
+    ProjSplits p;
+    const int mt = ceil_div(T, kProjBM);
+    split_k(mt * ceil_div(kQOut, kProjBN), kQLatent / kProjChunk, &p.q_splits, &p.q_cps);
+    split_k(mt * ceil_div(kKWOut, kProjBN), kResidual / kProjChunk, &p.kw_splits, &p.kw_cps);
+    return p;
+}
+
+size_t proj_workspace_bytes(int32_t T) {
+    if (T <= 0) return 0;
+    const ProjSplits p = proj_splits(T);
+    const size_t q = static_cast<size_t>(p.q_splits) * T * kQOut * sizeof(float);
+    const size_t kw = static_cast<size_t>(p.kw_splits) * T * kKWOut * sizeof(float);
+    return ((q + 255) & ~static_cast<size_t>(255)) + kw;
+}
+
+// grid (column blocks, row tiles, splits); wave w of block x owns columns
+// [32 (4x + w), +32) -- waves past N return at once (the kernel has no barrier).
+// part[split][m][n] = sum over the split's chunks of sum_k a[m][k] * b(n)[k], where rows
+// n < n_b0 of the weight come from b0 and the others from b1 (row n - n_b0).
+__global__ __launch_bounds__(256) void proj_gemm_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b0,
+    const uint16_t* __restrict__ b1, int n_b0, int M, int N, int K, int cps,
+    float* __restrict__ part) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int n0 = 32 * (4 * static_cast<int>(blockIdx.x) + wave);
+    if (n0 >= N) return;  // wave-uniform
+    const int m0 = kProjBM * static_cast<int>(blockIdx.y);
+    const int split = blockIdx.z;
+    const int col = lane & 31, hh = lane >> 5;
+    const int c_begin = split * cps;
+    int c_end = c_begin + cps;
+    const int chunks = K / kProjChunk;
+    c_end = c_end < chunks ? c_end : chunks;
+
+    // rows past M load row M - 1 (in bounds) and are never stored
+    const int ra0 = m0 + col < M ? m0 + col : M - 1;
+    const int ra1 = m0 + 32 + col < M ? m0 + 32 + col : M - 1;
+    const int nb = n0 + col;
+    const uint16_t* pa0 = a + static_cast<int64_t>(ra0) * K + 64 * hh;
+    const uint16_t* pa1 = a + static_cast<int64_t>(ra1) * K + 64 * hh;
+    const uint16_t* pb = (nb < n_b0 ? b0 + static_cast<int64_t>(nb) * K
+                                    : b1 + static_cast<int64_t>(nb - n_b0) * K) + 64 * hh;
+
+    struct Frag { u32x4 a0[8], a1[8], b[8]; };
+    auto load = [&](int c, Frag& f) {
+        const int64_t k = static_cast<int64_t>(c) * kProjChunk;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            f.a0[s] = *reinterpret_cast<const u32x4*>(pa0 + k + 8 * s);
+            f.a1[s] = *reinterpret_cast<const u32x4*>(pa1 + k + 8 * s);
+            f.b[s] = *reinterpret_cast<const u32x4*>(pb + k + 8 * s);
+        }
+    };
+    f32x16 acc0 = {}, acc1 = {};
+    auto mma = [&](const Frag& f) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a0[s]), as_bf16x8(f.b[s]), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a1[s]), as_bf16x8(f.b[s]), acc1, 0, 0, 0);
+        }
+    };
+    // two operand sets: the loads of chunk c + 1 are in flight during the MFMAs of chunk c
+    Frag x, y;
+    if (c_begin < c_end) load(c_begin, x);
+    for (int c = c_begin; c < c_end; c += 2) {
+        if (c + 1 < c_end) load(c + 1, y);
+        mma(x);
+        if (c + 2 < c_end) load(c + 2, x);
+        if (c + 1 < c_end) mma(y);
+    }
+
+    // accumulator layout: lane l holds column n0 + l % 32, rows 8 (r / 4) + 4 hh + r % 4
+    float* out = part + static_cast<int64_t>(split) * M * N + n0 + col;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (m0 + row < M) out[static_cast<int64_t>(m0 + row) * N] = acc0[r];
+        if (m0 + 32 + row < M) out[static_cast<int64_t>(m0 + 32 + row) * N] = acc1[r];
+    }
+}
+
+// One block (256 threads) per token t: threads 0..255 finish the 4096 query outputs (four
+// groups of four columns each), wave 0 the key (two columns per lane, LayerNorm over the
+// wave) and wave 1 the 32 head weights.  Splits are added in ascending order.
+__global__ __launch_bounds__(256) void proj_epilogue_kernel(
+    const float* __restrict__ pq, int q_splits, const float* __restrict__ pkw, int kw_splits,
+    int32_t T, const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
+    uint16_t* __restrict__ q_idx, uint16_t* __restrict__ w, uint16_t* __restrict__ keys,
+    const int64_t* __restrict__ key_rows) {
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t q_stride = static_cast<int64_t>(T) * kQOut;
+#pragma unroll
+    for (int i = 0; i < kQOut / (4 * 256); ++i) {
+        const int n = 4 * (tid + 256 * i);
+        const float* p = pq + static_cast<int64_t>(t) * kQOut + n;
+        f32x4 v = *reinterpret_cast<const f32x4*>(p);
+        for (int s = 1; s < q_splits; ++s) {
+            const f32x4 u = *reinterpret_cast<const f32x4*>(p + s * q_stride);
+            v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+        }
+        u32x2 o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(q_idx + static_cast<int64_t>(t) * kQOut + n) = o;
+    }
+    const int wave = tid >> 6, lane = lane_id();
+    const int64_t kw_stride = static_cast<int64_t>(T) * kKWOut;
+    const float* pk = pkw + static_cast<int64_t>(t) * kKWOut;
+    if (wave == 0) {
+        float x0 = pk[2 * lane], x1 = pk[2 * lane + 1];
+        for (int s = 1; s < kw_splits; ++s) {
+            x0 += pk[s * kw_stride + 2 * lane];
+            x1 += pk[s * kw_stride + 2 * lane + 1];
+        }
+        constexpr float inv_d = 1.0f / kIndexDim;
+        float sum = x0 + x1;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+        const float mean = sum * inv_d;
+        const float d0 = x0 - mean, d1 = x1 - mean;
+        float sq = d0 * d0 + d1 * d1;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) sq += __shfl_xor(sq, m);
+        const float r = 1.0f / sqrtf(sq * inv_d + eps);
+        const float y0 = d0 * r * gamma[2 * lane] + beta[2 * lane];
+        const float y1 = d1 * r * gamma[2 * lane + 1] + beta[2 * lane + 1];
+        *reinterpret_cast<uint32_t*>(keys + key_rows[t] * kIndexDim + 2 * lane) = pack_bf16x2(y0, y1);
+    } else if (wave == 1 && lane < kIndexHeads) {
+        float v = pk[kIndexDim + lane];
+        for (int s = 1; s < kw_splits; ++s) v += pk[s * kw_stride + kIndexDim + lane];
+        w[static_cast<int64_t>(t) * kIndexHeads + lane] = f32_to_bf16(v);
+    }
+}
+
+hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uint16_t* w_qi,
+                               const uint16_t* w_k, const uint16_t* w_w, const float* gamma,
+                               const float* beta, float eps, int32_t T, uint16_t* q_idx,
+                               uint16_t* w, uint16_t* keys, const int64_t* key_rows,
+                               void* workspace, hipStream_t stream) {
+    const ProjSplits p = proj_splits(T);
+    const size_t q_bytes = static_cast<size_t>(p.q_splits) * T * kQOut * sizeof(float);
+    float* pq = static_cast<float*>(workspace);
+    float* pkw = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          ((q_bytes + 255) & ~static_cast<size_t>(255)));
+    const int mt = ceil_div(T, kProjBM);
+    hipLaunchKernelGGL(proj_gemm_kernel, dim3(ceil_div(kQOut, kProjBN), mt, p.q_splits), dim3(256),
+                       0, stream, c_q, w_qi, w_qi, kQOut, T, kQOut, kQLatent, p.q_cps, pq);
+    hipLaunchKernelGGL(proj_gemm_kernel, dim3(ceil_div(kKWOut, kProjBN), mt, p.kw_splits),
+                       dim3(256), 0, stream, h, w_k, w_w, kIndexDim, T, kKWOut, kResidual,
+                       p.kw_cps, pkw);
+    hipLaunchKernelGGL(proj_epilogue_kernel, dim3(T), dim3(256), 0, stream, pq, p.q_splits, pkw,
+                       p.kw_splits, T, gamma, beta, eps, q_idx, w, keys, key_rows);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -16,6 +16,11 @@
  *   stage 4  restricted-softmax MLA read    section "Die Mathematik der Sparse Attention und
  *                                           ihrer fehlenden Masse" (softmax restricted to I_t,
  *                                           absorbed projections, shared 512+64 latent)
+ *   before 1 indexer-side projections      section "Eine Query durch den Indexer verfolgen"
+ *                                           (query latent -> [T,32,128], residual -> key ->
+ *                                           LayerNorm, residual -> 32 head weights)
+ *   after 4  value up-projection + gate     section "Was ändert sich – und was nicht?" and
+ *                                           the paragraph after the Gated-MLA one
  *
  * Conventions shared by every entry point
  *  - Every array argument is a DEVICE pointer (memory on the GPU the stream belongs to).
@@ -194,6 +199,41 @@ dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int6
  */
 dsa_status_t dsa_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
                             int32_t T, int32_t n_heads, uint16_t* out, void* stream);
+
+/*
+ * Before stages 1 and 2 -- the indexer-side projections of T new tokens, with the key
+ * LayerNorm and the append of the keys to the index-key cache.
+ * Page "Kimi K3.1 Pro: Sparse-Zugriffe, keine kleinere Historie", section "Eine Query durch
+ * den Indexer verfolgen": the query latent is projected to [T,32,128]; another projection maps
+ * residual states to [S,128] keys, followed by LayerNorm; a further one makes 32 head weights
+ * from each query's residual state.  Widths from section "Was ändert sich – und was nicht?"
+ * (query latent 1536, residual 7168).  No bias, scale or activation (the page names none).
+ * c_q       [T,1536] bf16 query latents, 16-byte aligned.
+ * h         [T,7168] bf16 residual states, 16-byte aligned.
+ * w_qi      [4096,1536] bf16, 16-byte aligned; row 128*head + dim makes q_idx[t][head][dim].
+ * w_k       [128,7168] bf16 key projection, 16-byte aligned.
+ * w_w       [32,7168] bf16 head-weight projection, 16-byte aligned.
+ * gamma, beta [128] fp32 LayerNorm affine, 4-byte aligned; eps finite and >= 0.
+ * q_idx     [T,32,128] bf16 out, 16-byte aligned: bf16(sum_i w_qi[j][i] * c_q[t][i]).
+ * w         [T,32] bf16 out, 2-byte aligned: bf16(sum_i w_w[head][i] * h[t][i]).
+ * keys      the index-key cache [rows,128] bf16, 16-byte aligned.  Row key_rows[t] receives
+ *           bf16(LayerNorm(k)) with k = sum_i w_k[:][i] * h[t][i], LayerNorm as in
+ *           dsa_index_keys_layernorm applied to the fp32 k; no other row is written.
+ * key_rows  [T] int64 device array, 8-byte aligned: absolute destination rows of the packed
+ *           cache (for request b at request-local position p: kv_off[b] + p).  The caller
+ *           guarantees they are distinct and inside the cache (device data is not checked).
+ * Sums are fp32 (bf16 products are exact), split over K in a fixed order (deterministic).
+ * workspace >= dsa_indexer_project_workspace_size(T) bytes, 256-byte aligned (fp32 partial
+ *           sums of the split contraction).
+ * Errors: INVALID_ARG for T < 0, a bad eps or null/misaligned pointers when T > 0;
+ * WORKSPACE for a missing, misaligned or short workspace.
+ */
+size_t dsa_indexer_project_workspace_size(int32_t T);
+dsa_status_t dsa_indexer_project(const uint16_t* c_q, const uint16_t* h, const uint16_t* w_qi,
+                                 const uint16_t* w_k, const uint16_t* w_w, const float* gamma,
+                                 const float* beta, float eps, int32_t T, uint16_t* q_idx,
+                                 uint16_t* w, uint16_t* keys, const int64_t* key_rows,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

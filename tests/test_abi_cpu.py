@@ -169,3 +169,37 @@ def test_value_gate_validation():
     assert vg(w=fake(0x10004)) == INVALID   # w_uv must be 16-byte aligned
     assert vg(out=fake(0x10002)) == INVALID  # out must be 4-byte aligned
     assert vg(g=fake(0x10001)) == INVALID   # gate must be 2-byte aligned
+
+
+def test_indexer_project_validation_and_workspace():
+    lib = dsa.library()
+    need = lib.dsa_indexer_project_workspace_size(64)
+    assert need > 0 and need % 256 == 0
+    assert lib.dsa_indexer_project_workspace_size(0) == 0
+    assert lib.dsa_indexer_project_workspace_size(4096) >= 4096 * (4096 + 160) * 4
+
+    def pj(T=64, eps=1e-6, ws=fake(), ws_bytes=need, **kw):
+        a = dict(c_q=fake(), h=fake(), w_qi=fake(), w_k=fake(), w_w=fake(), gamma=fake(),
+                 beta=fake(), q_idx=fake(), w=fake(), keys=fake(), key_rows=fake())
+        a.update(kw)
+        return lib.dsa_indexer_project(a["c_q"], a["h"], a["w_qi"], a["w_k"], a["w_w"],
+                                       a["gamma"], a["beta"], eps, T, a["q_idx"], a["w"],
+                                       a["keys"], a["key_rows"], ws, ws_bytes, P(0))
+
+    zeros = {n: P(0) for n in ("c_q", "h", "w_qi", "w_k", "w_w", "gamma", "beta", "q_idx", "w",
+                               "keys", "key_rows")}
+    assert pj(T=0, ws=P(0), ws_bytes=0, **zeros) == OK  # nothing to do, no pointer touched
+    assert pj(T=-1) == INVALID
+    assert pj(eps=float("nan")) == INVALID
+    assert pj(eps=-1.0) == INVALID
+    for n in zeros:
+        assert pj(**{n: P(0)}) == INVALID, n
+        assert n in last_error() or "null" in last_error()
+    for n in ("c_q", "h", "w_qi", "w_k", "w_w", "q_idx", "keys"):
+        assert pj(**{n: fake(0x10008)}) == INVALID, n  # 16-byte alignment
+    assert pj(key_rows=fake(0x10004)) == INVALID
+    assert pj(gamma=fake(0x10002)) == INVALID
+    assert pj(w=fake(0x10001)) == INVALID
+    assert pj(ws=P(0)) == WORKSPACE
+    assert pj(ws_bytes=need - 1) == WORKSPACE
+    assert pj(ws=fake(0x10010)) == WORKSPACE  # 256-byte alignment
