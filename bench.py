@@ -4,8 +4,12 @@ Headline: decode step = indexer scores + top-2048 (dsa_indexer_topk) followed by
 restricted-softmax absorbed-MLA read (dsa_sparse_mla_attn), on a batch of 64 requests with
 32768 cached positions each (one query per request), inputs resident in HBM.  Also reported:
 the prefill indexer (indexer + top-k) on a 4096-query chunk at positions 61440..65535 of a
-65536-position request, in TFLOP/s of causal scoring work, and the index-key LayerNorm
-cache fill.  All timings use HIP events on the stream the kernels run on.
+65536-position request, in TFLOP/s of causal scoring work, the index-key LayerNorm
+cache fill, and beside the step the two neighbouring steps of the layer: the indexer-side
+projections (query latent / residual -> q_idx, LayerNorm key into its cache row, head
+weights) for the decode batch (GB/s) and the prefill chunk (TFLOP/s), and the post-read value
+up-projection with its sigmoid gate.  All timings use HIP events on the stream the kernels
+run on.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
     python bench.py --profile-kernels   # a few launches of each kernel, for rocprofv3
@@ -54,6 +58,17 @@ def decode_alg(lay):
             "bytes_mla": int(b_mla.sum()),
             "bytes": int((b_idx + b_topk + b_mla).sum()),
             "flops_indexer": int(f_idx.sum()), "flops_mla": int(f_mla.sum())}
+
+
+def proj_alg_bytes(t):
+    """Indexer-side projections of t tokens: the three weights once, the query latents and
+    residual states read, q_idx, w and the cache rows written."""
+    weights = (4096 * 1536 + 128 * 7168 + 32 * 7168) * 2
+    return weights + t * (1536 + 7168) * 2 + t * (4096 + 32 + 128) * 2
+
+
+def proj_flops(t):
+    return 2 * t * (1536 * 4096 + 7168 * (128 + 32))
 
 
 def source_digest(name):
@@ -204,6 +219,20 @@ def main():
     def value_gate():
         dsa.value_gate(out, dg["w_uv"], dg["gate"], out=u_out)
 
+    # indexer-side projections of the batch's new tokens (query latent -> q_idx, residual ->
+    # key -> LayerNorm -> cache row, residual -> head weights); also measured beside the step
+    dp = synth.inputs_torch(lay, dev, parts=("proj",))
+    p_keys = torch.empty_like(keys)
+    p_rows = d["kv_off"][1:] - 1  # each token's own position: the last row of its request
+    p_q = torch.empty_like(d["q_idx"])
+    p_w = torch.empty_like(d["w"])
+    p_ws = torch.empty(dsa.indexer_project_workspace_size(lay.T), dtype=torch.uint8, device=dev)
+
+    def project():
+        dsa.indexer_project(dp["c_q"], dp["h"], dp["w_qi"], dp["w_k"], dp["w_w"], dp["gamma"],
+                            dp["beta"], synth.LN_EPS, p_keys, p_rows, q_idx=p_q, w=p_w,
+                            workspace=p_ws)
+
     if args.profile_kernels:
         for _ in range(10):
             step()
@@ -211,6 +240,7 @@ def main():
             topk_only()
             ln_fill()
             value_gate()
+            project()
         torch.cuda.synchronize()
         n = 256 << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -224,6 +254,11 @@ def main():
             for _ in range(2):
                 dsa.indexer_topk(pd["q_idx"], pd["w"], pkeys, pd["kv_off"], pd["q_req"],
                                  pd["q_pos"], play.max_s)
+            pp = synth.inputs_torch(play, dev, parts=("proj",))
+            for _ in range(2):
+                dsa.indexer_project(pp["c_q"], pp["h"], pp["w_qi"], pp["w_k"], pp["w_w"],
+                                    pp["gamma"], pp["beta"], synth.LN_EPS, pkeys,
+                                    pd["q_pos"].to(torch.int64))
         torch.cuda.synchronize()
         return
 
@@ -235,6 +270,8 @@ def main():
     ms_topk = per_call_events(topk_only, args.steps, stream, torch)
     ms_ln = per_call_events(ln_fill, max(3, args.steps // 4), stream, torch)
     ms_vg = per_call_events(value_gate, args.steps, stream, torch)
+    ms_pj = per_call_events(project, args.steps, stream, torch)
+    pj_bytes = proj_alg_bytes(lay.T)
     vg_bytes = 96 * 128 * 512 * 2 + lay.T * 96 * (512 + 2 * 128) * 2  # W_UV, o, gate, out
     vg_flops = 2 * lay.T * 96 * 128 * 512
     qps = lay.T / (ms_step * 1e-3)
@@ -260,6 +297,9 @@ def main():
         "post_read_value_gate": {"ms": round(ms_vg, 5), "bytes": vg_bytes,
                                  "GBps": round(vg_bytes / (ms_vg * 1e-3) / 1e9, 1),
                                  "tflops": round(vg_flops / (ms_vg * 1e-3) / 1e12, 1)},
+        "indexer_projections": {"ms": round(ms_pj, 5), "bytes": pj_bytes,
+                                "GBps": round(pj_bytes / (ms_pj * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(pj_bytes / (ms_pj * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "sparse_mla_tflops": round(alg["flops_mla"] / (ms_mla * 1e-3) / 1e12, 1),
         "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm",
                      "achieved": round(scores_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -296,6 +336,20 @@ def main():
             "tflops_scores_kernel": round(pflops / (ms_pf_scores * 1e-3) / 1e12, 1),
             "mfma_frac": round(pflops / (ms_pf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
         del pws, pscores
+        # the chunk's indexer-side projections (4096 tokens: 60.9 GFLOP of bf16 products)
+        pp = synth.inputs_torch(play, dev, parts=("proj",))
+        pp_keys = torch.empty_like(pkeys)
+        pp_rows = pd["q_pos"].to(torch.int64)
+
+        def prefill_project():
+            dsa.indexer_project(pp["c_q"], pp["h"], pp["w_qi"], pp["w_k"], pp["w_w"],
+                                pp["gamma"], pp["beta"], synth.LN_EPS, pp_keys, pp_rows)
+
+        ms_ppj = per_call_events(prefill_project, psteps, stream, torch)
+        res["prefill_indexer_projections"] = {
+            "ms": round(ms_ppj, 4),
+            "tflops": round(proj_flops(play.T) / (ms_ppj * 1e-3) / 1e12, 1),
+            "mfma_frac": round(proj_flops(play.T) / (ms_ppj * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
     # ------------------------------------------------------------- oracle on the host
     if not args.no_cpu_baseline:

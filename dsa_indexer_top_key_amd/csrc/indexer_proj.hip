@@ -38,7 +38,10 @@ constexpr int kKWOut = kIndexDim + kIndexHeads;  // 160: key columns, then head-
 constexpr int kProjChunk = 128;                  // K per chunk: 8 MFMA steps
 constexpr int kProjBM = 64;                      // rows per wave tile (two 32-row MFMA tiles)
 constexpr int kProjBN = 128;                     // columns per block (four waves x 32)
-constexpr int kProjTargetBlocks = 128;           // split K until about this many blocks
+constexpr int kProjTargetBlocks = 256;           // split K until about this many blocks
+constexpr int kProjMaxSplits = 16;               // ... with at most this many partial sums
+constexpr int kLdsTile = 128;                    // block tile (rows of A and of the weight)
+constexpr int kLdsChunk = 64;                    // and K chunk of the LDS-tiled kernel (below)
 
 struct ProjSplits {
     int q_splits, q_cps;    // query product: splits, chunks per split
@@ -50,15 +53,25 @@ static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 static void split_k(int blocks_mn, int chunks, int* splits, int* cps) {
     int s = ceil_div(kProjTargetBlocks, blocks_mn);
     s = s < 1 ? 1 : (s > chunks ? chunks : s);
+    s = s < kProjMaxSplits ? s : kProjMaxSplits;
     *cps = ceil_div(chunks, s);
     *splits = ceil_div(chunks, *cps);
 }
 
+// Token counts from which the LDS-tiled kernel runs (below it, the register-direct one).
+constexpr int kProjLdsMinT = 512;
+
 static ProjSplits proj_splits(int32_t T) {
     ProjSplits p;
-    const int mt = ceil_div(T, kProjBM);
-    split_k(mt * ceil_div(kQOut, kProjBN), kQLatent / kProjChunk, &p.q_splits, &p.q_cps);
-    split_k(mt * ceil_div(kKWOut, kProjBN), kResidual / kProjChunk, &p.kw_splits, &p.kw_cps);
+    if (T >= kProjLdsMinT) {
+        const int mt = ceil_div(T, kLdsTile);
+        split_k(mt * ceil_div(kQOut, kLdsTile), kQLatent / kLdsChunk, &p.q_splits, &p.q_cps);
+        split_k(mt * ceil_div(kKWOut, kLdsTile), kResidual / kLdsChunk, &p.kw_splits, &p.kw_cps);
+    } else {
+        const int mt = ceil_div(T, kProjBM);
+        split_k(mt * ceil_div(kQOut, kProjBN), kQLatent / kProjChunk, &p.q_splits, &p.q_cps);
+        split_k(mt * ceil_div(kKWOut, kProjBN), kResidual / kProjChunk, &p.kw_splits, &p.kw_cps);
+    }
     return p;
 }
 
@@ -137,6 +150,112 @@ __global__ __launch_bounds__(256) void proj_gemm_kernel(
     }
 }
 
+// Large M (prefill chunks): the same partial products from a 128 x 128 block tile whose A
+// rows and weight rows stream through LDS, shared by the block's four waves (2 x 2, each a
+// 64 x 64 tile of four accumulators), so every operand byte is read from L2 once per block.
+// K moves in 64-wide chunks (four MFMA steps, 128 bytes per row) through a three-slot ring
+// filled by direct global->LDS copies two chunks ahead; one barrier per chunk.  Row r of a
+// slot occupies 128 bytes; its 16-byte piece p sits at position p ^ ((r / 2) % 8), so the 16
+// rows an operand read touches (same p) fall in 16 distinct 16-byte bank groups.  Copy d of a
+// chunk moves rows 8d..8d+7 (A rows for d < 16, weight rows for d >= 16): lane 8 rr + c loads
+// piece c ^ ((row / 2) % 8) of row 8d + rr into position c.  At step s lane l supplies
+// row l % 32 and the dims [32 (l / 32) + 8 s, +8) of the chunk, for both operands.
+constexpr int kLdsRing = 3;
+constexpr int kLdsSlot = 2 * kLdsTile * kLdsChunk;  // bf16 elements per slot (A then weight)
+constexpr int kLdsCopies = 2 * kLdsTile / 8 / 4;  // 1 KB copies per wave per chunk: 8
+
+__global__ __launch_bounds__(256) void proj_gemm_lds_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b0,
+    const uint16_t* __restrict__ b1, int n_b0, int M, int N, int K, int cps,
+    float* __restrict__ part) {
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[kLdsRing][kLdsSlot];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave >> 1, wc = wave & 1;
+    const int m0 = kLdsTile * static_cast<int>(blockIdx.y);
+    const int n0 = kLdsTile * static_cast<int>(blockIdx.x);
+    const int split = blockIdx.z;
+    const int col = lane & 31, hh = lane >> 5;
+    const int chunks = K / kLdsChunk;
+    const int c_begin = split * cps;
+    int c_end = c_begin + cps;
+    c_end = c_end < chunks ? c_end : chunks;
+    const int n_chunks = c_end - c_begin;
+
+    // this wave's copies: rows 8d + rr of A (d < 16) or of the weight (d >= 16); rows past
+    // M or N read the last row (in bounds), their results are never stored
+    const int rr = lane >> 3, cpos = lane & 7;
+    const uint16_t* src[kLdsCopies];
+    uint32_t dst[kLdsCopies];
+#pragma unroll
+    for (int j = 0; j < kLdsCopies; ++j) {
+        const int d = kLdsCopies * wave + j;
+        const int r = 8 * (d & 15) + rr;
+        const int piece = cpos ^ ((r >> 1) & 7);
+        if (d < 16) {
+            const int m = m0 + r < M ? m0 + r : M - 1;
+            src[j] = a + static_cast<int64_t>(m) * K + 8 * piece;
+        } else {
+            const int n = n0 + r < N ? n0 + r : N - 1;
+            src[j] = (n < n_b0 ? b0 + static_cast<int64_t>(n) * K
+                               : b1 + static_cast<int64_t>(n - n_b0) * K) + 8 * piece;
+        }
+        dst[j] = static_cast<uint32_t>((d >= 16 ? kLdsTile * kLdsChunk : 0) + 8 * (d & 15) * kLdsChunk) * 2;
+    }
+    auto issue = [&](int i) {  // copies of the split's chunk i (clamped: past the end re-copy
+        const int c = c_begin + (i < n_chunks ? i : n_chunks - 1);  // its last chunk)
+        const uint32_t base = lds_offset(ring[i % kLdsRing]);
+#pragma unroll
+        for (int j = 0; j < kLdsCopies; ++j)
+            copy_to_lds(src[j] + static_cast<int64_t>(c) * kLdsChunk, base + dst[j]);
+    };
+
+    f32x16 acc[2][2] = {};
+    issue(0);
+    issue(1);
+    for (int i = 0; i < n_chunks; ++i) {
+        // this wave's copies of chunk i are done once only the copies of chunk i+1 remain
+        // outstanding; the barrier covers every wave's copies and frees slot (i + 2) % 3
+        wait_vmcnt<kLdsCopies>();
+        lds_barrier();
+        issue(i + 2);
+        const uint16_t* sa = ring[i % kLdsRing];
+        const uint16_t* sb = sa + kLdsTile * kLdsChunk;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 fa[2], fb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ra = 64 * wr + 32 * t + col;
+                const int rb = 64 * wc + 32 * t + col;
+                const int p = 4 * hh + s;
+                fa[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + ra * kLdsChunk + 8 * (p ^ ((ra >> 1) & 7))));
+                fb[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(sb + rb * kLdsChunk + 8 * (p ^ ((rb >> 1) & 7))));
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+        }
+    }
+    // no copy may still be writing LDS when the block ends
+    wait_vmcnt<0>();
+
+    float* out = part + static_cast<int64_t>(split) * M * N;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            const int n = n0 + 64 * wc + 32 * y + col;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + 64 * wr + 32 * x + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (m < M && n < N) out[static_cast<int64_t>(m) * N + n] = acc[x][y][r];
+            }
+        }
+}
+
 // One block (256 threads) per token t: threads 0..255 finish the 4096 query outputs (four
 // groups of four columns each), wave 0 the key (two columns per lane, LayerNorm over the
 // wave) and wave 1 the 32 head weights.  Splits are added in ascending order.
@@ -153,6 +272,9 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(
         const int n = 4 * (tid + 256 * i);
         const float* p = pq + static_cast<int64_t>(t) * kQOut + n;
         f32x4 v = *reinterpret_cast<const f32x4*>(p);
+        // unrolled so that the loads of several splits are in flight at once; the sums still
+        // go in ascending split order
+#pragma unroll 4
         for (int s = 1; s < q_splits; ++s) {
             const f32x4 u = *reinterpret_cast<const f32x4*>(p + s * q_stride);
             v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
@@ -167,6 +289,7 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(
     const float* pk = pkw + static_cast<int64_t>(t) * kKWOut;
     if (wave == 0) {
         float x0 = pk[2 * lane], x1 = pk[2 * lane + 1];
+#pragma unroll 4
         for (int s = 1; s < kw_splits; ++s) {
             x0 += pk[s * kw_stride + 2 * lane];
             x1 += pk[s * kw_stride + 2 * lane + 1];
@@ -186,6 +309,7 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(
         *reinterpret_cast<uint32_t*>(keys + key_rows[t] * kIndexDim + 2 * lane) = pack_bf16x2(y0, y1);
     } else if (wave == 1 && lane < kIndexHeads) {
         float v = pk[kIndexDim + lane];
+#pragma unroll 4
         for (int s = 1; s < kw_splits; ++s) v += pk[s * kw_stride + kIndexDim + lane];
         w[static_cast<int64_t>(t) * kIndexHeads + lane] = f32_to_bf16(v);
     }
@@ -201,12 +325,23 @@ hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uin
     float* pq = static_cast<float*>(workspace);
     float* pkw = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           ((q_bytes + 255) & ~static_cast<size_t>(255)));
-    const int mt = ceil_div(T, kProjBM);
-    hipLaunchKernelGGL(proj_gemm_kernel, dim3(ceil_div(kQOut, kProjBN), mt, p.q_splits), dim3(256),
-                       0, stream, c_q, w_qi, w_qi, kQOut, T, kQOut, kQLatent, p.q_cps, pq);
-    hipLaunchKernelGGL(proj_gemm_kernel, dim3(ceil_div(kKWOut, kProjBN), mt, p.kw_splits),
-                       dim3(256), 0, stream, h, w_k, w_w, kIndexDim, T, kKWOut, kResidual,
-                       p.kw_cps, pkw);
+    if (T >= kProjLdsMinT) {
+        const int mt = ceil_div(T, kLdsTile);
+        hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(ceil_div(kQOut, kLdsTile), mt, p.q_splits),
+                           dim3(256), 0, stream, c_q, w_qi, w_qi, kQOut, T, kQOut, kQLatent,
+                           p.q_cps, pq);
+        hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(ceil_div(kKWOut, kLdsTile), mt, p.kw_splits),
+                           dim3(256), 0, stream, h, w_k, w_w, kIndexDim, T, kKWOut, kResidual,
+                           p.kw_cps, pkw);
+    } else {
+        const int mt = ceil_div(T, kProjBM);
+        hipLaunchKernelGGL(proj_gemm_kernel, dim3(ceil_div(kQOut, kProjBN), mt, p.q_splits),
+                           dim3(256), 0, stream, c_q, w_qi, w_qi, kQOut, T, kQOut, kQLatent,
+                           p.q_cps, pq);
+        hipLaunchKernelGGL(proj_gemm_kernel, dim3(ceil_div(kKWOut, kProjBN), mt, p.kw_splits),
+                           dim3(256), 0, stream, h, w_k, w_w, kIndexDim, T, kKWOut, kResidual,
+                           p.kw_cps, pkw);
+    }
     hipLaunchKernelGGL(proj_epilogue_kernel, dim3(T), dim3(256), 0, stream, pq, p.q_splits, pkw,
                        p.kw_splits, T, gamma, beta, eps, q_idx, w, keys, key_rows);
     return hipGetLastError();

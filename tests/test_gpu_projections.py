@@ -95,8 +95,10 @@ def check_linear_out(got_bits, x, weight, k, ref_bits):
     assert np.mean(got_bits.reshape(ref_bits.shape) == ref_bits) > 0.98
 
 
-@pytest.mark.parametrize("t_count", [1, 64, 300])
+@pytest.mark.parametrize("t_count", [1, 64, 300, 512, 700])
 def test_indexer_project_parity(t_count):
+    """Below 512 tokens the register-direct products run, from 512 on the LDS-tiled ones
+    (700: five full 128-row tiles and a ragged one)."""
     print(f"[project] T={t_count}", flush=True)
     lay = synth.decode_layout("pj", 80 + t_count, [10] * t_count)
     d = synth.inputs_np(lay, parts=("proj",))
@@ -112,13 +114,13 @@ def test_indexer_project_parity(t_count):
     check_untouched(cache, key_rows)
 
 
-def test_indexer_project_exact_on_integer_inputs():
+@pytest.mark.parametrize("t", [70, 600])
+def test_indexer_project_exact_on_integer_inputs(t):
     """Small integers: every fp32 sum is exact, so q_idx and w equal the oracle bit for bit;
     the keys are the key LayerNorm of the exact integer projection.  70 tokens: one full and
-    one ragged 64-row tile."""
-    print("[project] exact integers", flush=True)
-    g = np.random.default_rng(90)
-    t = 70
+    one ragged 64-row tile of the register-direct products; 600: the LDS-tiled ones."""
+    print(f"[project] exact integers T={t}", flush=True)
+    g = np.random.default_rng(90 + t)
     bits = synth.bf16_bits_from_f32
     d = {"c_q": bits(g.integers(-3, 4, size=(t, 1536))),
          "h": bits(g.integers(-3, 4, size=(t, 7168))),
