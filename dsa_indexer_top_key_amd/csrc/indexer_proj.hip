@@ -14,16 +14,15 @@
 //
 // Two products X W^T with bf16 operands and fp32 sums on the matrix cores
 // (v_mfma_f32_32x32x16_bf16): the query product (K = 1536, N = 4096) and the residual
-// product (K = 7168, N = 160: the key's 128 columns followed by the 32 head weights).  Each
-// wave owns a 64 x 32 output tile (two accumulators sharing every weight operand) and loads
-// its operands straight from global memory in MFMA layout: at K step s of a 128-wide chunk,
-// lane l supplies row l % 32 and the dims [64 (l / 32) + 8 s, +8) -- the K order inside a
-// chunk is permuted identically for both operands, so each lane reads 128 contiguous bytes per
-// chunk and every row is read as whole 256-byte spans.  The K range is split so that small T
-// (decode: one token per request) still spreads the weight stream over hundreds of waves;
-// each split writes fp32 partial sums, and one epilogue block per token adds the splits in a
-// fixed order (deterministic), rounds q_idx and w to bf16, and normalises the key in fp32
-// (mean, biased variance, rsqrt(var + eps), gamma, beta) before rounding it into the cache.
+// product (K = 7168, N = 160: the key's 128 columns followed by the 32 head weights), both by
+// proj_gemm_lds_kernel (128 x 128 block tiles staged through LDS by whole-line global->LDS
+// copies).  The K range is split so that small T (decode: one token per request) still
+// spreads the weight stream over hundreds of blocks; each split writes fp32 partial sums, and
+// one epilogue block per token adds the splits in a fixed order (deterministic), rounds q_idx
+// and w to bf16, and normalises the key in fp32 (mean, biased variance, rsqrt(var + eps),
+// gamma, beta) before rounding it into the cache.  A register-direct variant (each wave
+// loading its operands in MFMA layout, 64 lanes over 64 cache lines per load) measured 3.8x
+// slower at 4096 tokens (480 vs 126 us per call) and 15% slower at 64 (35 vs 30 us).
 //
 // Roofline: decode (T = 64) streams 15 MB of weights once -- HBM-bound; a prefill chunk
 // (T = 4096) is 61 GFLOP of contraction -- bound by the matrix cores.
@@ -35,13 +34,10 @@ constexpr int kQLatent = 1536;
 constexpr int kResidual = 7168;
 constexpr int kQOut = kIndexHeads * kIndexDim;   // 4096 query outputs
 constexpr int kKWOut = kIndexDim + kIndexHeads;  // 160: key columns, then head-weight columns
-constexpr int kProjChunk = 128;                  // K per chunk: 8 MFMA steps
-constexpr int kProjBM = 64;                      // rows per wave tile (two 32-row MFMA tiles)
-constexpr int kProjBN = 128;                     // columns per block (four waves x 32)
+constexpr int kLdsTile = 128;                    // block tile: rows of A and of the weight
+constexpr int kLdsChunk = 64;                    // K per chunk: 4 MFMA steps
 constexpr int kProjTargetBlocks = 256;           // split K until about this many blocks
-constexpr int kProjMaxSplits = 16;               // ... with at most this many partial sums
-constexpr int kLdsTile = 128;                    // block tile (rows of A and of the weight)
-constexpr int kLdsChunk = 64;                    // and K chunk of the LDS-tiled kernel (below)
+constexpr int kProjMaxSplits = 32;               // ... with at most this many partial sums
 
 struct ProjSplits {
     int q_splits, q_cps;    // query product: splits, chunks per split
@@ -58,20 +54,11 @@ static void split_k(int blocks_mn, int chunks, int* splits, int* cps) {
     *splits = ceil_div(chunks, *cps);
 }
 
-// Token counts from which the LDS-tiled kernel runs (below it, the register-direct one).
-constexpr int kProjLdsMinT = 512;
-
 static ProjSplits proj_splits(int32_t T) {
     ProjSplits p;
-    if (T >= kProjLdsMinT) {
-        const int mt = ceil_div(T, kLdsTile);
-        split_k(mt * ceil_div(kQOut, kLdsTile), kQLatent / kLdsChunk, &p.q_splits, &p.q_cps);
-        split_k(mt * ceil_div(kKWOut, kLdsTile), kResidual / kLdsChunk, &p.kw_splits, &p.kw_cps);
-    } else {
-        const int mt = ceil_div(T, kProjBM);
-        split_k(mt * ceil_div(kQOut, kProjBN), kQLatent / kProjChunk, &p.q_splits, &p.q_cps);
-        split_k(mt * ceil_div(kKWOut, kProjBN), kResidual / kProjChunk, &p.kw_splits, &p.kw_cps);
-    }
+    const int mt = ceil_div(T, kLdsTile);
+    split_k(mt * ceil_div(kQOut, kLdsTile), kQLatent / kLdsChunk, &p.q_splits, &p.q_cps);
+    split_k(mt * ceil_div(kKWOut, kLdsTile), kResidual / kLdsChunk, &p.kw_splits, &p.kw_cps);
     return p;
 }
 
@@ -83,76 +70,11 @@ size_t proj_workspace_bytes(int32_t T) {
     return ((q + 255) & ~static_cast<size_t>(255)) + kw;
 }
 
-// grid (column blocks, row tiles, splits); wave w of block x owns columns
-// [32 (4x + w), +32) -- waves past N return at once (the kernel has no barrier).
-// part[split][m][n] = sum over the split's chunks of sum_k a[m][k] * b(n)[k], where rows
-// n < n_b0 of the weight come from b0 and the others from b1 (row n - n_b0).
-__global__ __launch_bounds__(256) void proj_gemm_kernel(
-    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b0,
-    const uint16_t* __restrict__ b1, int n_b0, int M, int N, int K, int cps,
-    float* __restrict__ part) {
-    const int lane = lane_id();
-    const int wave = threadIdx.x >> 6;
-    const int n0 = 32 * (4 * static_cast<int>(blockIdx.x) + wave);
-    if (n0 >= N) return;  // wave-uniform
-    const int m0 = kProjBM * static_cast<int>(blockIdx.y);
-    const int split = blockIdx.z;
-    const int col = lane & 31, hh = lane >> 5;
-    const int c_begin = split * cps;
-    int c_end = c_begin + cps;
-    const int chunks = K / kProjChunk;
-    c_end = c_end < chunks ? c_end : chunks;
-
-    // rows past M load row M - 1 (in bounds) and are never stored
-    const int ra0 = m0 + col < M ? m0 + col : M - 1;
-    const int ra1 = m0 + 32 + col < M ? m0 + 32 + col : M - 1;
-    const int nb = n0 + col;
-    const uint16_t* pa0 = a + static_cast<int64_t>(ra0) * K + 64 * hh;
-    const uint16_t* pa1 = a + static_cast<int64_t>(ra1) * K + 64 * hh;
-    const uint16_t* pb = (nb < n_b0 ? b0 + static_cast<int64_t>(nb) * K
-                                    : b1 + static_cast<int64_t>(nb - n_b0) * K) + 64 * hh;
-
-    struct Frag { u32x4 a0[8], a1[8], b[8]; };
-    auto load = [&](int c, Frag& f) {
-        const int64_t k = static_cast<int64_t>(c) * kProjChunk;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            f.a0[s] = *reinterpret_cast<const u32x4*>(pa0 + k + 8 * s);
-            f.a1[s] = *reinterpret_cast<const u32x4*>(pa1 + k + 8 * s);
-            f.b[s] = *reinterpret_cast<const u32x4*>(pb + k + 8 * s);
-        }
-    };
-    f32x16 acc0 = {}, acc1 = {};
-    auto mma = [&](const Frag& f) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a0[s]), as_bf16x8(f.b[s]), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a1[s]), as_bf16x8(f.b[s]), acc1, 0, 0, 0);
-        }
-    };
-    // two operand sets: the loads of chunk c + 1 are in flight during the MFMAs of chunk c
-    Frag x, y;
-    if (c_begin < c_end) load(c_begin, x);
-    for (int c = c_begin; c < c_end; c += 2) {
-        if (c + 1 < c_end) load(c + 1, y);
-        mma(x);
-        if (c + 2 < c_end) load(c + 2, x);
-        if (c + 1 < c_end) mma(y);
-    }
-
-    // accumulator layout: lane l holds column n0 + l % 32, rows 8 (r / 4) + 4 hh + r % 4
-    float* out = part + static_cast<int64_t>(split) * M * N + n0 + col;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (m0 + row < M) out[static_cast<int64_t>(m0 + row) * N] = acc0[r];
-        if (m0 + 32 + row < M) out[static_cast<int64_t>(m0 + 32 + row) * N] = acc1[r];
-    }
-}
-
-// Large M (prefill chunks): the same partial products from a 128 x 128 block tile whose A
-// rows and weight rows stream through LDS, shared by the block's four waves (2 x 2, each a
-// 64 x 64 tile of four accumulators), so every operand byte is read from L2 once per block.
+// part[split][m][n] = sum over the split's K chunks of sum_k a[m][k] * b(n)[k], where rows
+// n < n_b0 of the weight come from b0 and the others from b1 (row n - n_b0).  A 128 x 128
+// block tile: its A rows and weight rows stream through LDS, shared by the block's four waves
+// (2 x 2, each a 64 x 64 tile of four accumulators), so every operand byte is read from L2
+// once per block.  grid (column tiles, row tiles, splits).
 // K moves in 64-wide chunks (four MFMA steps, 128 bytes per row) through a three-slot ring
 // filled by direct global->LDS copies two chunks ahead; one barrier per chunk.  Row r of a
 // slot occupies 128 bytes; its 16-byte piece p sits at position p ^ ((r / 2) % 8), so the 16
@@ -325,23 +247,13 @@ hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uin
     float* pq = static_cast<float*>(workspace);
     float* pkw = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           ((q_bytes + 255) & ~static_cast<size_t>(255)));
-    if (T >= kProjLdsMinT) {
-        const int mt = ceil_div(T, kLdsTile);
-        hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(ceil_div(kQOut, kLdsTile), mt, p.q_splits),
-                           dim3(256), 0, stream, c_q, w_qi, w_qi, kQOut, T, kQOut, kQLatent,
-                           p.q_cps, pq);
-        hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(ceil_div(kKWOut, kLdsTile), mt, p.kw_splits),
-                           dim3(256), 0, stream, h, w_k, w_w, kIndexDim, T, kKWOut, kResidual,
-                           p.kw_cps, pkw);
-    } else {
-        const int mt = ceil_div(T, kProjBM);
-        hipLaunchKernelGGL(proj_gemm_kernel, dim3(ceil_div(kQOut, kProjBN), mt, p.q_splits),
-                           dim3(256), 0, stream, c_q, w_qi, w_qi, kQOut, T, kQOut, kQLatent,
-                           p.q_cps, pq);
-        hipLaunchKernelGGL(proj_gemm_kernel, dim3(ceil_div(kKWOut, kProjBN), mt, p.kw_splits),
-                           dim3(256), 0, stream, h, w_k, w_w, kIndexDim, T, kKWOut, kResidual,
-                           p.kw_cps, pkw);
-    }
+    const int mt = ceil_div(T, kLdsTile);
+    hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(ceil_div(kQOut, kLdsTile), mt, p.q_splits),
+                       dim3(256), 0, stream, c_q, w_qi, w_qi, kQOut, T, kQOut, kQLatent, p.q_cps,
+                       pq);
+    hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(ceil_div(kKWOut, kLdsTile), mt, p.kw_splits),
+                       dim3(256), 0, stream, h, w_k, w_w, kIndexDim, T, kKWOut, kResidual,
+                       p.kw_cps, pkw);
     hipLaunchKernelGGL(proj_epilogue_kernel, dim3(T), dim3(256), 0, stream, pq, p.q_splits, pkw,
                        p.kw_splits, T, gamma, beta, eps, q_idx, w, keys, key_rows);
     return hipGetLastError();

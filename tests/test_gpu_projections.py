@@ -97,8 +97,8 @@ def check_linear_out(got_bits, x, weight, k, ref_bits):
 
 @pytest.mark.parametrize("t_count", [1, 64, 300, 512, 700])
 def test_indexer_project_parity(t_count):
-    """Below 512 tokens the register-direct products run, from 512 on the LDS-tiled ones
-    (700: five full 128-row tiles and a ragged one)."""
+    """1 to 700 tokens: one partial 128-row tile up to five full tiles and a ragged one, with
+    split counts from 32 down to a few."""
     print(f"[project] T={t_count}", flush=True)
     lay = synth.decode_layout("pj", 80 + t_count, [10] * t_count)
     d = synth.inputs_np(lay, parts=("proj",))
@@ -117,8 +117,8 @@ def test_indexer_project_parity(t_count):
 @pytest.mark.parametrize("t", [70, 600])
 def test_indexer_project_exact_on_integer_inputs(t):
     """Small integers: every fp32 sum is exact, so q_idx and w equal the oracle bit for bit;
-    the keys are the key LayerNorm of the exact integer projection.  70 tokens: one full and
-    one ragged 64-row tile of the register-direct products; 600: the LDS-tiled ones."""
+    the keys are the key LayerNorm of the exact integer projection.  70 tokens: one ragged
+    128-row tile and many K splits; 600: four full tiles and a ragged one."""
     print(f"[project] exact integers T={t}", flush=True)
     g = np.random.default_rng(90 + t)
     bits = synth.bf16_bits_from_f32
