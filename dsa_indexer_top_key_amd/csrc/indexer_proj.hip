@@ -74,7 +74,7 @@ size_t proj_workspace_bytes(int32_t T) {
 // n < n_b0 of the weight come from b0 and the others from b1 (row n - n_b0).  A 128 x 128
 // block tile: its A rows and weight rows stream through LDS, shared by the block's four waves
 // (2 x 2, each a 64 x 64 tile of four accumulators), so every operand byte is read from L2
-// once per block.  grid (column tiles, row tiles, splits).
+// once per block.
 // K moves in 64-wide chunks (four MFMA steps, 128 bytes per row) through a three-slot ring
 // filled by direct global->LDS copies two chunks ahead; one barrier per chunk.  Row r of a
 // slot occupies 128 bytes; its 16-byte piece p sits at position p ^ ((r / 2) % 8), so the 16
@@ -86,17 +86,37 @@ constexpr int kLdsRing = 3;
 constexpr int kLdsSlot = 2 * kLdsTile * kLdsChunk;  // bf16 elements per slot (A then weight)
 constexpr int kLdsCopies = 2 * kLdsTile / 8 / 4;  // 1 KB copies per wave per chunk: 8
 
-__global__ __launch_bounds__(256) void proj_gemm_lds_kernel(
-    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b0,
-    const uint16_t* __restrict__ b1, int n_b0, int M, int N, int K, int cps,
-    float* __restrict__ part) {
+struct ProjProduct {
+    const uint16_t* a;   // [M, K]
+    const uint16_t* b0;  // weight rows 0 .. n_b0-1, [n_b0, K]
+    const uint16_t* b1;  // weight rows n_b0 .. N-1, [N - n_b0, K]
+    int n_b0, N, K, cps;
+    int col_tiles, row_tiles, blocks;  // blocks = col_tiles * row_tiles * splits
+    float* part;         // [splits, M, N]
+};
+
+// Both products run in one launch: blocks [0, p0.blocks) take the first product, the rest the
+// second (their latencies overlap; one launch instead of two).  Within a product,
+// block index = (split * row_tiles + row tile) * col_tiles + column tile.
+__global__ __launch_bounds__(256) void proj_gemm_lds_kernel(ProjProduct p0, ProjProduct p1,
+                                                            int M) {
     __shared__ __attribute__((aligned(1024))) uint16_t ring[kLdsRing][kLdsSlot];
+    const bool first = static_cast<int>(blockIdx.x) < p0.blocks;  // block-uniform
+    const ProjProduct& pr = first ? p0 : p1;
+    const int bid = first ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) - p0.blocks;
+    const uint16_t* __restrict__ a = pr.a;
+    const uint16_t* __restrict__ b0 = pr.b0;
+    const uint16_t* __restrict__ b1 = pr.b1;
+    const int n_b0 = pr.n_b0, N = pr.N, K = pr.K, cps = pr.cps;
+    float* __restrict__ part = pr.part;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave >> 1, wc = wave & 1;
-    const int m0 = kLdsTile * static_cast<int>(blockIdx.y);
-    const int n0 = kLdsTile * static_cast<int>(blockIdx.x);
-    const int split = blockIdx.z;
+    const int ct = bid % pr.col_tiles;
+    const int rt = (bid / pr.col_tiles) % pr.row_tiles;
+    const int split = bid / (pr.col_tiles * pr.row_tiles);
+    const int m0 = kLdsTile * rt;
+    const int n0 = kLdsTile * ct;
     const int col = lane & 31, hh = lane >> 5;
     const int chunks = K / kLdsChunk;
     const int c_begin = split * cps;
@@ -178,40 +198,43 @@ __global__ __launch_bounds__(256) void proj_gemm_lds_kernel(
         }
 }
 
-// One block (256 threads) per token t: threads 0..255 finish the 4096 query outputs (four
-// groups of four columns each), wave 0 the key (two columns per lane, LayerNorm over the
-// wave) and wave 1 the 32 head weights.  Splits are added in ascending order.
+// `parts` blocks (256 threads) per token t: block part j adds the splits of query columns
+// [j 4096 / parts, (j + 1) 4096 / parts) (two adjacent ones per thread and step) and rounds
+// them; part 0's first wave also finishes the key (two columns per lane, LayerNorm over the
+// wave) and the last part's the 32 head weights.  Splits are added in ascending order.  Small
+// T spreads a token over 8 blocks (T = 64: 64 blocks would leave most CUs idle), large T
+// takes one block per token.
+static int epilogue_parts(int32_t T) { return T < 1024 ? 8 : 1; }
+
 __global__ __launch_bounds__(256) void proj_epilogue_kernel(
     const float* __restrict__ pq, int q_splits, const float* __restrict__ pkw, int kw_splits,
     int32_t T, const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
     uint16_t* __restrict__ q_idx, uint16_t* __restrict__ w, uint16_t* __restrict__ keys,
-    const int64_t* __restrict__ key_rows) {
-    const int t = blockIdx.x;
+    const int64_t* __restrict__ key_rows, int parts) {
+    const int t = static_cast<int>(blockIdx.x) / parts;
+    const int j = static_cast<int>(blockIdx.x) - t * parts;
     const int tid = threadIdx.x;
     const int64_t q_stride = static_cast<int64_t>(T) * kQOut;
-#pragma unroll
-    for (int i = 0; i < kQOut / (4 * 256); ++i) {
-        const int n = 4 * (tid + 256 * i);
+    const int c_end = (j + 1) * (kQOut / parts);
+    for (int n = j * (kQOut / parts) + 2 * tid; n < c_end; n += 512) {
         const float* p = pq + static_cast<int64_t>(t) * kQOut + n;
-        f32x4 v = *reinterpret_cast<const f32x4*>(p);
+        f32x2 v = *reinterpret_cast<const f32x2*>(p);
         // unrolled so that the loads of several splits are in flight at once; the sums still
         // go in ascending split order
-#pragma unroll 4
+#pragma unroll 8
         for (int s = 1; s < q_splits; ++s) {
-            const f32x4 u = *reinterpret_cast<const f32x4*>(p + s * q_stride);
-            v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+            const f32x2 u = *reinterpret_cast<const f32x2*>(p + s * q_stride);
+            v[0] += u[0];
+            v[1] += u[1];
         }
-        u32x2 o;
-        o[0] = pack_bf16x2(v[0], v[1]);
-        o[1] = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<u32x2*>(q_idx + static_cast<int64_t>(t) * kQOut + n) = o;
+        *reinterpret_cast<uint32_t*>(q_idx + static_cast<int64_t>(t) * kQOut + n) = pack_bf16x2(v[0], v[1]);
     }
     const int wave = tid >> 6, lane = lane_id();
     const int64_t kw_stride = static_cast<int64_t>(T) * kKWOut;
     const float* pk = pkw + static_cast<int64_t>(t) * kKWOut;
-    if (wave == 0) {
+    if (j == 0 && wave == 0) {
         float x0 = pk[2 * lane], x1 = pk[2 * lane + 1];
-#pragma unroll 4
+#pragma unroll 8
         for (int s = 1; s < kw_splits; ++s) {
             x0 += pk[s * kw_stride + 2 * lane];
             x1 += pk[s * kw_stride + 2 * lane + 1];
@@ -229,9 +252,10 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(
         const float y0 = d0 * r * gamma[2 * lane] + beta[2 * lane];
         const float y1 = d1 * r * gamma[2 * lane + 1] + beta[2 * lane + 1];
         *reinterpret_cast<uint32_t*>(keys + key_rows[t] * kIndexDim + 2 * lane) = pack_bf16x2(y0, y1);
-    } else if (wave == 1 && lane < kIndexHeads) {
+    }
+    if (j == parts - 1 && wave == 1 && lane < kIndexHeads) {
         float v = pk[kIndexDim + lane];
-#pragma unroll 4
+#pragma unroll 8
         for (int s = 1; s < kw_splits; ++s) v += pk[s * kw_stride + kIndexDim + lane];
         w[static_cast<int64_t>(t) * kIndexHeads + lane] = f32_to_bf16(v);
     }
@@ -248,14 +272,16 @@ hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uin
     float* pkw = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           ((q_bytes + 255) & ~static_cast<size_t>(255)));
     const int mt = ceil_div(T, kLdsTile);
-    hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(ceil_div(kQOut, kLdsTile), mt, p.q_splits),
-                       dim3(256), 0, stream, c_q, w_qi, w_qi, kQOut, T, kQOut, kQLatent, p.q_cps,
-                       pq);
-    hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(ceil_div(kKWOut, kLdsTile), mt, p.kw_splits),
-                       dim3(256), 0, stream, h, w_k, w_w, kIndexDim, T, kKWOut, kResidual,
-                       p.kw_cps, pkw);
-    hipLaunchKernelGGL(proj_epilogue_kernel, dim3(T), dim3(256), 0, stream, pq, p.q_splits, pkw,
-                       p.kw_splits, T, gamma, beta, eps, q_idx, w, keys, key_rows);
+    ProjProduct q{c_q, w_qi, w_qi, kQOut, kQOut, kQLatent, p.q_cps, ceil_div(kQOut, kLdsTile), mt, 0, pq};
+    q.blocks = q.col_tiles * mt * p.q_splits;
+    ProjProduct kw{h, w_k, w_w, kIndexDim, kKWOut, kResidual, p.kw_cps, ceil_div(kKWOut, kLdsTile), mt, 0, pkw};
+    kw.blocks = kw.col_tiles * mt * p.kw_splits;
+    // the residual product's blocks (K = 7168) are the longest: dispatched first
+    hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(q.blocks + kw.blocks), dim3(256), 0, stream, kw, q, T);
+    const int parts = epilogue_parts(T);
+    hipLaunchKernelGGL(proj_epilogue_kernel, dim3(T * parts), dim3(256), 0, stream, pq,
+                       p.q_splits, pkw, p.kw_splits, T, gamma, beta, eps, q_idx, w, keys, key_rows,
+                       parts);
     return hipGetLastError();
 }
 
