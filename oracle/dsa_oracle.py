@@ -162,7 +162,8 @@ def indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, rows=None):
     for t in (range(q_idx.shape[0]) if rows is None else rows):
         b = int(q_req[t])
         n = admissible_count(q_pos[t], s_len[b])
-        k_rows = bf16_to_f64(keys[kv_off[b]: kv_off[b] + n])
+        k_seg = keys[kv_off[b]: kv_off[b] + n]
+        k_rows = bf16_to_f64(k_seg) if k_seg.dtype == np.uint16 else k_seg.astype(np.float64)
         out.append(indexer_scores_one(bf16_to_f64(q_idx[t]), bf16_to_f64(w[t]), k_rows))
     return out
 
@@ -377,6 +378,75 @@ def indexer_projections(c_q, h, w_qi, w_k, w_w, gamma, beta, eps) -> dict:
     key = layernorm64(k_raw, gamma, beta, eps)
     return {"q_idx": f64_to_bf16(q), "w": f64_to_bf16(linear(h, w_w)), "k_raw": k_raw,
             "key": key, "key_bf16": f64_to_bf16(key)}
+
+
+# ----------------------------------------------------------------------------------------
+# Reduced-precision index-key cache.  Section "Warum Top-2048 keinen 2048-Token-Cache
+# bedeutet": index quantisation and scale metadata change the physical cache; section "Was
+# ein Deployment validieren muss": cache precision is an optional configuration and must not
+# be presented as quality-preserving (no quality is claimed here).
+# Reading: each key row is stored as 128 OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias
+# 7, 3 mantissa bits, subnormals, no infinities, 448 the largest finite value) times one
+# power-of-two scale 2^e per row, e the smallest exponent with max_d |k_d| <= 448 * 2^e (e = 0
+# for an all-zero row).  Codes round k * 2^-e to nearest, ties to even.  Scores use the
+# decoded keys code * 2^e in the same formula as indexer_scores.
+# ----------------------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP E4M3 codes (uint8) -> float64 values (0x7F and 0xFF are NaN)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float32 values with |x| <= 448 -> OCP E4M3 codes, round to nearest, ties to even; the
+    sign bit is kept (-0 -> 0x80).  Values below 2^-6 round to multiples of 2^-9 (subnormal
+    codes; 8 * 2^-9 is the smallest normal, code 0x08)."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    sign = ((u >> 31) << 7).astype(np.uint8)
+    a = np.abs(x)
+    assert np.all(a <= E4M3_MAX)
+    sub = np.rint(a.astype(np.float64) * 512.0).astype(np.int64)  # a < 2^-6: exact, then RNE
+    ua = a.view(np.uint32).astype(np.int64)
+    r = ua + 0x7FFFF + ((ua >> 20) & 1)  # round the fp32 mantissa to 3 bits, ties to even
+    norm = ((((r >> 23) - 127 + 7) << 3) | ((r >> 20) & 7))
+    mag = np.where(a < np.float32(2.0 ** -6), sub, norm)
+    return (sign | mag.astype(np.uint8)).astype(np.uint8)
+
+
+def key_scale_exponent(keys) -> np.ndarray:
+    """Per row: the smallest e with max|k| <= 448 * 2^e (keys as bf16 bits or float)."""
+    k = np.asarray(keys)
+    k64 = bf16_to_f64(k) if k.dtype == np.uint16 else k.astype(np.float64)
+    amax = np.abs(k64).max(axis=-1)
+    f, x = np.frexp(amax)  # amax = f * 2^x, f in [0.5, 1)
+    e = (x - 1) - 8 + (f > 0.875)
+    return np.where(amax > 0, e, 0).astype(np.int32)
+
+
+def quantize_keys_fp8(keys_bf16):
+    """bf16 keys [N,128] -> (codes [N,128] uint8, scales [N] float32 = 2^e)."""
+    k32 = bf16_to_f64(keys_bf16).astype(np.float32)
+    e = key_scale_exponent(keys_bf16)
+    scaled = np.ldexp(k32, -e[:, None]).astype(np.float32)  # exact: a power-of-two scaling
+    return e4m3_encode(scaled), np.ldexp(np.float32(1.0), e).astype(np.float32)
+
+
+def dequantize_keys_fp8(codes, scales) -> np.ndarray:
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[:, None]
+
+
+def indexer_scores_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, rows=None):
+    """indexer_scores with the keys decoded from the FP8 cache."""
+    return indexer_scores(q_idx, w, dequantize_keys_fp8(codes, scales), kv_off, q_req, q_pos,
+                          rows=rows)
 
 
 # ----------------------------------------------------------------------------------------
