@@ -13,6 +13,7 @@ import os
 
 __all__ = ["DsaError", "library", "index_keys_layernorm", "indexer_scores", "topk", "value_gate",
            "indexer_project", "indexer_project_workspace_size", "Q_LATENT", "RESIDUAL",
+           "quantize_index_keys_fp8", "indexer_scores_fp8", "indexer_topk_fp8",
            "indexer_topk", "indexer_topk_workspace_size", "sparse_mla_attn",
            "sparse_mla_workspace_size", "INDEX_HEADS", "INDEX_DIM", "TOPK", "MLA_HEADS",
            "LATENT_DIM", "COMPANION_DIM", "VALUE_DIM"]
@@ -58,6 +59,11 @@ _SIGNATURES = {
                              _i32, _p, _p, _sz, _p], ctypes.c_int),
     "dsa_value_gate": ([_p, _p, _p, _i32, _i32, _p, _p], ctypes.c_int),
     "dsa_indexer_project_workspace_size": ([_i32], _sz),
+    "dsa_quantize_index_keys_fp8": ([_p, _i64, _p, _p, _p], ctypes.c_int),
+    "dsa_indexer_scores_fp8": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i64, _i32, _i32, _p, _i64,
+                                _p], ctypes.c_int),
+    "dsa_indexer_topk_fp8": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i64, _i32, _i32, _i32, _p,
+                              _p, _sz, _p], ctypes.c_int),
     "dsa_indexer_project": ([_p, _p, _p, _p, _p, _p, _p, _f32, _i32, _p, _p, _p, _p, _p, _sz, _p],
                             ctypes.c_int),
 }
@@ -298,3 +304,65 @@ def indexer_project(c_q, h, w_qi, w_k, w_w, gamma, beta, eps: float, keys, key_r
         _ptr(_contig(q_idx, "q_idx")), _ptr(_contig(w, "w")), _ptr(keys), _ptr(key_rows),
         _ptr(workspace), ws_bytes, _stream(stream)))
     return q_idx, w
+
+
+def _codes(codes, scales):
+    torch = _torch()
+    _contig(_dev(codes, "codes"), "codes")
+    _contig(_dev(scales, "scales"), "scales")
+    if codes.dtype != torch.uint8 or scales.dtype != torch.float32:
+        raise TypeError("codes must be uint8 and scales float32")
+    if codes.dim() != 2 or codes.shape[1] != INDEX_DIM or tuple(scales.shape) != (codes.shape[0],):
+        raise ValueError("codes must be [rows,128] and scales [rows]")
+
+
+def quantize_index_keys_fp8(keys, codes=None, scales=None, stream=None):
+    """FP8 index-key cache: bf16 keys [N,128] -> (codes [N,128] uint8 OCP E4M3, scales [N]
+    float32 powers of two); key = E4M3(code) * scale."""
+    torch = _torch()
+    _contig(_bits16(_dev(keys, "keys"), "keys"), "keys")
+    n = keys.shape[0]
+    if codes is None:
+        codes = torch.empty((n, INDEX_DIM), dtype=torch.uint8, device=keys.device)
+    if scales is None:
+        scales = torch.empty((n,), dtype=torch.float32, device=keys.device)
+    _codes(codes, scales)
+    _check("dsa_quantize_index_keys_fp8", library().dsa_quantize_index_keys_fp8(
+        _ptr(keys), n, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def indexer_scores_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, max_s: int, scores=None,
+                       stream=None):
+    """Stage 2 over the FP8 key cache: fp32 scores [T, max_s]; entries j >= n_t untouched."""
+    torch = _torch()
+    b = _layout(kv_off, q_req, q_pos)
+    _codes(codes, scales)
+    t = q_idx.shape[0]
+    if scores is None:
+        scores = torch.full((t, max_s), float("nan"), dtype=torch.float32, device=q_idx.device)
+    _check("dsa_indexer_scores_fp8", library().dsa_indexer_scores_fp8(
+        _ptr(_contig(_bits16(q_idx, "q_idx"), "q_idx")), _ptr(_contig(_bits16(w, "w"), "w")),
+        _ptr(codes), _ptr(scales), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b, int(max_s),
+        q_idx.shape[1], q_idx.shape[2], _ptr(scores), scores.stride(0), _stream(stream)))
+    return scores
+
+
+def indexer_topk_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, max_s: int, k: int = TOPK,
+                     ids=None, workspace=None, stream=None):
+    """Stages 2+3 over the FP8 key cache: [T,2048] request-local position IDs."""
+    torch = _torch()
+    b = _layout(kv_off, q_req, q_pos)
+    _codes(codes, scales)
+    t = q_idx.shape[0]
+    if ids is None:
+        ids = torch.empty((t, k), dtype=torch.int32, device=q_idx.device)
+    need = indexer_topk_workspace_size(t, max_s)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_idx.device)
+    _check("dsa_indexer_topk_fp8", library().dsa_indexer_topk_fp8(
+        _ptr(_contig(_bits16(q_idx, "q_idx"), "q_idx")), _ptr(_contig(_bits16(w, "w"), "w")),
+        _ptr(codes), _ptr(scales), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b, int(max_s),
+        q_idx.shape[1], q_idx.shape[2], k, _ptr(_contig(ids, "ids")), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return ids

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa_amd.so")
 SOURCES = ["ln_keys.hip", "indexer.hip", "indexer_prefill.hip", "topk.hip", "sparse_mla.hip", "value_gate.hip",
-           "indexer_proj.hip", "dsa_api.cpp"]
+           "indexer_proj.hip", "indexer_fp8.hip", "dsa_api.cpp"]
 # Per-file code-generation options.  sparse_mla: MFMA results in VGPRs where they fit (its
 # output accumulators then stay put; with the default AGPR form the register allocator
 # shuttled one output tile between AGPRs and VGPRs around every S^T chain).

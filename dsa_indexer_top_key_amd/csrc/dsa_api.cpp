@@ -31,6 +31,13 @@ size_t sparse_mla_workspace_bytes(int32_t T);
 hipError_t launch_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
                              int32_t T, uint16_t* out, hipStream_t stream);
 size_t proj_workspace_bytes(int32_t T);
+hipError_t launch_quantize_keys_fp8(const uint16_t* keys, int64_t n_rows, uint8_t* codes,
+                                    float* scales, hipStream_t stream);
+hipError_t launch_indexer_scores_fp8(const uint16_t* q_idx, const uint16_t* w, const uint8_t* codes,
+                                     const float* kscale, const int64_t* kv_off,
+                                     const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                     int64_t max_s, float* scores, int64_t ld,
+                                     hipStream_t stream);
 hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uint16_t* w_qi,
                                const uint16_t* w_k, const uint16_t* w_w, const float* gamma,
                                const float* beta, float eps, int32_t T, uint16_t* q_idx,
@@ -300,4 +307,72 @@ dsa_status_t dsa_indexer_project(const uint16_t* c_q, const uint16_t* h, const u
     return from_hip(dsa::launch_indexer_proj(c_q, h, w_qi, w_k, w_w, gamma, beta, eps, T, q_idx,
                                              w, keys, key_rows, workspace,
                                              static_cast<hipStream_t>(stream)), fn);
+}
+
+dsa_status_t dsa_quantize_index_keys_fp8(const uint16_t* keys, int64_t n_rows, uint8_t* codes,
+                                         float* scales, void* stream) {
+    const char* fn = "dsa_quantize_index_keys_fp8";
+    DSA_REQUIRE(n_rows >= 0, DSA_ERR_INVALID_ARG, "%s: n_rows=%lld is negative", fn,
+                static_cast<long long>(n_rows));
+    if (n_rows == 0) return ok();
+    DSA_REQUIRE(keys && codes && scales, DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+    DSA_REQUIRE(aligned(keys, 16) && aligned(codes, 16) && aligned(scales, 4), DSA_ERR_INVALID_ARG,
+                "%s: keys and codes must be 16-byte, scales 4-byte aligned", fn);
+    return from_hip(dsa::launch_quantize_keys_fp8(keys, n_rows, codes, scales,
+                                                  static_cast<hipStream_t>(stream)), fn);
+}
+
+dsa_status_t dsa_indexer_scores_fp8(const uint16_t* q_idx, const uint16_t* w, const uint8_t* codes,
+                                    const float* scales, const int64_t* kv_off,
+                                    const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                    int32_t B, int64_t max_S, int32_t n_heads, int32_t head_dim,
+                                    float* scores, int64_t ld_scores, void* stream) {
+    const char* fn = "dsa_indexer_scores_fp8";
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    if (T == 0) return ok();
+    dsa_status_t st = check_indexer(fn, q_idx, w, reinterpret_cast<const uint16_t*>(codes), kv_off,
+                                    q_req, q_pos, T, B, max_S, n_heads, head_dim);
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(scales && aligned(scales, 4), DSA_ERR_INVALID_ARG, "%s: scales null or misaligned", fn);
+    DSA_REQUIRE(scores && aligned(scores, 4), DSA_ERR_INVALID_ARG, "%s: scores null or misaligned", fn);
+    DSA_REQUIRE(ld_scores >= max_S, DSA_ERR_INVALID_ARG, "%s: ld_scores=%lld < max_S=%lld", fn,
+                static_cast<long long>(ld_scores), static_cast<long long>(max_S));
+    return from_hip(dsa::launch_indexer_scores_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, T,
+                                                   max_S, scores, ld_scores,
+                                                   static_cast<hipStream_t>(stream)), fn);
+}
+
+dsa_status_t dsa_indexer_topk_fp8(const uint16_t* q_idx, const uint16_t* w, const uint8_t* codes,
+                                  const float* scales, const int64_t* kv_off,
+                                  const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                  int32_t B, int64_t max_S, int32_t n_heads, int32_t head_dim,
+                                  int32_t topk, int32_t* ids, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    const char* fn = "dsa_indexer_topk_fp8";
+    DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
+    DSA_REQUIRE(topk == DSA_TOPK, DSA_ERR_UNSUPPORTED, "%s: topk=%d unsupported (only %d)", fn,
+                topk, DSA_TOPK);
+    if (T == 0) return ok();
+    dsa_status_t st = check_indexer(fn, q_idx, w, reinterpret_cast<const uint16_t*>(codes), kv_off,
+                                    q_req, q_pos, T, B, max_S, n_heads, head_dim);
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(scales && aligned(scales, 4), DSA_ERR_INVALID_ARG, "%s: scales null or misaligned", fn);
+    DSA_REQUIRE(ids && aligned(ids, 4), DSA_ERR_INVALID_ARG, "%s: ids null or misaligned", fn);
+    const size_t need = dsa_indexer_topk_workspace_size(T, max_S);
+    DSA_REQUIRE(workspace && aligned(workspace, kAlign), DSA_ERR_WORKSPACE,
+                "%s: workspace null or not %zu-byte aligned", fn, kAlign);
+    DSA_REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE,
+                "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* scores = static_cast<float*>(workspace);
+    const int64_t ld = score_ld(max_S);
+    hipError_t e = dsa::launch_indexer_scores_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, T,
+                                                  max_S, scores, ld, s);
+    if (e != hipSuccess) return from_hip(e, fn);
+    int32_t* cand = dsa::topk_workspace_bytes(T, max_S) > 0
+                        ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + score_bytes(T, max_S))
+                        : nullptr;
+    return from_hip(dsa::launch_topk(scores, ld, nullptr, kv_off, q_req, q_pos, T, max_S, ids, s,
+                                     cand),
+                    fn);
 }

@@ -150,6 +150,39 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 index-key cache (a reduced-precision cache variant).  Page "Kimi K3.1 Pro: Sparse-
+ * Zugriffe, keine kleinere Historie", section "Warum Top-2048 keinen 2048-Token-Cache
+ * bedeutet" (index quantisation and scale metadata change the physical cache) and section
+ * "Was ein Deployment validieren muss" (cache precision is an option, not a
+ * quality-preserving default; no quality is claimed).
+ * Row j is stored as 128 OCP FP8 E4M3 codes and a float scale 2^e_j, e_j the smallest
+ * exponent with max_d |k_jd| <= 448 * 2^e_j (e_j = 0 for an all-zero row);
+ * code = round-to-nearest-even(k_jd * 2^-e_j).  Decoded key = E4M3 value * scale.
+ *
+ * dsa_quantize_index_keys_fp8: keys [n_rows,128] bf16 (16-byte aligned) -> codes
+ *   [n_rows,128] uint8 (16-byte aligned) and scales [n_rows] float32 (4-byte aligned).
+ *   Bit-reproducible (exact power-of-two scaling, integer rounding).
+ * dsa_indexer_scores_fp8 / dsa_indexer_topk_fp8: as dsa_indexer_scores / dsa_indexer_topk with
+ *   the keys replaced by (codes, scales): scores[t][j] = sum_h w[t][h] * max(0,
+ *   q_idx[t][h] . decoded key j), fp32 sums; the workspace of dsa_indexer_topk_fp8 is sized by
+ *   dsa_indexer_topk_workspace_size.
+ * Errors: as the bf16 entry points; codes must be 16-byte and scales 4-byte aligned.
+ */
+dsa_status_t dsa_quantize_index_keys_fp8(const uint16_t* keys, int64_t n_rows, uint8_t* codes,
+                                         float* scales, void* stream);
+dsa_status_t dsa_indexer_scores_fp8(const uint16_t* q_idx, const uint16_t* w, const uint8_t* codes,
+                                    const float* scales, const int64_t* kv_off,
+                                    const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                    int32_t B, int64_t max_S, int32_t n_heads, int32_t head_dim,
+                                    float* scores, int64_t ld_scores, void* stream);
+dsa_status_t dsa_indexer_topk_fp8(const uint16_t* q_idx, const uint16_t* w, const uint8_t* codes,
+                                  const float* scales, const int64_t* kv_off,
+                                  const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                  int32_t B, int64_t max_S, int32_t n_heads, int32_t head_dim,
+                                  int32_t topk, int32_t* ids, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Stage 4 -- absorbed-MLA read restricted to the selected positions.
  * q        [T,96,576] bf16 absorbed queries (512 latent + 64 companion dims), 16-B aligned.
  * latent   row r at latent + r*ld_latent holds the 512-wide latent (first 512 elements).

@@ -203,3 +203,32 @@ def test_indexer_project_validation_and_workspace():
     assert pj(ws=P(0)) == WORKSPACE
     assert pj(ws_bytes=need - 1) == WORKSPACE
     assert pj(ws=fake(0x10010)) == WORKSPACE  # 256-byte alignment
+
+
+def test_fp8_key_cache_validation():
+    lib = dsa.library()
+    qz = lambda k=fake(), n=4, c=fake(), s=fake(): lib.dsa_quantize_index_keys_fp8(k, n, c, s, P(0))
+    assert qz(n=0, k=P(0), c=P(0), s=P(0)) == OK
+    assert qz(n=-1) == INVALID
+    assert qz(k=P(0)) == INVALID and qz(c=P(0)) == INVALID and qz(s=P(0)) == INVALID
+    assert qz(k=fake(0x10008)) == INVALID and qz(c=fake(0x10004)) == INVALID
+    assert qz(s=fake(0x10002)) == INVALID
+
+    def sc(T=2, B=2, S=100, H=32, D=128, c=fake(), s=fake(), out=fake(), ld=100):
+        return lib.dsa_indexer_scores_fp8(fake(), fake(), c, s, fake(), fake(), fake(), T, B, S, H,
+                                          D, out, ld, P(0))
+    assert sc(T=0) == OK
+    assert sc(T=-1) == INVALID
+    assert sc(H=16) == UNSUPPORTED
+    assert sc(c=P(0)) == INVALID and sc(s=P(0)) == INVALID and sc(out=P(0)) == INVALID
+    assert sc(c=fake(0x10008)) == INVALID and sc(s=fake(0x10002)) == INVALID
+    assert sc(ld=99) == INVALID
+    need = lib.dsa_indexer_topk_workspace_size(2, 100)
+
+    def tk(T=2, k=2048, ids=fake(), ws=fake(), wsb=need, s=fake()):
+        return lib.dsa_indexer_topk_fp8(fake(), fake(), fake(), s, fake(), fake(), fake(), T, 2,
+                                        100, 32, 128, k, ids, ws, wsb, P(0))
+    assert tk(T=0) == OK
+    assert tk(k=1024) == UNSUPPORTED
+    assert tk(ids=P(0)) == INVALID and tk(s=P(0)) == INVALID
+    assert tk(ws=P(0)) == WORKSPACE and tk(wsb=need - 1) == WORKSPACE
