@@ -7,8 +7,9 @@ the prefill indexer (indexer + top-k) on a 4096-query chunk at positions 61440..
 65536-position request, in TFLOP/s of causal scoring work, the index-key LayerNorm
 cache fill, and beside the step the two neighbouring steps of the layer: the indexer-side
 projections (query latent / residual -> q_idx, LayerNorm key into its cache row, head
-weights) for the decode batch (GB/s) and the prefill chunk (TFLOP/s), and the post-read value
-up-projection with its sigmoid gate.  All timings use HIP events on the stream the kernels
+weights) for the decode batch (GB/s) and the prefill chunk (TFLOP/s), the post-read value
+up-projection with its sigmoid gate, and the decode step over the FP8 index-key cache variant
+(E4M3 codes + one scale per key: 132 instead of 256 key bytes per position).  All timings use HIP events on the stream the kernels
 run on.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
@@ -46,10 +47,12 @@ def n_admissible(lay):
     return np.maximum(0, np.minimum(lay.q_pos.astype(np.int64) + 1, lay.s_len[lay.q_req]))
 
 
-def decode_alg(lay):
+def decode_alg(lay, key_bytes=256):
+    """Algorithmic bytes and flops of a decode step; key_bytes per cached index key (256 for
+    the bf16 cache, 132 for 128 FP8 codes + a 4-byte scale)."""
     n = n_admissible(lay)
     sel = np.minimum(n, 2048)
-    b_idx = 256 * n + 32 * 128 * 2 + 32 * 2          # keys, q_idx, w
+    b_idx = key_bytes * n + 32 * 128 * 2 + 32 * 2    # keys, q_idx, w
     b_topk = 2048 * 4                               # IDs written
     b_mla = 1152 * sel + 96 * 576 * 2 + 96 * 512 * 2  # gathered rows, q, out
     f_idx = 2 * 32 * 128 * n
@@ -233,6 +236,22 @@ def main():
                             dp["beta"], synth.LN_EPS, p_keys, p_rows, q_idx=p_q, w=p_w,
                             workspace=p_ws)
 
+    # FP8 index-key cache variant (a reduced-precision cache option; no quality is claimed):
+    # the same decode step with the keys read as E4M3 codes + one scale per key
+    f8_codes, f8_scales = dsa.quantize_index_keys_fp8(keys)
+
+    def quantize_fill():
+        dsa.quantize_index_keys_fp8(keys, codes=f8_codes, scales=f8_scales)
+
+    def step_fp8():
+        dsa.indexer_topk_fp8(d["q_idx"], d["w"], f8_codes, f8_scales, d["kv_off"], d["q_req"],
+                             d["q_pos"], lay.max_s, ids=ids, workspace=ws_idx)
+        step_mla()
+
+    def scores_fp8():
+        dsa.indexer_scores_fp8(d["q_idx"], d["w"], f8_codes, f8_scales, d["kv_off"], d["q_req"],
+                               d["q_pos"], lay.max_s, scores=scores)
+
     if args.profile_kernels:
         for _ in range(10):
             step()
@@ -241,6 +260,8 @@ def main():
             ln_fill()
             value_gate()
             project()
+            quantize_fill()
+            step_fp8()
         torch.cuda.synchronize()
         n = 256 << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -272,6 +293,10 @@ def main():
     ms_vg = per_call_events(value_gate, args.steps, stream, torch)
     ms_pj = per_call_events(project, args.steps, stream, torch)
     pj_bytes = proj_alg_bytes(lay.T)
+    ms_f8 = timed(step_fp8, args.steps, args.warmup, stream, torch)
+    ms_f8_scores = per_call_events(scores_fp8, args.steps, stream, torch)
+    ms_f8_fill = per_call_events(quantize_fill, max(3, args.steps // 4), stream, torch)
+    alg8 = decode_alg(lay, key_bytes=132)
     vg_bytes = 96 * 128 * 512 * 2 + lay.T * 96 * (512 + 2 * 128) * 2  # W_UV, o, gate, out
     vg_flops = 2 * lay.T * 96 * 128 * 512
     qps = lay.T / (ms_step * 1e-3)
@@ -300,6 +325,15 @@ def main():
         "indexer_projections": {"ms": round(ms_pj, 5), "bytes": pj_bytes,
                                 "GBps": round(pj_bytes / (ms_pj * 1e-3) / 1e9, 1),
                                 "hbm_frac": round(pj_bytes / (ms_pj * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "fp8_index_key_cache": {
+            "ms_per_step": round(ms_f8, 5), "queries_per_s": round(lay.T / (ms_f8 * 1e-3), 1),
+            "alg_bytes_per_step": alg8["bytes"],
+            "hbm_GBps": round(alg8["bytes"] / (ms_f8 * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg8["bytes"] / (ms_f8 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "scores_kernel_ms": round(ms_f8_scores, 5),
+            "scores_kernel_GBps": round(alg8["bytes_indexer"] / (ms_f8_scores * 1e-3) / 1e9, 1),
+            "quantize_fill_ms": round(ms_f8_fill, 5),
+            "quantize_fill_GBps": round(lay.N * (256 + 132) / (ms_f8_fill * 1e-3) / 1e9, 1)},
         "sparse_mla_tflops": round(alg["flops_mla"] / (ms_mla * 1e-3) / 1e12, 1),
         "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm",
                      "achieved": round(scores_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
