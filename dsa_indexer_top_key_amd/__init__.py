@@ -14,6 +14,7 @@ import os
 __all__ = ["DsaError", "library", "index_keys_layernorm", "indexer_scores", "topk", "value_gate",
            "indexer_project", "indexer_project_workspace_size", "Q_LATENT", "RESIDUAL",
            "quantize_index_keys_fp8", "indexer_scores_fp8", "indexer_topk_fp8",
+           "indexer_topk_paged", "sparse_mla_attn_paged",
            "indexer_topk", "indexer_topk_workspace_size", "sparse_mla_attn",
            "sparse_mla_workspace_size", "INDEX_HEADS", "INDEX_DIM", "TOPK", "MLA_HEADS",
            "LATENT_DIM", "COMPANION_DIM", "VALUE_DIM"]
@@ -60,6 +61,10 @@ _SIGNATURES = {
     "dsa_value_gate": ([_p, _p, _p, _i32, _i32, _p, _p], ctypes.c_int),
     "dsa_indexer_project_workspace_size": ([_i32], _sz),
     "dsa_quantize_index_keys_fp8": ([_p, _i64, _p, _p, _p], ctypes.c_int),
+    "dsa_indexer_topk_paged": ([_p, _p, _p, _p, _i32, _i32, _p, _p, _p, _i32, _i32, _i64, _i32, _i32,
+                                _i32, _p, _p, _sz, _p], ctypes.c_int),
+    "dsa_sparse_mla_attn_paged": ([_p, _p, _i64, _p, _i64, _p, _i32, _i32, _p, _p, _p, _i32, _i32,
+                                   _i32, _i32, _f32, _p, _i32, _p, _p, _sz, _p], ctypes.c_int),
     "dsa_indexer_scores_fp8": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i64, _i32, _i32, _p, _i64,
                                 _p], ctypes.c_int),
     "dsa_indexer_topk_fp8": ([_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i64, _i32, _i32, _i32, _p,
@@ -366,3 +371,68 @@ def indexer_topk_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, max_s: int, 
         q_idx.shape[1], q_idx.shape[2], k, _ptr(_contig(ids, "ids")), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return ids
+
+
+def _pages(page_table):
+    torch = _torch()
+    _contig(_dev(page_table, "page_table"), "page_table")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2:
+        raise TypeError("page_table must be an int32 [B, max_pages] tensor")
+    return page_table.shape[1]
+
+
+def indexer_topk_paged(q_idx, w, key_pool, page_table, page_size: int, kv_off, q_req, q_pos,
+                       max_s: int, k: int = TOPK, ids=None, workspace=None, stream=None):
+    """Stages 2+3 over a paged key pool: position p of request b is row
+    page_table[b, p // page_size] * page_size + p % page_size of key_pool [rows,128];
+    kv_off gives only the request lengths.  Same IDs as indexer_topk on the same logical cache."""
+    torch = _torch()
+    b = _layout(kv_off, q_req, q_pos)
+    max_pages = _pages(page_table)
+    t = q_idx.shape[0]
+    if ids is None:
+        ids = torch.empty((t, k), dtype=torch.int32, device=q_idx.device)
+    need = indexer_topk_workspace_size(t, max_s)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_idx.device)
+    _check("dsa_indexer_topk_paged", library().dsa_indexer_topk_paged(
+        _ptr(_contig(_bits16(q_idx, "q_idx"), "q_idx")), _ptr(_contig(_bits16(w, "w"), "w")),
+        _ptr(_contig(_bits16(key_pool, "key_pool"), "key_pool")), _ptr(page_table), int(page_size),
+        max_pages, _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b, int(max_s), q_idx.shape[1],
+        q_idx.shape[2], k, _ptr(_contig(ids, "ids")), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return ids
+
+
+def sparse_mla_attn_paged(q, latent_pool, kpe_pool, page_table, page_size: int, kv_off, q_req, ids,
+                          scale: float, out=None, lse=None, workspace=None, stream=None,
+                          out_dtype=None):
+    """Stage 4 over paged latent/companion pools (rows addressed as in indexer_topk_paged);
+    same results as sparse_mla_attn on the same logical cache."""
+    torch = _torch()
+    _contig(_bits16(q, "q"), "q")
+    _bits16(latent_pool, "latent_pool")
+    _bits16(kpe_pool, "kpe_pool")
+    ld_lat = _rows_ld(latent_pool, "latent_pool", LATENT_DIM)
+    ld_kpe = _rows_ld(kpe_pool, "kpe_pool", COMPANION_DIM)
+    max_pages = _pages(page_table)
+    b = kv_off.shape[0] - 1
+    for x, n in ((kv_off, "kv_off"), (q_req, "q_req"), (ids, "ids")):
+        _contig(_dev(x, n), n)
+    t, h = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((t, h, LATENT_DIM), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    if lse is None:
+        lse = torch.empty((t, h), dtype=torch.float32, device=q.device)
+    need = sparse_mla_workspace_size(t, h, ids.shape[1] if ids.dim() == 2 else TOPK)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_sparse_mla_attn_paged", library().dsa_sparse_mla_attn_paged(
+        _ptr(q), _ptr(latent_pool), ld_lat, _ptr(kpe_pool), ld_kpe, _ptr(page_table),
+        int(page_size), max_pages, _ptr(kv_off), _ptr(q_req), _ptr(ids), t, b, h, ids.shape[1],
+        float(scale), _ptr(_contig(out, "out")), 1 if out.dtype == torch.float32 else 0, _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse

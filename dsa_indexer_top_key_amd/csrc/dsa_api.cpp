@@ -16,7 +16,9 @@ hipError_t launch_ln_keys(const float* raw, const float* gamma, const float* bet
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
                                  const int64_t* kv_off, const int32_t* q_req,
                                  const int32_t* q_pos, int32_t T, int32_t B, int64_t max_s,
-                                 float* scores, int64_t ld, hipStream_t stream);
+                                 float* scores, int64_t ld, hipStream_t stream,
+                                 const int32_t* page_table = nullptr, int lg_page = 0,
+                                 int max_pages = 0);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
                        int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream,
@@ -26,7 +28,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
                              const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
                              const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
                              void* out, bool out_f32, float* lse, void* workspace,
-                             hipStream_t stream);
+                             hipStream_t stream, const int32_t* page_table = nullptr,
+                             int lg_page = 0, int max_pages = 0);
 size_t sparse_mla_workspace_bytes(int32_t T);
 hipError_t launch_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
                              int32_t T, uint16_t* out, hipStream_t stream);
@@ -184,12 +187,27 @@ size_t dsa_indexer_topk_workspace_size(int32_t T, int64_t max_S) {
     return score_bytes(T, max_S) + round_up(dsa::topk_workspace_bytes(T, max_S));
 }
 
-dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
-                              const int64_t* kv_off, const int32_t* q_req,
-                              const int32_t* q_pos, int32_t T, int32_t B, int64_t max_S,
-                              int32_t n_heads, int32_t head_dim, int32_t topk, int32_t* ids,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "dsa_indexer_topk";
+// Page-table arguments of the paged entry points: page_size a power of two in [64, 2^20],
+// max_pages >= 1, the table non-null and 4-byte aligned.  lg_page gets log2(page_size).
+static dsa_status_t check_pages(const char* fn, const int32_t* page_table, int32_t page_size,
+                                int32_t max_pages, int* lg_page) {
+    DSA_REQUIRE(page_size >= 64 && page_size <= (1 << 20) && (page_size & (page_size - 1)) == 0,
+                DSA_ERR_UNSUPPORTED, "%s: page_size=%d must be a power of two in [64, 2^20]", fn,
+                page_size);
+    DSA_REQUIRE(max_pages >= 1, DSA_ERR_INVALID_ARG, "%s: max_pages=%d must be >= 1", fn, max_pages);
+    DSA_REQUIRE(page_table && aligned(page_table, 4), DSA_ERR_INVALID_ARG,
+                "%s: page_table null or misaligned", fn);
+    *lg_page = __builtin_ctz(static_cast<unsigned>(page_size));
+    return DSA_OK;
+}
+
+static dsa_status_t indexer_topk_impl(const char* fn, const uint16_t* q_idx, const uint16_t* w,
+                                      const uint16_t* keys, const int64_t* kv_off,
+                                      const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                      int32_t B, int64_t max_S, int32_t n_heads, int32_t head_dim,
+                                      int32_t topk, int32_t* ids, void* workspace,
+                                      size_t workspace_bytes, void* stream,
+                                      const int32_t* page_table, int lg_page, int max_pages) {
     DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
     DSA_REQUIRE(topk == DSA_TOPK, DSA_ERR_UNSUPPORTED, "%s: topk=%d unsupported (only %d)", fn,
                 topk, DSA_TOPK);
@@ -207,7 +225,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
     float* scores = static_cast<float*>(workspace);
     const int64_t ld = score_ld(max_S);
     hipError_t e = dsa::launch_indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, T, B, max_S,
-                                              scores, ld, s);
+                                              scores, ld, s, page_table, lg_page, max_pages);
     if (e != hipSuccess) return from_hip(e, fn);
     int32_t* cand = dsa::topk_workspace_bytes(T, max_S) > 0
                         ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + score_bytes(T, max_S))
@@ -217,18 +235,47 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
                     fn);
 }
 
+dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
+                              const int64_t* kv_off, const int32_t* q_req,
+                              const int32_t* q_pos, int32_t T, int32_t B, int64_t max_S,
+                              int32_t n_heads, int32_t head_dim, int32_t topk, int32_t* ids,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return indexer_topk_impl("dsa_indexer_topk", q_idx, w, keys, kv_off, q_req, q_pos, T, B,
+                             max_S, n_heads, head_dim, topk, ids, workspace, workspace_bytes,
+                             stream, nullptr, 0, 0);
+}
+
+dsa_status_t dsa_indexer_topk_paged(const uint16_t* q_idx, const uint16_t* w,
+                                    const uint16_t* key_pool, const int32_t* page_table,
+                                    int32_t page_size, int32_t max_pages, const int64_t* kv_off,
+                                    const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                    int32_t B, int64_t max_S, int32_t n_heads, int32_t head_dim,
+                                    int32_t topk, int32_t* ids, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    const char* fn = "dsa_indexer_topk_paged";
+    int lg = 0;
+    if (T > 0) {
+        const dsa_status_t st = check_pages(fn, page_table, page_size, max_pages, &lg);
+        if (st != DSA_OK) return st;
+    }
+    return indexer_topk_impl(fn, q_idx, w, key_pool, kv_off, q_req, q_pos, T, B, max_S, n_heads,
+                             head_dim, topk, ids, workspace, workspace_bytes, stream, page_table,
+                             lg, max_pages);
+}
+
 size_t dsa_sparse_mla_workspace_size(int32_t T, int32_t n_heads, int32_t topk) {
     if (T <= 0 || n_heads != DSA_MLA_HEADS || topk != DSA_TOPK) return 0;
     return round_up(dsa::sparse_mla_workspace_bytes(T));
 }
 
-dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int64_t ld_latent,
-                                 const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
-                                 const int32_t* q_req, const int32_t* ids, int32_t T,
-                                 int32_t B, int32_t n_heads, int32_t topk, float scale,
-                                 void* out, int32_t out_dtype, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-    const char* fn = "dsa_sparse_mla_attn";
+static dsa_status_t sparse_mla_impl(const char* fn, const uint16_t* q, const uint16_t* latent,
+                                    int64_t ld_latent, const uint16_t* kpe, int64_t ld_kpe,
+                                    const int64_t* kv_off, const int32_t* q_req,
+                                    const int32_t* ids, int32_t T, int32_t B, int32_t n_heads,
+                                    int32_t topk, float scale, void* out, int32_t out_dtype,
+                                    float* lse, void* workspace, size_t workspace_bytes,
+                                    void* stream, const int32_t* page_table, int lg_page,
+                                    int max_pages) {
     DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
     DSA_REQUIRE(n_heads == DSA_MLA_HEADS, DSA_ERR_UNSUPPORTED,
                 "%s: n_heads=%d unsupported (only %d)", fn, n_heads, DSA_MLA_HEADS);
@@ -261,7 +308,39 @@ dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int6
     }
     return from_hip(dsa::launch_sparse_mla(q, latent, ld_latent, kpe, ld_kpe, kv_off, q_req, ids,
                                            T, scale, out, out_dtype == DSA_OUT_F32, lse,
-                                           workspace, static_cast<hipStream_t>(stream)), fn);
+                                           workspace, static_cast<hipStream_t>(stream),
+                                           page_table, lg_page, max_pages), fn);
+}
+
+dsa_status_t dsa_sparse_mla_attn(const uint16_t* q, const uint16_t* latent, int64_t ld_latent,
+                                 const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
+                                 const int32_t* q_req, const int32_t* ids, int32_t T,
+                                 int32_t B, int32_t n_heads, int32_t topk, float scale,
+                                 void* out, int32_t out_dtype, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return sparse_mla_impl("dsa_sparse_mla_attn", q, latent, ld_latent, kpe, ld_kpe, kv_off, q_req,
+                           ids, T, B, n_heads, topk, scale, out, out_dtype, lse, workspace,
+                           workspace_bytes, stream, nullptr, 0, 0);
+}
+
+dsa_status_t dsa_sparse_mla_attn_paged(const uint16_t* q, const uint16_t* latent_pool,
+                                       int64_t ld_latent, const uint16_t* kpe_pool,
+                                       int64_t ld_kpe, const int32_t* page_table,
+                                       int32_t page_size, int32_t max_pages,
+                                       const int64_t* kv_off, const int32_t* q_req,
+                                       const int32_t* ids, int32_t T, int32_t B, int32_t n_heads,
+                                       int32_t topk, float scale, void* out, int32_t out_dtype,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+    const char* fn = "dsa_sparse_mla_attn_paged";
+    int lg = 0;
+    if (T > 0) {
+        const dsa_status_t st = check_pages(fn, page_table, page_size, max_pages, &lg);
+        if (st != DSA_OK) return st;
+    }
+    return sparse_mla_impl(fn, q, latent_pool, ld_latent, kpe_pool, ld_kpe, kv_off, q_req, ids, T,
+                           B, n_heads, topk, scale, out, out_dtype, lse, workspace,
+                           workspace_bytes, stream, page_table, lg, max_pages);
 }
 
 }  // extern "C"

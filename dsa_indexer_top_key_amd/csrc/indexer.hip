@@ -67,11 +67,18 @@ static int64_t decode_chunk(int32_t T, int64_t max_s) {
 // accumulator gives lane l the key c and heads 4 g + r (r = 0..3).
 // Scores collect in LDS and leave at the end of the block in full 16-byte stores: writes
 // interleaved with the key stream measured about 10% slower than one burst at the end.
+// PAGED: the keys live in a page pool; logical position p of request b is pool row
+// page_table[b * max_pages + (p >> lg_page)] * 2^lg_page + p % 2^lg_page (kv_off then only gives
+// the request lengths).  Pages hold at least 64 positions, so a block's chunk (a multiple of 64,
+// at most 4096 keys) spans at most 64 pages: lane i holds the physical page of the chunk's i-th
+// page, and each 16-key tile, which lies in one page, reads it with a wave-uniform readlane.
+template <bool PAGED>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ keys, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos, int32_t chunks_per_q,
-    int32_t chunk, int64_t max_s, float* __restrict__ scores, int64_t ld, int vec_store) {
+    int32_t chunk, int64_t max_s, float* __restrict__ scores, int64_t ld, int vec_store,
+    const int32_t* __restrict__ page_table, int lg_page, int max_pages) {
     __shared__ __attribute__((aligned(16))) uint16_t ring[4][kDecodeRing][kDecodeTile * kIndexDim];
     __shared__ __attribute__((aligned(16))) float sbuf[kDecodeMaxChunk];
     const int t = blockIdx.x / chunks_per_q;
@@ -86,18 +93,31 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4;
     const int c = lane & 15;
-    const uint16_t* kb = keys + (kv_off[b] + k0) * kIndexDim;
+    const uint16_t* kb = PAGED ? keys : keys + (kv_off[b] + k0) * kIndexDim;
     const int n_tiles = (len + kDecodeTile - 1) / kDecodeTile;
     const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
-    // copies of this wave's j-th tile into ring slot j % 3; keys past the end copy key 0
+    int pte = 0;  // PAGED: physical page of the chunk's page `lane`
+    if constexpr (PAGED) {
+        const int64_t lp = (k0 >> lg_page) + lane;
+        const int64_t np = (k0 + len + (int64_t{1} << lg_page) - 1) >> lg_page;
+        pte = lp < np ? page_table[static_cast<int64_t>(b) * max_pages + lp] : 0;
+    }
+    // copies of this wave's j-th tile into ring slot j % 3; keys past the end copy key 0 (the
+    // tile's first key when paged, which keeps the whole tile in one page)
     auto issue = [&](int j) {
         const int kt = (wave + 4 * j) * kDecodeTile;
         const uint16_t* slot = ring[wave][j % kDecodeRing];
+        const uint16_t* tb = kb;
+        if constexpr (PAGED) {
+            const int rel = static_cast<int>(((k0 + kt) >> lg_page) - (k0 >> lg_page));
+            const int64_t page = __builtin_amdgcn_readlane(pte, rel);
+            tb = keys + ((page << lg_page) + ((k0 + kt) & ((int64_t{1} << lg_page) - 1)) - kt) * kIndexDim;
+        }
 #pragma unroll
         for (int d = 0; d < kDecodeCopies; ++d) {
             const int r = 4 * d + g;
-            const int key = kt + r < len ? kt + r : 0;
-            copy_to_lds<true>(kb + static_cast<int64_t>(key) * kIndexDim + 8 * (c ^ r),
+            const int key = kt + r < len ? kt + r : (PAGED ? kt : 0);
+            copy_to_lds<true>(tb + static_cast<int64_t>(key) * kIndexDim + 8 * (c ^ r),
                               lds_offset(slot + d * 4 * kIndexDim));
         }
     };
@@ -164,10 +184,12 @@ hipError_t launch_indexer_prefill(const uint16_t* q_idx, const uint16_t* w, cons
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
                                  const int64_t* kv_off, const int32_t* q_req,
                                  const int32_t* q_pos, int32_t T, int32_t B, int64_t max_s,
-                                 float* scores, int64_t ld, hipStream_t stream) {
+                                 float* scores, int64_t ld, hipStream_t stream,
+                                 const int32_t* page_table, int lg_page, int max_pages) {
     // Prefill kernel when queries come in runs of one request (on average >= 8 per
-    // request); per-query streaming otherwise.  Both are exact for any layout.
-    if (static_cast<int64_t>(T) >= 8 * static_cast<int64_t>(B)) {
+    // request); per-query streaming otherwise (always for a paged cache).  Both are exact for
+    // any layout.
+    if (!page_table && static_cast<int64_t>(T) >= 8 * static_cast<int64_t>(B)) {
         return launch_indexer_prefill(q_idx, w, keys, kv_off, q_req, q_pos, T, max_s, scores,
                                       ld, stream);
     } else {
@@ -176,10 +198,16 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const
         const int64_t blocks = cpq * T;
         if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
         const bool vec = reinterpret_cast<uintptr_t>(scores) % 16 == 0 && ld % 4 == 0;
-        hipLaunchKernelGGL(indexer_decode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256),
-                           0, stream, q_idx, w, keys, kv_off, q_req, q_pos,
-                           static_cast<int32_t>(cpq), static_cast<int32_t>(chunk), max_s, scores,
-                           ld, vec ? 1 : 0);
+        if (page_table)
+            hipLaunchKernelGGL(indexer_decode_kernel<true>, dim3(static_cast<unsigned>(blocks)),
+                               dim3(256), 0, stream, q_idx, w, keys, kv_off, q_req, q_pos,
+                               static_cast<int32_t>(cpq), static_cast<int32_t>(chunk), max_s,
+                               scores, ld, vec ? 1 : 0, page_table, lg_page, max_pages);
+        else
+            hipLaunchKernelGGL(indexer_decode_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                               dim3(256), 0, stream, q_idx, w, keys, kv_off, q_req, q_pos,
+                               static_cast<int32_t>(cpq), static_cast<int32_t>(chunk), max_s,
+                               scores, ld, vec ? 1 : 0, nullptr, 0, 0);
     }
     return hipGetLastError();
 }

@@ -140,12 +140,17 @@ __device__ __forceinline__ void store_tile_f32(float* dst, int64_t ld, int row0,
         dst[static_cast<int64_t>(row0 + 8 * (r >> 2) + 4 * hh + (r & 3)) * ld + col] = v[r];
 }
 
+// PAGED: the latent and companion rows live in a page pool; ID p of request b is pool row
+// page_table[b * max_pages + (p >> lg_page)] * 2^lg_page + p % 2^lg_page, translated once in the
+// ID phase (kv_off then only gives the request lengths).
+template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t ld_lat,
     const uint16_t* __restrict__ kpe, int64_t ld_kpe, const int64_t* __restrict__ kv_off,
     const int32_t* __restrict__ q_req, const int32_t* __restrict__ ids, int32_t T,
     int32_t nsplit, float scale_log2, void* __restrict__ out, int out_f32,
-    float* __restrict__ lse, void* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, void* __restrict__ part_o, float* __restrict__ part_lse,
+    const int32_t* __restrict__ page_table, int lg_page, int max_pages) {
     __shared__ MlaSmem sm;
     const int g = blockIdx.x;
     const int j = g >> 3;
@@ -186,8 +191,9 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         idv[k] = i < L ? idr[i] : -1;
     }
     const int b = q_req[t];
-    const int64_t base = kv_off[b];
-    const int64_t s_b = kv_off[b + 1] - base;
+    const int64_t off = kv_off[b];
+    const int64_t s_b = kv_off[b + 1] - off;
+    const int64_t base = PAGED ? 0 : off;  // paged: the rows below are pool rows
     if (tid == 0) sm.redo = 0;
     uint32_t end = 0;
 #pragma unroll
@@ -199,7 +205,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         const bool ok = id >= 0 && static_cast<int64_t>(id) < s_b;
         const uint64_t m = __ballot(ok);  // lanes 0..31: one tile, lanes 32..63: the next
         if (i < L) {
-            sm.rows[i] = ok ? id : 0;
+            int32_t row = ok ? id : 0;
+            if constexpr (PAGED)
+                row = (page_table[static_cast<int64_t>(b) * max_pages + (row >> lg_page)] << lg_page) |
+                      (row & ((1 << lg_page) - 1));
+            sm.rows[i] = row;
             if ((lane & 31) == 0) sm.tmask[i / kTile] = static_cast<uint32_t>(m >> (lane & 32));
         }
         if (ok) end = static_cast<uint32_t>(i + 1);
@@ -587,7 +597,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
                              const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
                              const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
                              void* out, bool out_f32, float* lse, void* workspace,
-                             hipStream_t stream) {
+                             hipStream_t stream, const int32_t* page_table, int lg_page,
+                             int max_pages) {
     const int ns = sparse_mla_nsplit(T);
     const int64_t groups = (static_cast<int64_t>(T) + 7) / 8;
     const int64_t blocks = groups * 8 * ns;
@@ -600,9 +611,15 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
                                             round256(static_cast<size_t>(T) * ns * kMlaHeads * kLatent * sizeof(float)));
     }
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, ns,
-                       scale_log2, out, out_f32 ? 1 : 0, lse, part_o, part_lse);
+    if (page_table)
+        hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256),
+                           0, stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, ns,
+                           scale_log2, out, out_f32 ? 1 : 0, lse, part_o, part_lse, page_table,
+                           lg_page, max_pages);
+    else
+        hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256),
+                           0, stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, ns,
+                           scale_log2, out, out_f32 ? 1 : 0, lse, part_o, part_lse, nullptr, 0, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     const unsigned cblocks = static_cast<unsigned>((static_cast<int64_t>(T) * kMlaHeads + 3) / 4);

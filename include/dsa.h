@@ -150,6 +150,40 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged page-pool cache layout (a cache layout variant).  Page "Kimi K3.1 Pro: Sparse-
+ * Zugriffe, keine kleinere Historie", section "Warum Top-2048 keinen 2048-Token-Cache
+ * bedeutet": page allocation changes the physical cache while the logical [T,2048] position
+ * IDs stay the same.
+ * The index keys, latent rows and companion rows of every request live in pools of fixed-size
+ * pages: logical position p of request b is pool row
+ *     page_table[b * max_pages + p / page_size] * page_size + p % page_size
+ * of key_pool [rows,128], latent_pool (row stride ld_latent) and kpe_pool (row stride ld_kpe).
+ * page_size  a power of two in [64, 2^20] (else UNSUPPORTED); max_pages >= 1 is the row stride
+ *            of page_table [B, max_pages] int32 (4-byte aligned).  Entries 0 .. ceil(S_b /
+ *            page_size) - 1 of row b must name pages of the pools, and pool rows must stay below
+ *            2^31 (device data is not checked).
+ * kv_off     [B+1] int64 as elsewhere, but only its differences (the request lengths S_b) are
+ *            used; the IDs, workspaces and outputs are those of dsa_indexer_topk and
+ *            dsa_sparse_mla_attn, and for the same logical cache the results are identical.
+ */
+dsa_status_t dsa_indexer_topk_paged(const uint16_t* q_idx, const uint16_t* w,
+                                    const uint16_t* key_pool, const int32_t* page_table,
+                                    int32_t page_size, int32_t max_pages, const int64_t* kv_off,
+                                    const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                    int32_t B, int64_t max_S, int32_t n_heads, int32_t head_dim,
+                                    int32_t topk, int32_t* ids, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+dsa_status_t dsa_sparse_mla_attn_paged(const uint16_t* q, const uint16_t* latent_pool,
+                                       int64_t ld_latent, const uint16_t* kpe_pool,
+                                       int64_t ld_kpe, const int32_t* page_table,
+                                       int32_t page_size, int32_t max_pages,
+                                       const int64_t* kv_off, const int32_t* q_req,
+                                       const int32_t* ids, int32_t T, int32_t B, int32_t n_heads,
+                                       int32_t topk, float scale, void* out, int32_t out_dtype,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
  * FP8 index-key cache (a reduced-precision cache variant).  Page "Kimi K3.1 Pro: Sparse-
  * Zugriffe, keine kleinere Historie", section "Warum Top-2048 keinen 2048-Token-Cache
  * bedeutet" (index quantisation and scale metadata change the physical cache) and section

@@ -450,6 +450,24 @@ def indexer_scores_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, rows=None)
 
 
 # ----------------------------------------------------------------------------------------
+# Paged page-pool layout.  Section "Warum Top-2048 keinen 2048-Token-Cache bedeutet": page
+# allocation changes the physical cache, not the logical positions the method works on.
+# Reading: position p of request b lives in pool row page_table[b][p // P] * P + p % P; every
+# stage computes on the logical (request-contiguous) rows, so the oracle unpages first.
+# ----------------------------------------------------------------------------------------
+def unpage_rows(pool, page_table, page_size, kv_off) -> np.ndarray:
+    """Request-contiguous rows [sum S_b, ...] gathered from a page pool."""
+    pool = np.asarray(pool)
+    pt = np.asarray(page_table, dtype=np.int64)
+    lens = request_lengths(kv_off)
+    parts = []
+    for b, n in enumerate(lens):
+        p = np.arange(n, dtype=np.int64)
+        parts.append(pool[pt[b, p // page_size] * page_size + p % page_size])
+    return np.concatenate(parts) if parts else pool[:0]
+
+
+# ----------------------------------------------------------------------------------------
 # Dense reference and dropped mass (oracle only, never timed).
 # Section "Die Mathematik ...": compared with a hypothetical full read at fixed logits and
 # values, with eps the full softmax mass outside I_t, the retained and dropped reads are

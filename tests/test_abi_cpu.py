@@ -232,3 +232,27 @@ def test_fp8_key_cache_validation():
     assert tk(k=1024) == UNSUPPORTED
     assert tk(ids=P(0)) == INVALID and tk(s=P(0)) == INVALID
     assert tk(ws=P(0)) == WORKSPACE and tk(wsb=need - 1) == WORKSPACE
+
+
+def test_paged_validation():
+    lib = dsa.library()
+    need = lib.dsa_indexer_topk_workspace_size(2, 100)
+
+    def tk(T=2, ps=64, mp=2, pt=fake(), ids=fake()):
+        return lib.dsa_indexer_topk_paged(fake(), fake(), fake(), pt, ps, mp, fake(), fake(),
+                                          fake(), T, 2, 100, 32, 128, 2048, ids, fake(), need, P(0))
+    assert tk(T=0, pt=P(0), ps=0, mp=0) == OK  # nothing to do
+    for ps in (0, 32, 63, 96, 1 << 21):
+        assert tk(ps=ps) == UNSUPPORTED, ps
+    assert tk(mp=0) == INVALID
+    assert tk(pt=P(0)) == INVALID and tk(pt=fake(0x10002)) == INVALID
+    assert tk(ids=P(0)) == INVALID
+    need_s = lib.dsa_sparse_mla_workspace_size(2, 96, 2048)
+
+    def sp(T=2, ps=64, mp=2, pt=fake(), ld=576):
+        return lib.dsa_sparse_mla_attn_paged(fake(), fake(), ld, fake(), ld, pt, ps, mp, fake(),
+                                             fake(), fake(), T, 2, 96, 2048, 0.07, fake(), 0,
+                                             fake(), fake(), need_s, P(0))
+    assert sp(T=0, pt=P(0), ps=0, mp=0) == OK
+    assert sp(ps=100) == UNSUPPORTED and sp(mp=-1) == INVALID and sp(pt=P(0)) == INVALID
+    assert sp(ld=500) == INVALID
