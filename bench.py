@@ -8,8 +8,9 @@ the prefill indexer (indexer + top-k) on a 4096-query chunk at positions 61440..
 cache fill, and beside the step the two neighbouring steps of the layer: the indexer-side
 projections (query latent / residual -> q_idx, LayerNorm key into its cache row, head
 weights) for the decode batch (GB/s) and the prefill chunk (TFLOP/s), the post-read value
-up-projection with its sigmoid gate, and the decode step over the FP8 index-key cache variant
-(E4M3 codes + one scale per key: 132 instead of 256 key bytes per position).  All timings use HIP events on the stream the kernels
+up-projection with its sigmoid gate, the decode step over the FP8 index-key cache variant
+(E4M3 codes + one scale per key: 132 instead of 256 key bytes per position), and the decode
+step over a paged page-pool cache (64-position pages in random pool order).  All timings use HIP events on the stream the kernels
 run on.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
@@ -252,6 +253,34 @@ def main():
         dsa.indexer_scores_fp8(d["q_idx"], d["w"], f8_codes, f8_scales, d["kv_off"], d["q_req"],
                                d["q_pos"], lay.max_s, scores=scores)
 
+    # paged page-pool layout: the same decode step with the keys, latent and companion rows in
+    # 64-position pages of a pool in seeded random page order
+    page = 64
+    n_pages = -(-lay.s_len // page)
+    perm = np.random.default_rng(7).permutation(int(n_pages.sum()))
+    pt_np = np.zeros((lay.B, int(n_pages.max())), np.int32)
+    row_of, k = [], 0
+    for bq in range(lay.B):
+        pt_np[bq, :n_pages[bq]] = perm[k:k + n_pages[bq]]
+        k += n_pages[bq]
+        pp = np.arange(lay.s_len[bq], dtype=np.int64)
+        row_of.append(pt_np[bq, pp // page].astype(np.int64) * page + pp % page)
+    rows_t = torch.as_tensor(np.concatenate(row_of), device=dev)
+    pg_table = torch.as_tensor(pt_np, device=dev)
+    pg_keys = torch.empty((len(perm) * page, 128), dtype=keys.dtype, device=dev)
+    pg_keys[rows_t] = keys
+    pg_lat = torch.empty((len(perm) * page, 512), dtype=d["latent"].dtype, device=dev)
+    pg_lat[rows_t] = d["latent"]
+    pg_kpe = torch.empty((len(perm) * page, 64), dtype=d["kpe"].dtype, device=dev)
+    pg_kpe[rows_t] = d["kpe"]
+    del rows_t
+
+    def step_paged():
+        dsa.indexer_topk_paged(d["q_idx"], d["w"], pg_keys, pg_table, page, d["kv_off"],
+                               d["q_req"], d["q_pos"], lay.max_s, ids=ids, workspace=ws_idx)
+        dsa.sparse_mla_attn_paged(d["q"], pg_lat, pg_kpe, pg_table, page, d["kv_off"], d["q_req"],
+                                  ids, synth.ATTN_SCALE, out=out, lse=lse, workspace=ws_mla)
+
     if args.profile_kernels:
         for _ in range(10):
             step()
@@ -262,6 +291,7 @@ def main():
             project()
             quantize_fill()
             step_fp8()
+            step_paged()
         torch.cuda.synchronize()
         n = 256 << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -297,6 +327,7 @@ def main():
     ms_f8_scores = per_call_events(scores_fp8, args.steps, stream, torch)
     ms_f8_fill = per_call_events(quantize_fill, max(3, args.steps // 4), stream, torch)
     alg8 = decode_alg(lay, key_bytes=132)
+    ms_pg = timed(step_paged, args.steps, args.warmup, stream, torch)
     vg_bytes = 96 * 128 * 512 * 2 + lay.T * 96 * (512 + 2 * 128) * 2  # W_UV, o, gate, out
     vg_flops = 2 * lay.T * 96 * 128 * 512
     qps = lay.T / (ms_step * 1e-3)
@@ -334,6 +365,11 @@ def main():
             "scores_kernel_GBps": round(alg8["bytes_indexer"] / (ms_f8_scores * 1e-3) / 1e9, 1),
             "quantize_fill_ms": round(ms_f8_fill, 5),
             "quantize_fill_GBps": round(lay.N * (256 + 132) / (ms_f8_fill * 1e-3) / 1e9, 1)},
+        "paged_cache": {
+            "page_size": page, "ms_per_step": round(ms_pg, 5),
+            "queries_per_s": round(lay.T / (ms_pg * 1e-3), 1),
+            "hbm_GBps": round(alg["bytes"] / (ms_pg * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg["bytes"] / (ms_pg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "sparse_mla_tflops": round(alg["flops_mla"] / (ms_mla * 1e-3) / 1e12, 1),
         "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm",
                      "achieved": round(scores_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
