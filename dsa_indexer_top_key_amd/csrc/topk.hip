@@ -351,15 +351,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         const uint32_t bstar = sm.prm[0];
         need -= sm.prm[1];
         cand = sm.hist[bstar];
-        if (kSaveBins && value_mode && cand <= kFastCand) {  // block-uniform
-            // Small threshold bin: its keys go to LDS and one wave finds the need-th largest
-            // key theta by counting (#keys > theta < need <= #keys >= theta); the final range
-            // is then the single key theta.  (Rows without saved bins would recompute every
-            // element's bin for this, which measured slower than the range search below.)
-#pragma unroll
-            for (int e = 0; e < E; ++e)  // (saved bins imply one register-resident chunk)
-                if (kbin[kSaveBins ? e : 0] == bstar) sm.cbuf[atomicAdd(&sm.prm[4], 1u)] = key[e];
-            lds_barrier();
+        // Small threshold bin (at most kFastCand keys, gathered in cbuf): one wave finds the
+        // need-th largest key theta by counting (#keys > theta < need <= #keys >= theta); the
+        // final range is then the single key theta.  Contains a barrier.
+        auto resolve_small_bin = [&]() {
             if (wave == 0) {
                 const uint32_t nc = __builtin_amdgcn_readfirstlane(cand);  // uniform loop bound
                 const uint32_t mine = static_cast<uint32_t>(lane) < nc ? sm.cbuf[lane] : 0u;
@@ -381,6 +376,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             rlo = rhi = sm.prm[2];
             need -= sm.prm[3];
             cand = sm.prm[5];
+        };
+        if (kSaveBins && value_mode && cand <= kFastCand) {  // block-uniform
+            // the saved bins name the threshold bin's keys
+#pragma unroll
+            for (int e = 0; e < E; ++e)  // (saved bins imply one register-resident chunk)
+                if (kbin[kSaveBins ? e : 0] == bstar) sm.cbuf[atomicAdd(&sm.prm[4], 1u)] = key[e];
+            lds_barrier();
+            resolve_small_bin();
         } else if (value_mode) {
             if (wave == 0) {
                 uint32_t klo, khi;
@@ -393,6 +396,36 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             lds_barrier();
             rlo = sm.prm[2];
             rhi = sm.prm[3];
+            if (!STREAM && cand <= kFastCand) {  // block-uniform
+                // Register-resident row without saved bins: the threshold bin is exactly the
+                // key range [rlo, rhi] (the bin map is monotone), so one compare per element
+                // gathers its keys -- cheaper than recomputing every element's bin, and than a
+                // refinement level over the range.  The gathered count must equal the bin's
+                // count; if it does not (it always should), the refinement levels below run.
+                // (k in [rlo, rhi]; absent keys (0) never are.)  One wave-uniform branch per
+                // group of four elements: almost every group holds none of the bin's keys.
+#pragma unroll
+                for (int g = 0; g < kGroups; ++g) {
+                    bool in[4];
+                    uint64_t any = 0;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        in[c] = key[4 * g + c] - rlo <= rhi - rlo;
+                        any |= __ballot(in[c]);
+                    }
+                    if (any) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            if (in[c]) {
+                                const uint32_t i = atomicAdd(&sm.prm[4], 1u);
+                                if (i < kFastCand) sm.cbuf[i] = key[4 * g + c];
+                            }
+                        }
+                    }
+                }
+                lds_barrier();
+                if (sm.prm[4] == cand) resolve_small_bin();  // block-uniform
+            }
         } else {
             const uint64_t nlo = static_cast<uint64_t>(rlo) + (static_cast<uint64_t>(bstar) << sh);
             const uint64_t nhi = nlo + ((1ull << sh) - 1);

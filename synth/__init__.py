@@ -219,6 +219,8 @@ def score_rows_np(seed: int, kind: str, rows: int, n: int) -> np.ndarray:
         x = np.tile(np.arange(n, 0, -1, dtype=np.float64), (rows, 1))
     elif kind == "heavy_tail":
         x = g.standard_cauchy((rows, n))
+    elif kind == "coarse":        # gaussian on a 1/64 grid: a handful of equal keys per value
+        x = np.round(g.standard_normal((rows, n)) * 512.0) / 64.0
     else:
         raise KeyError(kind)
     return x.astype(np.float32)
