@@ -199,21 +199,12 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m, uint32_t acc) {
 // (equal scores: lower position first) is the same at both levels, so the merge is exact.
 enum TopkMode { kRow = 0, kParts = 1, kMerge = 2 };
 
-template <int E, bool STREAM, bool VEC, int MODE>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
-    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
-    const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids,
-    int32_t parts, int64_t chunk, const int32_t* __restrict__ cands) {
-    static_assert(E % 4 == 0, "elements come in groups of four consecutive positions");
-    static_assert(MODE != kMerge || !STREAM, "a merge holds its candidates in registers");
-    constexpr int kGroups = E / 4;
-    __shared__ TopkSmem sm;
-    const int t = MODE == kParts ? static_cast<int>(blockIdx.x) / parts : static_cast<int>(blockIdx.x);
-    const int part = MODE == kParts ? static_cast<int>(blockIdx.x) - t * parts : 0;
-    const int tid = threadIdx.x;
-    const int lane = lane_id(), wave = tid >> 6;
-
+// Elements of row t: explicit n_valid[t], else the causal prefix min(q_pos + 1, S_b); at most
+// max_n, at least 0.
+__device__ __forceinline__ int64_t topk_row_len(int t, const int32_t* __restrict__ n_valid,
+                                                const int64_t* __restrict__ kv_off,
+                                                const int32_t* __restrict__ q_req,
+                                                const int32_t* __restrict__ q_pos, int64_t max_n) {
     int64_t n_row;
     if (n_valid) {
         n_row = n_valid[t];
@@ -224,7 +215,63 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         n_row = n_row < s_b ? n_row : s_b;
     }
     n_row = n_row < max_n ? n_row : max_n;
-    n_row = n_row > 0 ? n_row : 0;
+    return n_row > 0 ? n_row : 0;
+}
+
+// Rows selected by a persistent block (one per CU, looping over rows) have the first
+// kPreGroups load groups of every wave copied into LDS while the block still works on the
+// previous row: the row load (256 KB for 65536 elements) otherwise leaves the CU idle for
+// about half of a row's time.  The slices are wave-private (wave w copies exactly the 1 KB
+// groups it reads itself), so only the wave's own vmcnt / lgkmcnt waits order them.
+constexpr int kPreGroups = 8;  // 16 waves x 8 KB = 128 KB of LDS
+
+// Wait until this wave's LDS operations have completed (lgkmcnt 0, the other counters at
+// their maxima).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Copy this wave's prefetch groups of a row of n elements (only groups lying wholly inside
+// the row) into its LDS slices: group g of wave w holds positions 64E*w + 256g .. +255.
+template <int E>
+__device__ __forceinline__ void topk_prefetch(f32x4* pre, const float* row, int64_t n) {
+    int lane = lane_id();
+    __asm__ volatile("" : "+v"(lane));  // (recomputed per row, see topk_select)
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    wait_lgkmcnt0();  // the wave's reads of the slices (previous row) are done
+#pragma unroll
+    for (int g = 0; g < kPreGroups; ++g) {
+        const int64_t base = static_cast<int64_t>(wave) * 64 * E + 256 * g;
+        if (base + 256 <= n)
+            copy_to_lds<true>(row + base + 4 * lane, lds_offset(pre + (wave * kPreGroups + g) * 64));
+    }
+}
+
+// Selection of one row (kRow, kMerge) or part (kParts) by the whole block; ob is the output
+// row (the block's index without persistence).  PRE: pre_rd (or null) holds this row's
+// prefetched groups; the next row's groups (next_row, n_next; null if none) are copied into
+// the same slices as soon as this row's elements are in registers.
+template <int E, bool STREAM, bool VEC, int MODE, bool PRE>
+__device__ __forceinline__ void topk_select(
+    TopkSmem& sm, const int t, const int part, const int64_t ob,
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
+    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
+    const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids,
+    int32_t parts, int64_t chunk, const int32_t* __restrict__ cands,
+    f32x4* pre, bool pre_rd, const float* next_row, int64_t n_next) {
+    static_assert(E % 4 == 0, "elements come in groups of four consecutive positions");
+    static_assert(MODE != kMerge || !STREAM, "a merge holds its candidates in registers");
+    static_assert(!PRE || (MODE == kRow && !STREAM && VEC && E >= 4 * kPreGroups),
+                  "prefetch: register-resident rows with aligned 16-byte loads");
+    constexpr int kGroups = E / 4;
+    int tid = threadIdx.x;
+    int lane = lane_id();
+    // In the persistent row loop the per-lane address terms would be hoisted out of the loop
+    // and stay live (spilled) through the whole selection: make them opaque per row.
+    if constexpr (PRE) __asm__ volatile("" : "+v"(tid), "+v"(lane));
+    const int wave = PRE ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+
+    const int64_t n_row = topk_row_len(t, n_valid, kv_off, q_req, q_pos, max_n);
     int64_t n = n_row;  // elements this block selects from (element index p < n)
     if (MODE == kParts) {
         n = n_row - part * chunk;
@@ -233,9 +280,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     } else if (MODE == kMerge) {
         n = static_cast<int64_t>(parts) * kTopK;
     }
-    int32_t* out = ids + static_cast<int64_t>(blockIdx.x) * kTopK;
+    int32_t* out = ids + ob * kTopK;
     const int64_t n_short = MODE == kMerge ? n_row : n;
     if (n_short <= kTopK) {
+        if constexpr (PRE) topk_prefetch<E>(pre, next_row, n_next);
         for (int i = tid; i < kTopK; i += kTopkThreads) out[i] = i < n_short ? i : -1;
         return;
     }
@@ -259,6 +307,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
                     cpos[4 * g + c] = pos;
                     key[4 * g + c] = pos >= 0 ? score_key(row[pos]) : 0u;
                 }
+            } else if (PRE && g < kPreGroups && pre_rd &&
+                       static_cast<int64_t>(wave) * 64 * E + 256 * g + 256 <= n) {  // wave-uniform
+                const f32x4 v = pre[(wave * kPreGroups + g) * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) key[4 * g + c] = score_key(v[c]);
             } else if (VEC && p + 3 < n) {
                 const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + p));
 #pragma unroll
@@ -288,6 +341,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         uint32_t d0 = ~0u, d1 = 0u;
         block_minmax(sm, amin, amax, d0, d1);
     }
+    // Every wave's keys are in registers: the next row's copies now stream while this row is
+    // selected (issued earlier, they would compete with the slower waves' loads of this row).
+    if constexpr (PRE) topk_prefetch<E>(pre, next_row, n_next);
     amin += 1u;
     uint32_t fmin = amin, fmax = amax;
     if (amin <= kKeyNegInf || amax >= kKeyPosInf) {  // block-uniform
@@ -629,7 +685,44 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     // (scattered 4-byte stores straight to global memory measured slightly slower)
     lds_barrier();
 #pragma unroll
-    for (int i = tid; i < kTopK; i += kTopkThreads) out[i] = static_cast<int32_t>(sm.hist[i]);
+    for (int i = static_cast<int>(threadIdx.x); i < kTopK; i += kTopkThreads)
+        out[i] = static_cast<int32_t>(sm.hist[i]);
+}
+
+// One block per row (or part); PRE: a persistent grid of one block per CU, block b taking
+// rows b, b + grid, ... of the n_rows rows.
+template <int E, bool STREAM, bool VEC, int MODE, bool PRE>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
+    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
+    const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids,
+    int32_t parts, int64_t chunk, const int32_t* __restrict__ cands, int32_t n_rows) {
+    __shared__ TopkSmem sm;
+    if constexpr (!PRE) {
+        const int b = static_cast<int>(blockIdx.x);
+        const int t = MODE == kParts ? b / parts : b;
+        const int part = MODE == kParts ? b - t * parts : 0;
+        topk_select<E, STREAM, VEC, MODE, false>(sm, t, part, b, scores, ld, n_valid, kv_off,
+                                                 q_req, q_pos, max_n, ids, parts, chunk, cands,
+                                                 nullptr, false, nullptr, 0);
+    } else {
+        __shared__ f32x4 pre[kTopkWaves * kPreGroups * 64];
+        const int step = static_cast<int>(gridDim.x);
+        for (int t = static_cast<int>(blockIdx.x); t < n_rows; t += step) {
+            const bool has_pre = t != static_cast<int>(blockIdx.x);  // block-uniform
+            if (has_pre) {
+                wait_vmcnt<0>();                      // this wave's copies of row t have landed
+                __asm__ volatile("" ::: "memory");  // (no LDS read moves above the wait)
+                lds_barrier();                        // the previous row's last LDS reads are done
+            }
+            const int tn = t + step;
+            const float* next = tn < n_rows ? scores + static_cast<int64_t>(tn) * ld : nullptr;
+            const int64_t n_next = next ? topk_row_len(tn, n_valid, kv_off, q_req, q_pos, max_n) : 0;
+            topk_select<E, STREAM, VEC, MODE, true>(sm, t, 0, t, scores, ld, n_valid, kv_off,
+                                                    q_req, q_pos, max_n, ids, parts, chunk,
+                                                    cands, pre, has_pre, next, n_next);
+        }
+    }
 }
 
 template <int E, bool STREAM, int MODE>
@@ -638,13 +731,27 @@ static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, cons
                           int64_t max_n, int32_t* ids, int32_t parts, int64_t chunk,
                           const int32_t* cands, bool vec, hipStream_t stream) {
     if (vec)
-        hipLaunchKernelGGL((topk_kernel<E, STREAM, true, MODE>), dim3(blocks), dim3(kTopkThreads),
-                           0, stream, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids,
-                           parts, chunk, cands);
-    else
-        hipLaunchKernelGGL((topk_kernel<E, STREAM, false, MODE>), dim3(blocks),
+        hipLaunchKernelGGL((topk_kernel<E, STREAM, true, MODE, false>), dim3(blocks),
                            dim3(kTopkThreads), 0, stream, scores, ld, n_valid, kv_off, q_req,
-                           q_pos, max_n, ids, parts, chunk, cands);
+                           q_pos, max_n, ids, parts, chunk, cands, 0);
+    else
+        hipLaunchKernelGGL((topk_kernel<E, STREAM, false, MODE, false>), dim3(blocks),
+                           dim3(kTopkThreads), 0, stream, scores, ld, n_valid, kv_off, q_req,
+                           q_pos, max_n, ids, parts, chunk, cands, 0);
+}
+
+// Compute units of the current device (the persistent grid size), looked up once per device.
+static int device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 // One selection pass over rows (or parts) of at most `len` elements each.
@@ -661,7 +768,13 @@ static void launch_pass(unsigned blocks, int64_t len, const float* scores, int64
         launch_topk_e<16, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
     else if (len <= 32 * kTopkThreads)
         launch_topk_e<32, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
-    else if (len <= 64 * kTopkThreads)
+    else if (len <= 64 * kTopkThreads && MODE == kRow && vec) {
+        // persistent blocks with the next row's LDS prefetch (one block per CU)
+        const unsigned grid = std::min(blocks, static_cast<unsigned>(device_cus()));
+        hipLaunchKernelGGL((topk_kernel<64, false, true, kRow, true>), dim3(grid),
+                           dim3(kTopkThreads), 0, stream, scores, ld, n_valid, kv_off, q_req,
+                           q_pos, max_n, ids, parts, chunk, nullptr, static_cast<int32_t>(blocks));
+    } else if (len <= 64 * kTopkThreads)
         launch_topk_e<64, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
     else
         launch_topk_e<16, true, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);

@@ -206,6 +206,28 @@ def test_topk_bit_exact_long_rows(n, kind):
         assert np.array_equal(got[t], O.topk_ids(rows[t, :n_valid[t]])), f"row {t}"
 
 
+def test_topk_persistent_rows_bit_exact():
+    """More rows than CUs, each of up to 40000 elements: the selection runs one persistent
+    block per CU that prefetches its next row into LDS while selecting the current one.  Row
+    lengths of every class (empty, short, ragged, full) follow one another inside a block."""
+    print("[topk persistent] 600 rows", flush=True)
+    dsa = dsa_mod()
+    t_count, ld = 600, 40000
+    g = np.random.default_rng(31)
+    rows = np.concatenate([synth.score_rows_np(31, "gauss", t_count // 2, ld),
+                           synth.score_rows_np(32, "coarse", t_count - t_count // 2, ld)])
+    rows = rows[g.permutation(t_count)]
+    n_valid = g.integers(32769, ld + 1, size=t_count).astype(np.int32)
+    n_valid[::7] = g.integers(0, 2049, size=len(n_valid[::7]))
+    n_valid[3::11] = ld
+    n_valid[5::13] = g.integers(2049, 32769, size=len(n_valid[5::13]))
+    ids = dsa.topk(dev(rows), dev(n_valid), max_n=ld)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for t in range(t_count):
+        assert np.array_equal(got[t], O.topk_ids(rows[t, :n_valid[t]])), f"row {t} (n={n_valid[t]})"
+
+
 def check_selection(lay, ids, ref_scores):
     for t in range(lay.T):
         row = ids[t]
