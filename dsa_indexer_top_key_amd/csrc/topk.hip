@@ -7,9 +7,11 @@
 // positions.  Tie rule (the page is silent): equal scores go to the lower position, -0 ==
 // +0, NaN ranks lowest -- so the selected set, and the ascending ID row, are unique.
 //
-// One 1024-thread block per row.  Scores become order-preserving u32 keys (0 is reserved
-// for "no element"), kept in registers (E per thread, position e*1024 + tid) when the row
-// fits, re-streamed from global memory per pass otherwise.  Selection is a radix-style
+// One 1024-thread block per row; rows of 32769..65536 elements (the prefill case) run one
+// persistent block per CU instead, which copies half of its next row into LDS while it
+// selects the current one.  Scores become order-preserving u32 keys (0 is reserved for "no
+// element"), kept in registers (E per thread) when the row fits, re-streamed from global
+// memory per pass otherwise.  Selection is a radix-style
 // threshold search on an LDS histogram of 2048 bins:
 //   level 0  bins linear in the score value between the row's finite min and max (a
 //            monotone map, so whole bins are above / below the threshold; spreading the
