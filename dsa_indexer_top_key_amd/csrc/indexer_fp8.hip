@@ -160,6 +160,23 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) wr[mt][r] = bf16_to_f32(w[t * kIndexHeads + 16 * mt + 4 * g + r]);
 
+    // Head-weighted ReLU sum of a tile's 32 x 16 products, the four 16-lane rows reduced by
+    // the cross-row swaps (v_permlane16_swap, then v_permlane32_swap: lane l adds lane l ^ 16,
+    // then l ^ 32, on the VALU); row 0 holds key c's score.
+    auto epilogue = [&](const f32x4& a0, const f32x4& a1, int jj) {
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v += wr[0][r] * fmaxf(a0[r], 0.f) + wr[1][r] * fmaxf(a1[r], 0.f);
+        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                          false, false);
+        v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                          false, false);
+        v = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+        if (g == 0) sbuf[(wave + 4 * jj) * kF8Tile + c] = v;
+    };
+    // A tile's epilogue runs after the next tile's MFMAs are issued, so it overlaps them.
+    f32x4 pa0 = {0.f, 0.f, 0.f, 0.f}, pa1 = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < my_tiles; ++j) {
         // tile j landed once only the copies issued after it may be outstanding
         if (j + kF8Ring - 1 < my_tiles) {
@@ -186,13 +203,11 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8_kernel(
             a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], kf[s], a0, 0, 0, 0);
             a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], kf[s], a1, 0, 0, 0);
         }
-        float v = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v += wr[0][r] * fmaxf(a0[r], 0.f) + wr[1][r] * fmaxf(a1[r], 0.f);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (g == 0) sbuf[(wave + 4 * j) * kF8Tile + c] = v;
+        if (j > 0) epilogue(pa0, pa1, j - 1);
+        pa0 = a0;
+        pa1 = a1;
     }
+    if (my_tiles > 0) epilogue(pa0, pa1, my_tiles - 1);
     __syncthreads();
     float* srow = scores + static_cast<int64_t>(t) * ld + k0;
     const float* sc = kscale + row0;
