@@ -378,7 +378,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         float mx = sacc[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // scale > 0 keeps the order
+        // the two lane halves hold the head's two K-halves: v_permlane32_swap pairs lane l
+        // with lane l ^ 32 on the VALU (no LDS round trip)
+        const auto mxs = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                          false, false);
+        mx = fmaxf(__uint_as_float(mxs[0]), __uint_as_float(mxs[1])) * scale_log2;  // scale > 0 keeps the order
         m_seen = fmaxf(m_seen, mx);
         if (m_ref == -INFINITY) m_ref = mx;  // first tile of pass 0 (uniform per head)
         overflow |= mx > m_ref + 32.f;
@@ -466,7 +470,9 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     }
 
     // ---- epilogue: rows of O are heads 8(r/4) + 4hh + r%4 of this group
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const auto ls = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                     false, false);
+    const float l_tot = __uint_as_float(ls[0]) + __uint_as_float(ls[1]);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse2 = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;
     const int head0 = 32 * wave;
