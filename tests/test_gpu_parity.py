@@ -192,7 +192,8 @@ def test_topk_bit_exact_on_identical_scores(kind):
 
 @pytest.mark.parametrize("n,kind", [(32768, "gauss"), (32768, "special"), (65536, "gauss"),
                                     (65536, "ints"), (65536, "special"), (65536, "coarse"),
-                                    (40000, "coarse"), (50000, "heavy_tail"), (70001, "gauss"),
+                                    (40000, "coarse"), (40001, "gauss"), (33000, "coarse"),
+                                    (50000, "heavy_tail"), (70001, "gauss"),
                                     (70001, "two_valued"), (200000, "special")])
 def test_topk_bit_exact_long_rows(n, kind):
     print(f"[topk long] n={n} {kind}", flush=True)
