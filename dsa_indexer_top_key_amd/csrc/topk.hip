@@ -250,9 +250,11 @@ __device__ __forceinline__ void topk_prefetch(f32x4* pre, const float* row, int6
 }
 
 // Selection of one row (kRow, kMerge) or part (kParts) by the whole block; ob is the output
-// row (the block's index without persistence).  PRE: pre_rd (or null) holds this row's
-// prefetched groups; the next row's groups (next_row, n_next; null if none) are copied into
-// the same slices as soon as this row's elements are in registers.
+// row (the block's index without persistence).  PRE: when pre_rd, the LDS slices hold this
+// row's first kPreGroups groups, and when nxt_rd, nxt holds its later groups (register
+// loads issued during the previous row's compaction).  The next row's groups (next_row,
+// n_next; null if none) are copied into the slices as soon as this row's elements are in
+// registers, and loaded into nxt once they are in the selection bitmaps (*nxt_issued).
 template <int E, bool STREAM, bool VEC, int MODE, bool PRE>
 __device__ __forceinline__ void topk_select(
     TopkSmem& sm, const int t, const int part, const int64_t ob,
@@ -260,7 +262,8 @@ __device__ __forceinline__ void topk_select(
     const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
     const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids,
     int32_t parts, int64_t chunk, const int32_t* __restrict__ cands,
-    f32x4* pre, bool pre_rd, const float* next_row, int64_t n_next) {
+    f32x4* pre, bool pre_rd, const float* next_row, int64_t n_next, f32x4* nxt, bool nxt_rd,
+    bool* nxt_issued) {
     static_assert(E % 4 == 0, "elements come in groups of four consecutive positions");
     static_assert(MODE != kMerge || !STREAM, "a merge holds its candidates in registers");
     static_assert(!PRE || (MODE == kRow && !STREAM && VEC && E >= 4 * kPreGroups),
@@ -285,7 +288,10 @@ __device__ __forceinline__ void topk_select(
     int32_t* out = ids + ob * kTopK;
     const int64_t n_short = MODE == kMerge ? n_row : n;
     if (n_short <= kTopK) {
-        if constexpr (PRE) topk_prefetch<E>(pre, next_row, n_next);
+        if constexpr (PRE) {
+            topk_prefetch<E>(pre, next_row, n_next);
+            *nxt_issued = false;
+        }
         for (int i = tid; i < kTopK; i += kTopkThreads) out[i] = i < n_short ? i : -1;
         return;
     }
@@ -312,6 +318,11 @@ __device__ __forceinline__ void topk_select(
             } else if (PRE && g < kPreGroups && pre_rd &&
                        static_cast<int64_t>(wave) * 64 * E + 256 * g + 256 <= n) {  // wave-uniform
                 const f32x4 v = pre[(wave * kPreGroups + g) * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) key[4 * g + c] = score_key(v[c]);
+            } else if (PRE && g >= kPreGroups && nxt_rd &&
+                       static_cast<int64_t>(wave) * 64 * E + 256 * g + 256 <= n) {  // wave-uniform
+                const f32x4 v = nxt[PRE && g >= kPreGroups ? g - kPreGroups : 0];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) key[4 * g + c] = score_key(v[c]);
             } else if (VEC && p + 3 < n) {
@@ -561,6 +572,19 @@ __device__ __forceinline__ void topk_select(
                 if ((lane & 7) == 0) sm.bm[1][widx] = wt;
             }
         }
+        if constexpr (PRE) {
+            // the keys are in the bitmaps and their registers free: load the next row's groups
+            // that are not in LDS; they arrive during the ranking below
+#pragma unroll
+            for (int g = kPreGroups; g < kGroups; ++g) {
+                const int64_t base = static_cast<int64_t>(wave) * 64 * E + 256 * g;
+                // (assigned on every path, so no earlier value stays live through a row)
+                nxt[g - kPreGroups] = next_row && base + 256 <= n_next  // wave-uniform
+                    ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(next_row + base + 4 * lane))
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            *nxt_issued = true;
+        }
         lds_barrier();
         // this thread's words, in position order
         const int w0 = tid * kWpt;
@@ -706,23 +730,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         const int part = MODE == kParts ? b - t * parts : 0;
         topk_select<E, STREAM, VEC, MODE, false>(sm, t, part, b, scores, ld, n_valid, kv_off,
                                                  q_req, q_pos, max_n, ids, parts, chunk, cands,
-                                                 nullptr, false, nullptr, 0);
+                                                 nullptr, false, nullptr, 0, nullptr, false,
+                                                 nullptr);
     } else {
         __shared__ f32x4 pre[kTopkWaves * kPreGroups * 64];
+        f32x4 nxt[E / 4 - kPreGroups];  // the next row's later groups, loaded into registers
+        bool nxt_rd = false;
         const int step = static_cast<int>(gridDim.x);
         for (int t = static_cast<int>(blockIdx.x); t < n_rows; t += step) {
             const bool has_pre = t != static_cast<int>(blockIdx.x);  // block-uniform
             if (has_pre) {
-                wait_vmcnt<0>();                      // this wave's copies of row t have landed
+                wait_vmcnt<0>();                      // this wave's copies (and loads) of row t have landed
                 __asm__ volatile("" ::: "memory");  // (no LDS read moves above the wait)
                 lds_barrier();                        // the previous row's last LDS reads are done
             }
             const int tn = t + step;
             const float* next = tn < n_rows ? scores + static_cast<int64_t>(tn) * ld : nullptr;
             const int64_t n_next = next ? topk_row_len(tn, n_valid, kv_off, q_req, q_pos, max_n) : 0;
+            bool issued = false;
             topk_select<E, STREAM, VEC, MODE, true>(sm, t, 0, t, scores, ld, n_valid, kv_off,
                                                     q_req, q_pos, max_n, ids, parts, chunk,
-                                                    cands, pre, has_pre, next, n_next);
+                                                    cands, pre, has_pre, next, n_next, nxt,
+                                                    has_pre && nxt_rd, &issued);
+            nxt_rd = issued;
         }
     }
 }
