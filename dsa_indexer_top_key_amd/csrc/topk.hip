@@ -814,9 +814,9 @@ static void launch_pass(unsigned blocks, int64_t len, const float* scores, int64
 
 // Parts per row for the two-stage selection: rows are split while fewer than 256 blocks
 // would run (one block per CU) and every part keeps at least 65536 elements; at most 16
-// parts.  A selection pass has a large fixed cost (about 25 us for a 32768-element row,
-// mostly barriers and dependent LDS round trips), so splitting shorter rows measured slower
-// (two passes of 8192 elements took longer than one pass of 32768).
+// parts.  A selection pass has a large fixed cost (block-wide scans, barriers and dependent
+// LDS round trips), so splitting shorter rows measured slower: 64 rows of 32768 in four parts
+// of 8192 plus the merge took 12 us longer than one pass per row.
 int topk_parts(int32_t T, int64_t max_n) {
     int p = 1;
     while (p < 16 && static_cast<int64_t>(T) * p < 256 && max_n >= static_cast<int64_t>(p) * 2 * 65536) p *= 2;
