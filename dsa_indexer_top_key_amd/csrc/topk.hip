@@ -9,7 +9,7 @@
 //
 // One 1024-thread block per row; rows of 32769..65536 elements (the prefill case) run one
 // persistent block per CU instead, which copies half of its next row into LDS while it
-// selects the current one.  Scores become order-preserving u32 keys (0 is reserved for "no
+// selects the current one and loads the other half into registers during the compaction.  Scores become order-preserving u32 keys (0 is reserved for "no
 // element"), kept in registers (E per thread) when the row fits, re-streamed from global
 // memory per pass otherwise.  Selection is a radix-style
 // threshold search on an LDS histogram of 2048 bins:
