@@ -22,6 +22,8 @@
 // final compaction is an ordered scan (wave ballot + mbcnt within a wave, an LDS scan of the
 // per-(element, wave) counts across the block) that writes the selected positions in
 // ascending order; ties at the threshold key are ranked by position with the same scan.
+#include <atomic>
+
 #include "common.h"
 
 namespace dsa {
@@ -772,18 +774,19 @@ static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, cons
                            q_pos, max_n, ids, parts, chunk, cands, 0);
 }
 
-// Compute units of the current device (the persistent grid size), looked up once per device.
+// Compute units of the current device (the persistent grid size), looked up once per device
+// (threads that race on the first lookup store the same value).
 static int device_cus() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] <= 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // One selection pass over rows (or parts) of at most `len` elements each.
