@@ -296,6 +296,35 @@ def test_indexer_topk_prefill():
     check_selection(lay, ids.cpu().numpy(), ref)
 
 
+def test_indexer_topk_persistent_prefill_chunk():
+    """600 chunk queries in two requests, rows of 35,701..40,000 admissible positions: more
+    rows than CUs, so the selection runs the persistent blocks with row lengths taken from
+    kv_off / q_req / q_pos.  The fused selection equals the standalone one over the same
+    scores (explicit lengths) bit for bit, and sampled queries match the oracle."""
+    print("[indexer_topk] persistent prefill chunk", flush=True)
+    dsa = dsa_mod()
+    q_req = np.repeat(np.arange(2, dtype=np.int32), 300)
+    q_pos = np.concatenate([39700 + np.arange(300), 35700 + np.arange(300)]).astype(np.int32)
+    lay = synth.Layout("ppc", 33, [40000, 36000], q_req, q_pos)
+    d, keys = idx_inputs(lay, 33)
+    args = (dev(d["q_idx"]), dev(d["w"]), dev(keys), dev(lay.kv_off), dev(lay.q_req),
+            dev(lay.q_pos), lay.max_s)
+    ids = dsa.indexer_topk(*args)
+    scores = dsa.indexer_scores(*args)
+    n_valid = np.minimum(lay.q_pos + 1, lay.s_len[lay.q_req]).astype(np.int32)
+    ids2 = dsa.topk(scores, dev(n_valid), max_n=lay.max_s)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    got = ids.cpu().numpy()
+    for t in (0, 299, 300, 599):
+        b = int(lay.q_req[t])
+        lo, hi = int(lay.kv_off[b]), int(lay.kv_off[b + 1])
+        one = synth.Layout("ppc1", 33, [hi - lo], np.zeros(1, np.int32), lay.q_pos[t:t + 1])
+        ref = O.indexer_scores(d["q_idx"][t:t + 1], d["w"][t:t + 1], keys[lo:hi], one.kv_off,
+                               one.q_req, one.q_pos)
+        check_selection(one, got[t:t + 1], ref)
+
+
 # ---------------------------------------------------------------------------------------
 # stage 4
 # ---------------------------------------------------------------------------------------
