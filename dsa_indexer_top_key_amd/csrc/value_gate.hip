@@ -21,8 +21,7 @@
 // tile a wave runs 32 v_mfma_f32_32x32x16_bf16 (A = query rows of o from LDS at a 1040-byte
 // row stride, bank-conflict-free), applies the gate to the fp32 sums (sigmoid in fp32) and
 // stores bf16 (round to nearest even).  Block index = split x 96 + h, so all blocks of a head
-// run on one XCD (96 is a multiple of 8) and share W_UV[h] in its L2.  Up to 64 queries the
-// blocks split the value columns instead (see value_gate_kernel).
+// run on one XCD (96 is a multiple of 8) and share W_UV[h] in its L2.
 #include "common.h"
 
 namespace dsa {
@@ -34,11 +33,6 @@ constexpr int kVgCopies = 8 + 2;        // copies per wave and tile: 8 rows of o
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
-// SMALL (T <= 64, at most two query tiles): one block per (head, half of the value columns)
-// instead, so a block loads only 64 KB of W_UV: its four waves stage both tiles (the same
-// copies as above, one slot per tile), then wave w computes tile w / 2 for column group
-// 2 half + w % 2.
-template <bool SMALL>
 __global__ __launch_bounds__(256, 1) void value_gate_kernel(const uint16_t* __restrict__ o,
                                                             const uint16_t* __restrict__ w_uv,
                                                             const uint16_t* __restrict__ gate,
@@ -48,18 +42,17 @@ __global__ __launch_bounds__(256, 1) void value_gate_kernel(const uint16_t* __re
     __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][kVgRows * kVgStride];
     __shared__ __attribute__((aligned(16))) uint16_t g_lds[2][kVgRows * kValueDim];
     const int h = static_cast<int>(blockIdx.x) % kMlaHeads;
-    const int split = static_cast<int>(blockIdx.x) / kMlaHeads;  // SMALL: the column half
-    const int tt0 = SMALL ? 0 : static_cast<int>(static_cast<int64_t>(n_tiles) * split / n_split);
-    const int tt1 = SMALL ? n_tiles : static_cast<int>(static_cast<int64_t>(n_tiles) * (split + 1) / n_split);
+    const int split = static_cast<int>(blockIdx.x) / kMlaHeads;
+    const int tt0 = static_cast<int>(static_cast<int64_t>(n_tiles) * split / n_split);
+    const int tt1 = static_cast<int>(static_cast<int64_t>(n_tiles) * (split + 1) / n_split);
     const int lane = lane_id();
-    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave: copy role
-    const int cc = SMALL ? 2 * split + (cg & 1) : cg;                 // column group computed
+    const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave = column group
     const int r = lane & 31;
     const int hh = lane >> 5;
-    // this wave's W_UV rows: B operand of K-step s is dims 16 s + 8 hh .. +8 of row 32 cc + r
+    // this wave's W_UV rows: B operand of K-step s is dims 16 s + 8 hh .. +8 of row 32 cg + r
     u32x4 bw[kLatent / 16];
     {
-        const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kValueDim + 32 * cc + r) * kLatent + 8 * hh;
+        const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kValueDim + 32 * cg + r) * kLatent + 8 * hh;
 #pragma unroll
         for (int s = 0; s < kLatent / 16; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
     }
@@ -83,29 +76,6 @@ __global__ __launch_bounds__(256, 1) void value_gate_kernel(const uint16_t* __re
                         lds_offset(g_lds[b] + (8 * cg + 4 * k) * kValueDim));
         }
     };
-    if constexpr (SMALL) {
-        for (int tt = 0; tt < n_tiles; ++tt) stage(tt, tt);  // n_tiles <= 2
-        wait_vmcnt<0>();
-        __syncthreads();  // every wave's copies are in
-        const int tt = cg >> 1;
-        if (tt >= n_tiles) return;  // T <= 32: waves 2 and 3 have no tile
-        const uint16_t* ap = a_lds[tt] + r * kVgStride + 8 * hh;
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < kLatent / 16; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(*reinterpret_cast<const u32x4*>(ap + 16 * s)), as_bf16x8(bw[s]), acc, 0, 0, 0);
-        const int t0 = tt * kVgRows;
-        float v[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = 8 * (e >> 2) + 4 * hh + (e & 3);
-            v[e] = acc[e] * sigmoidf_(bf16_to_f32(g_lds[tt][row * kValueDim + 32 * cc + r]));
-        }
-        store_tile_bf16(out + (static_cast<int64_t>(t0) * kMlaHeads + h) * kValueDim,
-                        kMlaHeads * kValueDim, 0, 32 * cc, v, lane, T - t0);
-        return;
-    }
     if (tt0 < tt1) stage(tt0, 0);
     for (int tt = tt0; tt < tt1; ++tt) {
         const int b = (tt - tt0) & 1;
@@ -143,13 +113,8 @@ hipError_t launch_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint
     const int n_tiles = (T + kVgRows - 1) / kVgRows;
     // splits per head: up to 8 (768 blocks: three rounds of one block per CU), at most one
     // per tile
-    if (n_tiles <= 2) {  // T <= 64: two blocks per head, each half of the value columns
-        hipLaunchKernelGGL(value_gate_kernel<true>, dim3(static_cast<unsigned>(kMlaHeads * 2)),
-                           dim3(256), 0, stream, o, w_uv, gate, T, n_tiles, 2, out);
-        return hipGetLastError();
-    }
     const int n_split = n_tiles < 8 ? n_tiles : 8;
-    hipLaunchKernelGGL(value_gate_kernel<false>, dim3(static_cast<unsigned>(kMlaHeads * n_split)), dim3(256),
+    hipLaunchKernelGGL(value_gate_kernel, dim3(static_cast<unsigned>(kMlaHeads * n_split)), dim3(256),
                        0, stream, o, w_uv, gate, T, n_tiles, n_split, out);
     return hipGetLastError();
 }
