@@ -718,7 +718,8 @@ __device__ __forceinline__ void topk_select(
 }
 
 // One block per row (or part); PRE: a persistent grid of one block per CU, block b taking
-// rows b, b + grid, ... of the n_rows rows.
+// rows b, b + grid, ... of the n_rows rows.  No block waits for another, so results do not
+// depend on how many blocks are resident at once.
 template <int E, bool STREAM, bool VEC, int MODE, bool PRE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
