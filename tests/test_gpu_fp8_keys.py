@@ -157,6 +157,35 @@ def test_indexer_topk_fp8_matches_standalone_topk_and_oracle():
         assert diff <= set(O.selection_band(ref[t]).tolist()), f"query {t}"
 
 
+def test_indexer_topk_fp8_long_rows_many_queries():
+    """300 chunk queries with 33,001..33,300 admissible positions (more rows than CUs, so the
+    persistent selection): the FP8 selection equals the standalone top-k of the FP8 scores bit
+    for bit, and sampled queries match the oracle over the same codes."""
+    print("[fp8] indexer_topk long rows", flush=True)
+    dsa = dsa_mod()
+    lay = synth.prefill_layout("f8p2", 17, 33300, 33000, 300)
+    d = synth.inputs_np(lay, parts=("index",))
+    keys = synth.bf16_bits_from_f32(np.random.default_rng(17).standard_normal((lay.N, 128)))
+    codes, scales = quantize(keys)
+    args = (dev(d["q_idx"]), dev(d["w"]), dev(codes), dev(scales), dev(lay.kv_off),
+            dev(lay.q_req), dev(lay.q_pos))
+    ids = dsa.indexer_topk_fp8(*args, lay.max_s)
+    scores = dsa.indexer_scores_fp8(*args, lay.max_s)
+    n_valid = np.minimum(lay.q_pos + 1, lay.s_len[lay.q_req]).astype(np.int32)
+    ids2 = dsa.topk(scores, dev(n_valid), max_n=lay.max_s)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    got = ids.cpu().numpy()
+    for t in (0, 150, 299):
+        one = synth.Layout("f8p2one", 17, [lay.N], np.zeros(1, np.int32), lay.q_pos[t:t + 1])
+        ref = O.indexer_scores_fp8(d["q_idx"][t:t + 1], d["w"][t:t + 1], codes, scales,
+                                   one.kv_off, one.q_req, one.q_pos)[0]
+        valid = got[t][got[t] >= 0]
+        assert len(valid) == 2048 and np.all(got[t][2048:] == -1)
+        diff = set(valid.tolist()) ^ set(O.topk_ids(ref)[:2048].tolist())
+        assert diff <= set(O.selection_band(ref).tolist()), f"query {t}"
+
+
 def test_fp8_full_size_decode_sampled():
     """The 64 x 32768 decode batch: LayerNorm keys quantised on the GPU, the FP8 selection of
     sampled queries against the oracle over the same codes."""
