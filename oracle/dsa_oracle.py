@@ -17,8 +17,6 @@ closed forms, library routines, brute force or the page's printed arithmetic.
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 # ----------------------------------------------------------------------------------------
@@ -165,21 +163,6 @@ def indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, rows=None):
         k_seg = keys[kv_off[b]: kv_off[b] + n]
         k_rows = bf16_to_f64(k_seg) if k_seg.dtype == np.uint16 else k_seg.astype(np.float64)
         out.append(indexer_scores_one(bf16_to_f64(q_idx[t]), bf16_to_f64(w[t]), k_rows))
-    return out
-
-
-def indexer_score_magnitude(q_idx, w, keys, kv_off, q_req, q_pos, rows=None):
-    """Condition magnitude  sum_h |w_th| * ReLU(q_th . k_j)  per admissible position."""
-    q_idx = np.asarray(q_idx)
-    kv_off = np.asarray(kv_off, dtype=np.int64)
-    s_len = request_lengths(kv_off)
-    out = []
-    for t in (range(q_idx.shape[0]) if rows is None else rows):
-        b = int(q_req[t])
-        n = admissible_count(q_pos[t], s_len[b])
-        k_rows = bf16_to_f64(np.asarray(keys)[kv_off[b]: kv_off[b] + n])
-        logits = bf16_to_f64(q_idx[t]) @ k_rows.T
-        out.append(np.abs(bf16_to_f64(np.asarray(w)[t])) @ np.maximum(logits, 0.0))
     return out
 
 
@@ -541,7 +524,3 @@ def payload_bytes_at(tokens: int, layers: int = GLOBAL_LAYERS) -> int:
 def selection_fraction(k: int = TOPK, context: int = CONTEXT_LIMIT) -> float:
     return k / context
 
-
-def attention_scale(qk_head_dim: int = 192) -> float:
-    """Softmax scale 1/sqrt(192) of the main attention (used as given by the caller)."""
-    return 1.0 / math.sqrt(qk_head_dim)
