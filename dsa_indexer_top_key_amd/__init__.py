@@ -101,11 +101,65 @@ def _torch():
     return torch
 
 
-def _dev(x, name):
+def _tensor(x, name):
     torch = _torch()
-    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
-        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     return x
+
+
+def _spec(x, name, dtypes, shape=None, contiguous=True):
+    """Validate one tensor argument: its dtype (one of `dtypes`), its shape (a tuple whose
+    None entries match any size; None = any shape) and its layout (densely packed when
+    `contiguous`).  Raises TypeError (dtype) or ValueError (shape, layout) before anything is
+    launched: the C ABI sees only pointers, so a wrong shape here would become an
+    out-of-bounds device access.  Where the tensors live is checked last, for all of a call's
+    tensors at once (_same_device)."""
+    _tensor(x, name)
+    if x.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, "
+                        f"got {x.dtype}")
+    if shape is not None:
+        if x.dim() != len(shape) or any(w is not None and int(n) != w for n, w in zip(x.shape, shape)):
+            want = ", ".join("*" if w is None else str(w) for w in shape)
+            raise ValueError(f"{name} must have shape [{want}], got {list(x.shape)}")
+    if contiguous and not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return x
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _bits16(x, name, shape=None):
+    """A densely packed bf16 tensor (bfloat16 or 16-bit bit patterns) on the GPU."""
+    return _spec(x, name, _bf16_types(), shape)
+
+
+def _same_device(*xs):
+    """Every given tensor on the GPU, all on one device (the last check before a call)."""
+    xs = [x for x in xs if x is not None]
+    for x in xs:
+        if x.device.type != "cuda":
+            raise TypeError(f"every tensor argument must be a torch tensor on the GPU "
+                            f"(one of shape {list(x.shape)} is on {x.device})")
+    devs = {x.device for x in xs}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(str(d) for d in devs)}")
+
+
+def _workspace(ws, need, name="workspace"):
+    """A caller-given workspace: a densely packed GPU tensor of at least `need` bytes."""
+    if ws is None:
+        return None
+    _tensor(ws, name)
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"{name} holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+    return ws
 
 
 def _ptr(x):
@@ -118,20 +172,6 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _bits16(x, name):
-    torch = _torch()
-    _dev(x, name)
-    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise TypeError(f"{name} must hold bf16 values (bfloat16 or 16-bit bit patterns)")
-    return x
-
-
-def _contig(x, name):
-    if not x.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    return x
-
-
 def _rows_ld(x, name, width):
     """Row stride (elements) of a 2-D view whose rows hold at least `width` elements."""
     if x.dim() != 2 or x.stride(1) != 1 or x.shape[1] < width:
@@ -142,54 +182,87 @@ def _rows_ld(x, name, width):
 def index_keys_layernorm(raw, gamma, beta, eps: float = 1e-6, keys=None, stream=None):
     """Stage 1: raw [N,128] float32 -> LayerNormed bf16 keys [N,128]."""
     torch = _torch()
-    _contig(_dev(raw, "raw"), "raw")
+    _spec(raw, "raw", (torch.float32,), (None, INDEX_DIM))
     n = raw.shape[0]
+    _spec(gamma, "gamma", (torch.float32,), (INDEX_DIM,))
+    _spec(beta, "beta", (torch.float32,), (INDEX_DIM,))
     if keys is None:
         keys = torch.empty((n, INDEX_DIM), dtype=torch.bfloat16, device=raw.device)
+    _bits16(keys, "keys", (n, INDEX_DIM))
+    _same_device(raw, gamma, beta, keys)
     _check("dsa_index_keys_layernorm", library().dsa_index_keys_layernorm(
-        _ptr(raw), _ptr(_contig(_dev(gamma, "gamma"), "gamma")),
-        _ptr(_contig(_dev(beta, "beta"), "beta")), float(eps), _ptr(_contig(keys, "keys")), n,
-        _stream(stream)))
+        _ptr(raw), _ptr(gamma), _ptr(beta), float(eps), _ptr(keys), n, _stream(stream)))
     return keys
 
 
-def _layout(kv_off, q_req, q_pos):
-    for x, n in ((kv_off, "kv_off"), (q_req, "q_req"), (q_pos, "q_pos")):
-        _contig(_dev(x, n), n)
+def _layout(kv_off, q_req, q_pos, t):
+    """Request layout of t queries: kv_off [B+1] int64, q_req and q_pos [t] int32; returns B."""
     torch = _torch()
-    if kv_off.dtype != torch.int64 or q_req.dtype != torch.int32 or q_pos.dtype != torch.int32:
-        raise TypeError("kv_off must be int64, q_req and q_pos int32")
+    _spec(kv_off, "kv_off", (torch.int64,), (None,))
+    if kv_off.shape[0] < 2:
+        raise ValueError("kv_off must hold B + 1 >= 2 row offsets")
+    _spec(q_req, "q_req", (torch.int32,), (t,))
+    if q_pos is not None:
+        _spec(q_pos, "q_pos", (torch.int32,), (t,))
     return kv_off.shape[0] - 1
+
+
+def _index_queries(q_idx, w):
+    """q_idx [T,32,128] and w [T,32] bf16; returns T."""
+    _bits16(q_idx, "q_idx", (None, INDEX_HEADS, INDEX_DIM))
+    t = q_idx.shape[0]
+    _bits16(w, "w", (t, INDEX_HEADS))
+    return t
+
+
+def _ids(ids, t, k, device):
+    torch = _torch()
+    if ids is None:
+        ids = torch.empty((t, k), dtype=torch.int32, device=device)
+    return _spec(ids, "ids", (torch.int32,), (t, k))
+
+
+def _score_rows(scores, t, max_s, name="scores"):
+    """A row-major float32 [t, >= max_s] view (rows may be padded); returns its row stride."""
+    torch = _torch()
+    _spec(scores, name, (torch.float32,), (t, None), contiguous=False)
+    if scores.stride(1) != 1 or scores.shape[1] < max_s or (t > 1 and scores.stride(0) < max_s):
+        raise ValueError(f"{name} must be a row-major float32 [T, >= {max_s}] view")
+    return scores.stride(0)
 
 
 def indexer_scores(q_idx, w, keys, kv_off, q_req, q_pos, max_s: int, scores=None, stream=None):
     """Stage 2 alone: fp32 scores [T, max_s]; entries j >= n_t are left untouched."""
     torch = _torch()
-    b = _layout(kv_off, q_req, q_pos)
-    t = q_idx.shape[0]
+    t = _index_queries(q_idx, w)
+    b = _layout(kv_off, q_req, q_pos, t)
+    _bits16(keys, "keys", (None, INDEX_DIM))
     if scores is None:
         scores = torch.full((t, max_s), float("nan"), dtype=torch.float32, device=q_idx.device)
+    ld = _score_rows(scores, t, int(max_s))
+    _same_device(q_idx, w, keys, kv_off, q_req, q_pos, scores)
     _check("dsa_indexer_scores", library().dsa_indexer_scores(
-        _ptr(_contig(_bits16(q_idx, "q_idx"), "q_idx")), _ptr(_contig(_bits16(w, "w"), "w")),
-        _ptr(_contig(_bits16(keys, "keys"), "keys")), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t,
-        b, int(max_s), q_idx.shape[1], q_idx.shape[2], _ptr(scores), scores.stride(0),
-        _stream(stream)))
+        _ptr(q_idx), _ptr(w), _ptr(keys), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b,
+        int(max_s), INDEX_HEADS, INDEX_DIM, _ptr(scores), ld, _stream(stream)))
     return scores
 
 
 def topk(scores, n_valid, k: int = TOPK, max_n=None, ids=None, stream=None):
     """Stage 3 alone: canonical top-k column IDs of fp32 score rows."""
     torch = _torch()
-    _dev(scores, "scores")
-    if scores.dim() != 2 or scores.stride(1) != 1 or scores.dtype != torch.float32:
-        raise ValueError("scores must be a row-major float32 [T, ld] tensor")
-    _contig(_dev(n_valid, "n_valid"), "n_valid")
+    _tensor(scores, "scores")
+    if scores.dim() != 2:
+        raise ValueError("scores must be a 2-D float32 [T, ld] tensor")
     t = scores.shape[0]
     max_n = scores.shape[1] if max_n is None else int(max_n)
-    if ids is None:
-        ids = torch.empty((t, k), dtype=torch.int32, device=scores.device)
-    _check("dsa_topk", library().dsa_topk(_ptr(scores), scores.stride(0), _ptr(n_valid), t, max_n,
-                                          k, _ptr(_contig(ids, "ids")), _stream(stream)))
+    if max_n > scores.shape[1]:
+        raise ValueError(f"max_n={max_n} exceeds the {scores.shape[1]} columns of scores")
+    ld = _score_rows(scores, t, max_n)
+    _spec(n_valid, "n_valid", (torch.int32,), (t,))
+    ids = _ids(ids, t, k, scores.device)
+    _same_device(scores, n_valid, ids)
+    _check("dsa_topk", library().dsa_topk(_ptr(scores), ld, _ptr(n_valid), t, max_n, k,
+                                          _ptr(ids), _stream(stream)))
     return ids
 
 
@@ -201,23 +274,46 @@ def indexer_topk(q_idx, w, keys, kv_off, q_req, q_pos, max_s: int, k: int = TOPK
                  workspace=None, stream=None):
     """Stages 2+3: [T,2048] request-local position IDs (ascending, -1 padded)."""
     torch = _torch()
-    b = _layout(kv_off, q_req, q_pos)
-    t = q_idx.shape[0]
-    if ids is None:
-        ids = torch.empty((t, k), dtype=torch.int32, device=q_idx.device)
+    t = _index_queries(q_idx, w)
+    b = _layout(kv_off, q_req, q_pos, t)
+    _bits16(keys, "keys", (None, INDEX_DIM))
+    ids = _ids(ids, t, k, q_idx.device)
     need = indexer_topk_workspace_size(t, max_s)
+    _workspace(workspace, need)
+    _same_device(q_idx, w, keys, kv_off, q_req, q_pos, ids, workspace)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_idx.device)
     _check("dsa_indexer_topk", library().dsa_indexer_topk(
-        _ptr(_contig(_bits16(q_idx, "q_idx"), "q_idx")), _ptr(_contig(_bits16(w, "w"), "w")),
-        _ptr(_contig(_bits16(keys, "keys"), "keys")), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t,
-        b, int(max_s), q_idx.shape[1], q_idx.shape[2], k, _ptr(_contig(ids, "ids")),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(q_idx), _ptr(w), _ptr(keys), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b,
+        int(max_s), INDEX_HEADS, INDEX_DIM, k, _ptr(ids), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return ids
 
 
 def sparse_mla_workspace_size(t: int, n_heads: int = MLA_HEADS, k: int = TOPK) -> int:
     return int(library().dsa_sparse_mla_workspace_size(t, n_heads, k))
+
+
+def _mla_args(q, latent, kpe, kv_off, q_req, ids, out, lse, out_dtype, latent_name="latent",
+              kpe_name="kpe"):
+    """Checks shared by the contiguous and paged reads; returns (T, B, ld_lat, ld_kpe, out, lse)."""
+    torch = _torch()
+    _bits16(q, "q", (None, MLA_HEADS, QK_DIM))
+    t = q.shape[0]
+    _spec(latent, latent_name, _bf16_types(), (None, None), contiguous=False)
+    _spec(kpe, kpe_name, _bf16_types(), (None, None), contiguous=False)
+    ld_lat = _rows_ld(latent, latent_name, LATENT_DIM)
+    ld_kpe = _rows_ld(kpe, kpe_name, COMPANION_DIM)
+    b = _layout(kv_off, q_req, None, t)
+    _spec(ids, "ids", (torch.int32,), (t, TOPK))
+    if out is None:
+        out = torch.empty((t, MLA_HEADS, LATENT_DIM), dtype=out_dtype or torch.bfloat16,
+                          device=q.device)
+    _spec(out, "out", (torch.bfloat16, torch.float32), (t, MLA_HEADS, LATENT_DIM))
+    if lse is None:
+        lse = torch.empty((t, MLA_HEADS), dtype=torch.float32, device=q.device)
+    _spec(lse, "lse", (torch.float32,), (t, MLA_HEADS))
+    return t, b, ld_lat, ld_kpe, out, lse
 
 
 def sparse_mla_attn(q, latent, kpe, kv_off, q_req, ids, scale: float, out=None, lse=None,
@@ -226,30 +322,18 @@ def sparse_mla_attn(q, latent, kpe, kv_off, q_req, ids, scale: float, out=None, 
 
     out is bfloat16 unless out_dtype=torch.float32 (or a float32 `out` is passed)."""
     torch = _torch()
-    _contig(_bits16(q, "q"), "q")
-    _bits16(latent, "latent")
-    _bits16(kpe, "kpe")
-    ld_lat = _rows_ld(latent, "latent", LATENT_DIM)
-    ld_kpe = _rows_ld(kpe, "kpe", COMPANION_DIM)
-    b = kv_off.shape[0] - 1
-    for x, n in ((kv_off, "kv_off"), (q_req, "q_req"), (ids, "ids")):
-        _contig(_dev(x, n), n)
-    t, h = q.shape[0], q.shape[1]
-    if out is None:
-        out = torch.empty((t, h, LATENT_DIM), dtype=out_dtype or torch.bfloat16, device=q.device)
-    if out.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out must be bfloat16 or float32")
-    out_code = 1 if out.dtype == torch.float32 else 0
-    if lse is None:
-        lse = torch.empty((t, h), dtype=torch.float32, device=q.device)
-    need = sparse_mla_workspace_size(t, h, ids.shape[1] if ids.dim() == 2 else TOPK)
+    t, b, ld_lat, ld_kpe, out, lse = _mla_args(q, latent, kpe, kv_off, q_req, ids, out, lse,
+                                               out_dtype)
+    need = sparse_mla_workspace_size(t)
+    _workspace(workspace, need)
+    _same_device(q, latent, kpe, kv_off, q_req, ids, out, lse, workspace)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_sparse_mla_attn", library().dsa_sparse_mla_attn(
         _ptr(q), _ptr(latent), ld_lat, _ptr(kpe), ld_kpe, _ptr(kv_off), _ptr(q_req), _ptr(ids), t,
-        b, h, ids.shape[1], float(scale), _ptr(_contig(out, "out")), out_code, _ptr(lse),
-        _ptr(workspace), ws_bytes, _stream(stream)))
+        b, MLA_HEADS, TOPK, float(scale), _ptr(out), 1 if out.dtype == torch.float32 else 0,
+        _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
 
 
@@ -258,16 +342,16 @@ def value_gate(o, w_uv, gate, out=None, stream=None):
     w_uv [96,128,512] bf16, gate [T,96,128] bf16 logits -> out [T,96,128] bf16 with
     out[t,h] = (w_uv[h] @ o[t,h]) * sigmoid(gate[t,h])."""
     torch = _torch()
-    for x, n in ((o, "o"), (w_uv, "w_uv"), (gate, "gate")):
-        _contig(_bits16(_dev(x, n), n), n)
-    t, h = o.shape[0], o.shape[1]
-    if tuple(o.shape[1:]) != (h, LATENT_DIM) or tuple(w_uv.shape) != (h, VALUE_DIM, LATENT_DIM) \
-            or tuple(gate.shape) != (t, h, VALUE_DIM):
-        raise ValueError("value_gate expects o [T,H,512], w_uv [H,128,512], gate [T,H,128]")
+    _bits16(o, "o", (None, MLA_HEADS, LATENT_DIM))
+    t = o.shape[0]
+    _bits16(w_uv, "w_uv", (MLA_HEADS, VALUE_DIM, LATENT_DIM))
+    _bits16(gate, "gate", (t, MLA_HEADS, VALUE_DIM))
     if out is None:
-        out = torch.empty((t, h, VALUE_DIM), dtype=torch.bfloat16, device=o.device)
+        out = torch.empty((t, MLA_HEADS, VALUE_DIM), dtype=torch.bfloat16, device=o.device)
+    _bits16(out, "out", (t, MLA_HEADS, VALUE_DIM))
+    _same_device(o, w_uv, gate, out)
     _check("dsa_value_gate", library().dsa_value_gate(
-        _ptr(o), _ptr(w_uv), _ptr(gate), t, h, _ptr(_contig(out, "out")), _stream(stream)))
+        _ptr(o), _ptr(w_uv), _ptr(gate), t, MLA_HEADS, _ptr(out), _stream(stream)))
     return out
 
 
@@ -282,56 +366,54 @@ def indexer_project(c_q, h, w_qi, w_k, w_w, gamma, beta, eps: float, keys, key_r
     Returns (q_idx [T,32,128], w [T,32]) bf16 and writes LayerNorm(w_k h[t]) as bf16 into row
     key_rows[t] (int64, absolute) of the index-key cache `keys` [rows,128]."""
     torch = _torch()
-    for x, n in ((c_q, "c_q"), (h, "h"), (w_qi, "w_qi"), (w_k, "w_k"), (w_w, "w_w"),
-                 (keys, "keys")):
-        _contig(_bits16(_dev(x, n), n), n)
-    for x, n in ((gamma, "gamma"), (beta, "beta"), (key_rows, "key_rows")):
-        _contig(_dev(x, n), n)
+    _bits16(c_q, "c_q", (None, Q_LATENT))
     t = c_q.shape[0]
-    if tuple(c_q.shape) != (t, Q_LATENT) or tuple(h.shape) != (t, RESIDUAL) \
-            or tuple(w_qi.shape) != (INDEX_HEADS * INDEX_DIM, Q_LATENT) \
-            or tuple(w_k.shape) != (INDEX_DIM, RESIDUAL) or tuple(w_w.shape) != (INDEX_HEADS, RESIDUAL) \
-            or keys.dim() != 2 or keys.shape[1] != INDEX_DIM or tuple(key_rows.shape) != (t,):
-        raise ValueError("indexer_project expects c_q [T,1536], h [T,7168], w_qi [4096,1536], "
-                         "w_k [128,7168], w_w [32,7168], keys [rows,128], key_rows [T]")
-    if key_rows.dtype != torch.int64 or gamma.dtype != torch.float32 or beta.dtype != torch.float32:
-        raise TypeError("key_rows must be int64, gamma and beta float32")
+    _bits16(h, "h", (t, RESIDUAL))
+    _bits16(w_qi, "w_qi", (INDEX_HEADS * INDEX_DIM, Q_LATENT))
+    _bits16(w_k, "w_k", (INDEX_DIM, RESIDUAL))
+    _bits16(w_w, "w_w", (INDEX_HEADS, RESIDUAL))
+    _spec(gamma, "gamma", (torch.float32,), (INDEX_DIM,))
+    _spec(beta, "beta", (torch.float32,), (INDEX_DIM,))
+    _bits16(keys, "keys", (None, INDEX_DIM))
+    _spec(key_rows, "key_rows", (torch.int64,), (t,))
     if q_idx is None:
         q_idx = torch.empty((t, INDEX_HEADS, INDEX_DIM), dtype=torch.bfloat16, device=c_q.device)
+    _bits16(q_idx, "q_idx", (t, INDEX_HEADS, INDEX_DIM))
     if w is None:
         w = torch.empty((t, INDEX_HEADS), dtype=torch.bfloat16, device=c_q.device)
+    _bits16(w, "w", (t, INDEX_HEADS))
     need = indexer_project_workspace_size(t)
+    _workspace(workspace, need)
+    _same_device(c_q, h, w_qi, w_k, w_w, gamma, beta, keys, key_rows, q_idx, w, workspace)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=c_q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_indexer_project", library().dsa_indexer_project(
         _ptr(c_q), _ptr(h), _ptr(w_qi), _ptr(w_k), _ptr(w_w), _ptr(gamma), _ptr(beta), float(eps), t,
-        _ptr(_contig(q_idx, "q_idx")), _ptr(_contig(w, "w")), _ptr(keys), _ptr(key_rows),
-        _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(q_idx), _ptr(w), _ptr(keys), _ptr(key_rows), _ptr(workspace), ws_bytes,
+        _stream(stream)))
     return q_idx, w
 
 
-def _codes(codes, scales):
+def _codes(codes, scales, n=None):
+    """FP8 key cache: codes [rows,128] uint8 and scales [rows] float32."""
     torch = _torch()
-    _contig(_dev(codes, "codes"), "codes")
-    _contig(_dev(scales, "scales"), "scales")
-    if codes.dtype != torch.uint8 or scales.dtype != torch.float32:
-        raise TypeError("codes must be uint8 and scales float32")
-    if codes.dim() != 2 or codes.shape[1] != INDEX_DIM or tuple(scales.shape) != (codes.shape[0],):
-        raise ValueError("codes must be [rows,128] and scales [rows]")
+    _spec(codes, "codes", (torch.uint8,), (n, INDEX_DIM))
+    _spec(scales, "scales", (torch.float32,), (codes.shape[0],))
 
 
 def quantize_index_keys_fp8(keys, codes=None, scales=None, stream=None):
     """FP8 index-key cache: bf16 keys [N,128] -> (codes [N,128] uint8 OCP E4M3, scales [N]
     float32 powers of two); key = E4M3(code) * scale."""
     torch = _torch()
-    _contig(_bits16(_dev(keys, "keys"), "keys"), "keys")
+    _bits16(keys, "keys", (None, INDEX_DIM))
     n = keys.shape[0]
     if codes is None:
         codes = torch.empty((n, INDEX_DIM), dtype=torch.uint8, device=keys.device)
     if scales is None:
         scales = torch.empty((n,), dtype=torch.float32, device=keys.device)
-    _codes(codes, scales)
+    _codes(codes, scales, n)
+    _same_device(keys, codes, scales)
     _check("dsa_quantize_index_keys_fp8", library().dsa_quantize_index_keys_fp8(
         _ptr(keys), n, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
@@ -341,15 +423,16 @@ def indexer_scores_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, max_s: int
                        stream=None):
     """Stage 2 over the FP8 key cache: fp32 scores [T, max_s]; entries j >= n_t untouched."""
     torch = _torch()
-    b = _layout(kv_off, q_req, q_pos)
+    t = _index_queries(q_idx, w)
+    b = _layout(kv_off, q_req, q_pos, t)
     _codes(codes, scales)
-    t = q_idx.shape[0]
     if scores is None:
         scores = torch.full((t, max_s), float("nan"), dtype=torch.float32, device=q_idx.device)
+    ld = _score_rows(scores, t, int(max_s))
+    _same_device(q_idx, w, codes, scales, kv_off, q_req, q_pos, scores)
     _check("dsa_indexer_scores_fp8", library().dsa_indexer_scores_fp8(
-        _ptr(_contig(_bits16(q_idx, "q_idx"), "q_idx")), _ptr(_contig(_bits16(w, "w"), "w")),
-        _ptr(codes), _ptr(scales), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b, int(max_s),
-        q_idx.shape[1], q_idx.shape[2], _ptr(scores), scores.stride(0), _stream(stream)))
+        _ptr(q_idx), _ptr(w), _ptr(codes), _ptr(scales), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t,
+        b, int(max_s), INDEX_HEADS, INDEX_DIM, _ptr(scores), ld, _stream(stream)))
     return scores
 
 
@@ -357,27 +440,26 @@ def indexer_topk_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, max_s: int, 
                      ids=None, workspace=None, stream=None):
     """Stages 2+3 over the FP8 key cache: [T,2048] request-local position IDs."""
     torch = _torch()
-    b = _layout(kv_off, q_req, q_pos)
+    t = _index_queries(q_idx, w)
+    b = _layout(kv_off, q_req, q_pos, t)
     _codes(codes, scales)
-    t = q_idx.shape[0]
-    if ids is None:
-        ids = torch.empty((t, k), dtype=torch.int32, device=q_idx.device)
+    ids = _ids(ids, t, k, q_idx.device)
     need = indexer_topk_workspace_size(t, max_s)
+    _workspace(workspace, need)
+    _same_device(q_idx, w, codes, scales, kv_off, q_req, q_pos, ids, workspace)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_idx.device)
     _check("dsa_indexer_topk_fp8", library().dsa_indexer_topk_fp8(
-        _ptr(_contig(_bits16(q_idx, "q_idx"), "q_idx")), _ptr(_contig(_bits16(w, "w"), "w")),
-        _ptr(codes), _ptr(scales), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b, int(max_s),
-        q_idx.shape[1], q_idx.shape[2], k, _ptr(_contig(ids, "ids")), _ptr(workspace),
+        _ptr(q_idx), _ptr(w), _ptr(codes), _ptr(scales), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t,
+        b, int(max_s), INDEX_HEADS, INDEX_DIM, k, _ptr(ids), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return ids
 
 
-def _pages(page_table):
+def _pages(page_table, b):
+    """Page table [B, max_pages] int32; returns max_pages."""
     torch = _torch()
-    _contig(_dev(page_table, "page_table"), "page_table")
-    if page_table.dtype != torch.int32 or page_table.dim() != 2:
-        raise TypeError("page_table must be an int32 [B, max_pages] tensor")
+    _spec(page_table, "page_table", (torch.int32,), (b, None))
     return page_table.shape[1]
 
 
@@ -387,20 +469,21 @@ def indexer_topk_paged(q_idx, w, key_pool, page_table, page_size: int, kv_off, q
     page_table[b, p // page_size] * page_size + p % page_size of key_pool [rows,128];
     kv_off gives only the request lengths.  Same IDs as indexer_topk on the same logical cache."""
     torch = _torch()
-    b = _layout(kv_off, q_req, q_pos)
-    max_pages = _pages(page_table)
-    t = q_idx.shape[0]
-    if ids is None:
-        ids = torch.empty((t, k), dtype=torch.int32, device=q_idx.device)
+    t = _index_queries(q_idx, w)
+    b = _layout(kv_off, q_req, q_pos, t)
+    _bits16(key_pool, "key_pool", (None, INDEX_DIM))
+    max_pages = _pages(page_table, b)
+    ids = _ids(ids, t, k, q_idx.device)
     need = indexer_topk_workspace_size(t, max_s)
+    _workspace(workspace, need)
+    _same_device(q_idx, w, key_pool, page_table, kv_off, q_req, q_pos, ids, workspace)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_idx.device)
     _check("dsa_indexer_topk_paged", library().dsa_indexer_topk_paged(
-        _ptr(_contig(_bits16(q_idx, "q_idx"), "q_idx")), _ptr(_contig(_bits16(w, "w"), "w")),
-        _ptr(_contig(_bits16(key_pool, "key_pool"), "key_pool")), _ptr(page_table), int(page_size),
-        max_pages, _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b, int(max_s), q_idx.shape[1],
-        q_idx.shape[2], k, _ptr(_contig(ids, "ids")), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(q_idx), _ptr(w), _ptr(key_pool), _ptr(page_table), int(page_size), max_pages,
+        _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b, int(max_s), INDEX_HEADS, INDEX_DIM, k,
+        _ptr(ids), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return ids
 
 
@@ -410,29 +493,18 @@ def sparse_mla_attn_paged(q, latent_pool, kpe_pool, page_table, page_size: int, 
     """Stage 4 over paged latent/companion pools (rows addressed as in indexer_topk_paged);
     same results as sparse_mla_attn on the same logical cache."""
     torch = _torch()
-    _contig(_bits16(q, "q"), "q")
-    _bits16(latent_pool, "latent_pool")
-    _bits16(kpe_pool, "kpe_pool")
-    ld_lat = _rows_ld(latent_pool, "latent_pool", LATENT_DIM)
-    ld_kpe = _rows_ld(kpe_pool, "kpe_pool", COMPANION_DIM)
-    max_pages = _pages(page_table)
-    b = kv_off.shape[0] - 1
-    for x, n in ((kv_off, "kv_off"), (q_req, "q_req"), (ids, "ids")):
-        _contig(_dev(x, n), n)
-    t, h = q.shape[0], q.shape[1]
-    if out is None:
-        out = torch.empty((t, h, LATENT_DIM), dtype=out_dtype or torch.bfloat16, device=q.device)
-    if out.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out must be bfloat16 or float32")
-    if lse is None:
-        lse = torch.empty((t, h), dtype=torch.float32, device=q.device)
-    need = sparse_mla_workspace_size(t, h, ids.shape[1] if ids.dim() == 2 else TOPK)
+    t, b, ld_lat, ld_kpe, out, lse = _mla_args(q, latent_pool, kpe_pool, kv_off, q_req, ids, out,
+                                               lse, out_dtype, "latent_pool", "kpe_pool")
+    max_pages = _pages(page_table, b)
+    need = sparse_mla_workspace_size(t)
+    _workspace(workspace, need)
+    _same_device(q, latent_pool, kpe_pool, page_table, kv_off, q_req, ids, out, lse, workspace)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_sparse_mla_attn_paged", library().dsa_sparse_mla_attn_paged(
         _ptr(q), _ptr(latent_pool), ld_lat, _ptr(kpe_pool), ld_kpe, _ptr(page_table),
-        int(page_size), max_pages, _ptr(kv_off), _ptr(q_req), _ptr(ids), t, b, h, ids.shape[1],
-        float(scale), _ptr(_contig(out, "out")), 1 if out.dtype == torch.float32 else 0, _ptr(lse),
+        int(page_size), max_pages, _ptr(kv_off), _ptr(q_req), _ptr(ids), t, b, MLA_HEADS, TOPK,
+        float(scale), _ptr(out), 1 if out.dtype == torch.float32 else 0, _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse

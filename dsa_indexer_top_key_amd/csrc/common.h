@@ -44,6 +44,26 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Request of query t: q_req[t] when it lies in [0, B), else -1.  A query outside the batch
+// has no admissible position (its scores are not written, its ID row is all -1, its read is
+// zero), so no request-indexed array is ever read out of bounds.
+__device__ __forceinline__ int query_request(const int32_t* q_req, int64_t t, int32_t B) {
+    const int b = q_req[t];
+    return (b >= 0 && b < B) ? b : -1;
+}
+
+// Admissible count n_t = min(pos + 1, S_b) (causal, the diagonal included), clamped to
+// [0, max_s]; 0 for a query outside the batch (b < 0).
+__device__ __forceinline__ int64_t admissible_count(const int64_t* kv_off, int b, int32_t pos,
+                                                    int64_t max_s) {
+    if (b < 0) return 0;
+    const int64_t s_b = kv_off[b + 1] - kv_off[b];
+    int64_t n = static_cast<int64_t>(pos) + 1;
+    n = n < s_b ? n : s_b;
+    n = n < max_s ? n : max_s;
+    return n > 0 ? n : 0;
+}
+
 // Workgroup barrier that orders LDS only: LDS writes issued before it are visible to LDS
 // reads after it, while global-memory loads (and global->LDS copies) stay in flight; where
 // a kernel hands such data across the barrier it waits on vmcnt explicitly.

@@ -21,13 +21,13 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const
                                  int max_pages = 0);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
-                       int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream,
+                       int32_t B, int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream,
                        int32_t* cand_ws);
 size_t topk_workspace_bytes(int32_t T, int64_t max_n);
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t ld_lat,
                              const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
-                             const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
-                             void* out, bool out_f32, float* lse, void* workspace,
+                             const int32_t* q_req, const int32_t* ids, int32_t T, int32_t B,
+                             float scale, void* out, bool out_f32, float* lse, void* workspace,
                              hipStream_t stream, const int32_t* page_table = nullptr,
                              int lg_page = 0, int max_pages = 0);
 size_t sparse_mla_workspace_bytes(int32_t T);
@@ -39,7 +39,7 @@ hipError_t launch_quantize_keys_fp8(const uint16_t* keys, int64_t n_rows, uint8_
 hipError_t launch_indexer_scores_fp8(const uint16_t* q_idx, const uint16_t* w, const uint8_t* codes,
                                      const float* kscale, const int64_t* kv_off,
                                      const int32_t* q_req, const int32_t* q_pos, int32_t T,
-                                     int64_t max_s, float* scores, int64_t ld,
+                                     int32_t B, int64_t max_s, float* scores, int64_t ld,
                                      hipStream_t stream);
 hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uint16_t* w_qi,
                                const uint16_t* w_k, const uint16_t* w_w, const float* gamma,
@@ -169,7 +169,7 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, const int32_t* n_valid, i
                 static_cast<long long>(ld), static_cast<long long>(max_n));
     DSA_REQUIRE(aligned(scores, 4) && aligned(n_valid, 4) && aligned(ids, 4),
                 DSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
-    return from_hip(dsa::launch_topk(scores, ld, n_valid, nullptr, nullptr, nullptr, T, max_n,
+    return from_hip(dsa::launch_topk(scores, ld, n_valid, nullptr, nullptr, nullptr, 0, T, max_n,
                                      ids, static_cast<hipStream_t>(stream), nullptr), fn);
 }
 
@@ -230,8 +230,8 @@ static dsa_status_t indexer_topk_impl(const char* fn, const uint16_t* q_idx, con
     int32_t* cand = dsa::topk_workspace_bytes(T, max_S) > 0
                         ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + score_bytes(T, max_S))
                         : nullptr;
-    return from_hip(dsa::launch_topk(scores, ld, nullptr, kv_off, q_req, q_pos, T, max_S, ids, s,
-                                     cand),
+    return from_hip(dsa::launch_topk(scores, ld, nullptr, kv_off, q_req, q_pos, B, T, max_S, ids,
+                                     s, cand),
                     fn);
 }
 
@@ -307,7 +307,7 @@ static dsa_status_t sparse_mla_impl(const char* fn, const uint16_t* q, const uin
                     "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
     }
     return from_hip(dsa::launch_sparse_mla(q, latent, ld_latent, kpe, ld_kpe, kv_off, q_req, ids,
-                                           T, scale, out, out_dtype == DSA_OUT_F32, lse,
+                                           T, B, scale, out, out_dtype == DSA_OUT_F32, lse,
                                            workspace, static_cast<hipStream_t>(stream),
                                            page_table, lg_page, max_pages), fn);
 }
@@ -343,7 +343,6 @@ dsa_status_t dsa_sparse_mla_attn_paged(const uint16_t* q, const uint16_t* latent
                            workspace_bytes, stream, page_table, lg, max_pages);
 }
 
-}  // extern "C"
 
 dsa_status_t dsa_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint16_t* gate,
                             int32_t T, int32_t n_heads, uint16_t* out, void* stream) {
@@ -351,7 +350,7 @@ dsa_status_t dsa_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint1
     DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
     DSA_REQUIRE(n_heads == DSA_MLA_HEADS, DSA_ERR_UNSUPPORTED, "%s: n_heads=%d unsupported (only %d)",
                 fn, n_heads, DSA_MLA_HEADS);
-    if (T == 0) return DSA_OK;
+    if (T == 0) return ok();
     DSA_REQUIRE(o && w_uv && gate && out, DSA_ERR_INVALID_ARG, "%s: null pointer", fn);
     DSA_REQUIRE(aligned(o, 16) && aligned(w_uv, 16) && aligned(gate, 2) && aligned(out, 4),
                 DSA_ERR_INVALID_ARG, "%s: o and w_uv must be 16-byte, gate 2-byte, out 4-byte aligned", fn);
@@ -417,7 +416,7 @@ dsa_status_t dsa_indexer_scores_fp8(const uint16_t* q_idx, const uint16_t* w, co
     DSA_REQUIRE(ld_scores >= max_S, DSA_ERR_INVALID_ARG, "%s: ld_scores=%lld < max_S=%lld", fn,
                 static_cast<long long>(ld_scores), static_cast<long long>(max_S));
     return from_hip(dsa::launch_indexer_scores_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, T,
-                                                   max_S, scores, ld_scores,
+                                                   B, max_S, scores, ld_scores,
                                                    static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -446,12 +445,14 @@ dsa_status_t dsa_indexer_topk_fp8(const uint16_t* q_idx, const uint16_t* w, cons
     float* scores = static_cast<float*>(workspace);
     const int64_t ld = score_ld(max_S);
     hipError_t e = dsa::launch_indexer_scores_fp8(q_idx, w, codes, scales, kv_off, q_req, q_pos, T,
-                                                  max_S, scores, ld, s);
+                                                  B, max_S, scores, ld, s);
     if (e != hipSuccess) return from_hip(e, fn);
     int32_t* cand = dsa::topk_workspace_bytes(T, max_S) > 0
                         ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + score_bytes(T, max_S))
                         : nullptr;
-    return from_hip(dsa::launch_topk(scores, ld, nullptr, kv_off, q_req, q_pos, T, max_S, ids, s,
-                                     cand),
+    return from_hip(dsa::launch_topk(scores, ld, nullptr, kv_off, q_req, q_pos, B, T, max_S, ids,
+                                     s, cand),
                     fn);
 }
+
+}  // extern "C"

@@ -24,16 +24,6 @@
 
 namespace dsa {
 
-// Admissible count n_t = min(q_pos + 1, S_b), clamped to [0, max_s].
-__device__ __forceinline__ int64_t admissible(const int64_t* kv_off, int b, int32_t pos,
-                                              int64_t max_s) {
-    const int64_t s_b = kv_off[b + 1] - kv_off[b];
-    int64_t n = static_cast<int64_t>(pos) + 1;
-    n = n < s_b ? n : s_b;
-    n = n < max_s ? n : max_s;
-    return n > 0 ? n : 0;
-}
-
 // ---------------------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------------------
@@ -76,15 +66,16 @@ template <bool PAGED>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ keys, const int64_t* __restrict__ kv_off,
-    const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos, int32_t chunks_per_q,
-    int32_t chunk, int64_t max_s, float* __restrict__ scores, int64_t ld, int vec_store,
+    const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos, int32_t B,
+    int32_t chunks_per_q, int32_t chunk, int64_t max_s, float* __restrict__ scores, int64_t ld,
+    int vec_store,
     const int32_t* __restrict__ page_table, int lg_page, int max_pages) {
     __shared__ __attribute__((aligned(16))) uint16_t ring[4][kDecodeRing][kDecodeTile * kIndexDim];
     __shared__ __attribute__((aligned(16))) float sbuf[kDecodeMaxChunk];
     const int t = blockIdx.x / chunks_per_q;
     const int ci = blockIdx.x - t * chunks_per_q;
-    const int b = q_req[t];
-    const int64_t n = admissible(kv_off, b, q_pos[t], max_s);
+    const int b = query_request(q_req, t, B);
+    const int64_t n = admissible_count(kv_off, b, q_pos[t], max_s);
     const int64_t k0 = static_cast<int64_t>(ci) * chunk;
     if (k0 >= n) return;  // block-uniform
     const int len = static_cast<int>((k0 + chunk < n ? k0 + chunk : n) - k0);
@@ -100,7 +91,9 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     if constexpr (PAGED) {
         const int64_t lp = (k0 >> lg_page) + lane;
         const int64_t np = (k0 + len + (int64_t{1} << lg_page) - 1) >> lg_page;
-        pte = lp < np ? page_table[static_cast<int64_t>(b) * max_pages + lp] : 0;
+        // entries past the table's row (S_b > max_pages * page_size breaks the contract) are
+        // never read: such positions score page 0
+        pte = lp < np && lp < max_pages ? page_table[static_cast<int64_t>(b) * max_pages + lp] : 0;
     }
     // copies of this wave's j-th tile into ring slot j % 3; keys past the end copy key 0 (the
     // tile's first key when paged, which keeps the whole tile in one page)
@@ -193,8 +186,8 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
 
 hipError_t launch_indexer_prefill(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
                                   const int64_t* kv_off, const int32_t* q_req,
-                                  const int32_t* q_pos, int32_t T, int64_t max_s, float* scores,
-                                  int64_t ld, hipStream_t stream);
+                                  const int32_t* q_pos, int32_t T, int32_t B, int64_t max_s,
+                                  float* scores, int64_t ld, hipStream_t stream);
 
 hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
                                  const int64_t* kv_off, const int32_t* q_req,
@@ -205,7 +198,7 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const
     // request); per-query streaming otherwise (always for a paged cache).  Both are exact for
     // any layout.
     if (!page_table && static_cast<int64_t>(T) >= 8 * static_cast<int64_t>(B)) {
-        return launch_indexer_prefill(q_idx, w, keys, kv_off, q_req, q_pos, T, max_s, scores,
+        return launch_indexer_prefill(q_idx, w, keys, kv_off, q_req, q_pos, T, B, max_s, scores,
                                       ld, stream);
     } else {
         const int64_t chunk = decode_chunk(T, max_s);
@@ -215,12 +208,12 @@ hipError_t launch_indexer_scores(const uint16_t* q_idx, const uint16_t* w, const
         const bool vec = reinterpret_cast<uintptr_t>(scores) % 16 == 0 && ld % 4 == 0;
         if (page_table)
             hipLaunchKernelGGL(indexer_decode_kernel<true>, dim3(static_cast<unsigned>(blocks)),
-                               dim3(256), 0, stream, q_idx, w, keys, kv_off, q_req, q_pos,
+                               dim3(256), 0, stream, q_idx, w, keys, kv_off, q_req, q_pos, B,
                                static_cast<int32_t>(cpq), static_cast<int32_t>(chunk), max_s,
                                scores, ld, vec ? 1 : 0, page_table, lg_page, max_pages);
         else
             hipLaunchKernelGGL(indexer_decode_kernel<false>, dim3(static_cast<unsigned>(blocks)),
-                               dim3(256), 0, stream, q_idx, w, keys, kv_off, q_req, q_pos,
+                               dim3(256), 0, stream, q_idx, w, keys, kv_off, q_req, q_pos, B,
                                static_cast<int32_t>(cpq), static_cast<int32_t>(chunk), max_s,
                                scores, ld, vec ? 1 : 0, nullptr, 0, 0);
     }

@@ -54,15 +54,6 @@ int64_t f8_chunk(int32_t T, int64_t max_s) {
     return c > kF8MaxChunk ? kF8MaxChunk : c;
 }
 
-__device__ __forceinline__ int64_t admissible_f8(const int64_t* kv_off, int b, int32_t pos,
-                                                 int64_t max_s) {
-    const int64_t s_b = kv_off[b + 1] - kv_off[b];
-    int64_t n = static_cast<int64_t>(pos) + 1;
-    n = n < s_b ? n : s_b;
-    n = n < max_s ? n : max_s;
-    return n > 0 ? n : 0;
-}
-
 }  // namespace
 
 // Half a wave (32 lanes) per key row: each lane holds four consecutive bf16 values (8 bytes)
@@ -110,14 +101,14 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ codes, const float* __restrict__ kscale,
     const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
-    const int32_t* __restrict__ q_pos, int32_t chunks_per_q, int32_t chunk, int64_t max_s,
-    float* __restrict__ scores, int64_t ld, int vec_store) {
+    const int32_t* __restrict__ q_pos, int32_t B, int32_t chunks_per_q, int32_t chunk,
+    int64_t max_s, float* __restrict__ scores, int64_t ld, int vec_store) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[4][kF8Ring][kF8Tile * kF8Key];
     __shared__ __attribute__((aligned(16))) float sbuf[kF8MaxChunk];
     const int t = blockIdx.x / chunks_per_q;
     const int ci = blockIdx.x - t * chunks_per_q;
-    const int b = q_req[t];
-    const int64_t n = admissible_f8(kv_off, b, q_pos[t], max_s);
+    const int b = query_request(q_req, t, B);
+    const int64_t n = admissible_count(kv_off, b, q_pos[t], max_s);
     const int64_t k0 = static_cast<int64_t>(ci) * chunk;
     if (k0 >= n) return;  // block-uniform
     const int len = static_cast<int>((k0 + chunk < n ? k0 + chunk : n) - k0);
@@ -240,7 +231,7 @@ hipError_t launch_quantize_keys_fp8(const uint16_t* keys, int64_t n_rows, uint8_
 hipError_t launch_indexer_scores_fp8(const uint16_t* q_idx, const uint16_t* w, const uint8_t* codes,
                                      const float* kscale, const int64_t* kv_off,
                                      const int32_t* q_req, const int32_t* q_pos, int32_t T,
-                                     int64_t max_s, float* scores, int64_t ld,
+                                     int32_t B, int64_t max_s, float* scores, int64_t ld,
                                      hipStream_t stream) {
     const int64_t chunk = f8_chunk(T, max_s);
     const int64_t cpq = (max_s + chunk - 1) / chunk;
@@ -248,7 +239,7 @@ hipError_t launch_indexer_scores_fp8(const uint16_t* q_idx, const uint16_t* w, c
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool vec = reinterpret_cast<uintptr_t>(scores) % 16 == 0 && ld % 4 == 0;
     hipLaunchKernelGGL(indexer_decode_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                       stream, q_idx, w, codes, kscale, kv_off, q_req, q_pos,
+                       stream, q_idx, w, codes, kscale, kv_off, q_req, q_pos, B,
                        static_cast<int32_t>(cpq), static_cast<int32_t>(chunk), max_s, scores, ld,
                        vec ? 1 : 0);
     return hipGetLastError();

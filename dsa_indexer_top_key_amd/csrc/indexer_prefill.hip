@@ -37,15 +37,6 @@ constexpr int kQPW = 2;          // queries per wave: 8 waves, 2 per SIMD
 constexpr int kPTile = 128;      // keys per LDS tile (32 KB)
 constexpr int kPRing = 4;        // ring slots: tiles i..i+3 (i+3 being copied)
 
-__device__ __forceinline__ int64_t admissible_n(const int64_t* kv_off, int b, int32_t pos,
-                                                int64_t max_s) {
-    const int64_t s_b = kv_off[b + 1] - kv_off[b];
-    int64_t n = static_cast<int64_t>(pos) + 1;
-    n = n < s_b ? n : s_b;
-    n = n < max_s ? n : max_s;
-    return n > 0 ? n : 0;
-}
-
 }  // namespace
 
 // grid: one block per 16 consecutive queries; 512 threads (8 waves), wave w owning queries
@@ -61,7 +52,7 @@ __device__ __forceinline__ int64_t admissible_n(const int64_t* kv_off, int b, in
 __global__ __launch_bounds__(64 * (kPQ / kQPW)) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ keys, const int64_t* __restrict__ kv_off,
-    const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos, int32_t T,
+    const int32_t* __restrict__ q_req, const int32_t* __restrict__ q_pos, int32_t T, int32_t B,
     int64_t max_s, float* __restrict__ scores, int64_t ld) {
     constexpr int QPW = kQPW;
     constexpr int kWaves = kPQ / QPW;
@@ -83,8 +74,9 @@ __global__ __launch_bounds__(64 * (kPQ / kQPW)) void indexer_prefill_kernel(
     if (tid < kPQ) {
         const int t = t0 + tid;
         if (t < T) {
-            s_req[tid] = q_req[t];
-            s_n[tid] = admissible_n(kv_off, q_req[t], q_pos[t], max_s);
+            const int b = query_request(q_req, t, B);
+            s_req[tid] = b;  // -1 outside the batch: no admissible position
+            s_n[tid] = admissible_count(kv_off, b, q_pos[t], max_s);
         } else {
             s_req[tid] = -1;
             s_n[tid] = 0;
@@ -233,11 +225,11 @@ __global__ __launch_bounds__(64 * (kPQ / kQPW)) void indexer_prefill_kernel(
 
 hipError_t launch_indexer_prefill(const uint16_t* q_idx, const uint16_t* w, const uint16_t* keys,
                                   const int64_t* kv_off, const int32_t* q_req,
-                                  const int32_t* q_pos, int32_t T, int64_t max_s, float* scores,
-                                  int64_t ld, hipStream_t stream) {
+                                  const int32_t* q_pos, int32_t T, int32_t B, int64_t max_s,
+                                  float* scores, int64_t ld, hipStream_t stream) {
     const int blocks = (T + kPQ - 1) / kPQ;
     hipLaunchKernelGGL(indexer_prefill_kernel, dim3(blocks), dim3(64 * (kPQ / kQPW)), 0, stream,
-                       q_idx, w, keys, kv_off, q_req, q_pos, T, max_s, scores, ld);
+                       q_idx, w, keys, kv_off, q_req, q_pos, T, B, max_s, scores, ld);
     return hipGetLastError();
 }
 

@@ -147,7 +147,7 @@ template <bool PAGED>
 __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t ld_lat,
     const uint16_t* __restrict__ kpe, int64_t ld_kpe, const int64_t* __restrict__ kv_off,
-    const int32_t* __restrict__ q_req, const int32_t* __restrict__ ids, int32_t T,
+    const int32_t* __restrict__ q_req, const int32_t* __restrict__ ids, int32_t T, int32_t B,
     int32_t nsplit, float scale_log2, void* __restrict__ out, int out_f32,
     float* __restrict__ lse, void* __restrict__ part_o, float* __restrict__ part_lse,
     const int32_t* __restrict__ page_table, int lg_page, int max_pages) {
@@ -190,9 +190,13 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         const int i = 256 * k + tid;
         idv[k] = i < L ? idr[i] : -1;
     }
-    const int b = q_req[t];
-    const int64_t off = kv_off[b];
-    const int64_t s_b = kv_off[b + 1] - off;
+    // a query outside the batch (q_req[t] not in [0, B)) has no valid ID: zero read, lse -inf
+    const int b = query_request(q_req, t, B);
+    const int64_t off = b >= 0 ? kv_off[b] : 0;
+    int64_t s_b = b >= 0 ? kv_off[b + 1] - off : 0;
+    // paged: IDs beyond the page table's row (S_b > max_pages * page_size breaks the
+    // contract) count as padding, so no entry past the row is read
+    if constexpr (PAGED) s_b = s_b < (static_cast<int64_t>(max_pages) << lg_page) ? s_b : (static_cast<int64_t>(max_pages) << lg_page);
     const int64_t base = PAGED ? 0 : off;  // paged: the rows below are pool rows
     if (tid == 0) sm.redo = 0;
     uint32_t end = 0;
@@ -206,9 +210,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         const uint64_t m = __ballot(ok);  // lanes 0..31: one tile, lanes 32..63: the next
         if (i < L) {
             int32_t row = ok ? id : 0;
-            if constexpr (PAGED)
-                row = (page_table[static_cast<int64_t>(b) * max_pages + (row >> lg_page)] << lg_page) |
-                      (row & ((1 << lg_page) - 1));
+            if constexpr (PAGED)  // (b < 0 leaves no valid ID and no tile to copy)
+                if (b >= 0)
+                    row = (page_table[static_cast<int64_t>(b) * max_pages + (row >> lg_page)] << lg_page) |
+                          (row & ((1 << lg_page) - 1));
             sm.rows[i] = row;
             if ((lane & 31) == 0) sm.tmask[i / kTile] = static_cast<uint32_t>(m >> (lane & 32));
         }
@@ -601,8 +606,8 @@ size_t sparse_mla_workspace_bytes(int32_t T) {
 
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t ld_lat,
                              const uint16_t* kpe, int64_t ld_kpe, const int64_t* kv_off,
-                             const int32_t* q_req, const int32_t* ids, int32_t T, float scale,
-                             void* out, bool out_f32, float* lse, void* workspace,
+                             const int32_t* q_req, const int32_t* ids, int32_t T, int32_t B,
+                             float scale, void* out, bool out_f32, float* lse, void* workspace,
                              hipStream_t stream, const int32_t* page_table, int lg_page,
                              int max_pages) {
     const int ns = sparse_mla_nsplit(T);
@@ -619,12 +624,12 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* latent, int64_t 
     const float scale_log2 = scale * 1.4426950408889634f;
     if (page_table)
         hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256),
-                           0, stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, ns,
+                           0, stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, B, ns,
                            scale_log2, out, out_f32 ? 1 : 0, lse, part_o, part_lse, page_table,
                            lg_page, max_pages);
     else
         hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256),
-                           0, stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, ns,
+                           0, stream, q, latent, ld_lat, kpe, ld_kpe, kv_off, q_req, ids, T, B, ns,
                            scale_log2, out, out_f32 ? 1 : 0, lse, part_o, part_lse, nullptr, 0, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;

@@ -203,23 +203,26 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m, uint32_t acc) {
 // (equal scores: lower position first) is the same at both levels, so the merge is exact.
 enum TopkMode { kRow = 0, kParts = 1, kMerge = 2 };
 
-// Elements of row t: explicit n_valid[t], else the causal prefix min(q_pos + 1, S_b); at most
-// max_n, at least 0.
-__device__ __forceinline__ int64_t topk_row_len(int t, const int32_t* __restrict__ n_valid,
-                                                const int64_t* __restrict__ kv_off,
-                                                const int32_t* __restrict__ q_req,
-                                                const int32_t* __restrict__ q_pos, int64_t max_n) {
+// Where each row's length comes from: explicit n_valid[t] when n_valid is given, else the
+// causal prefix min(q_pos[t] + 1, S_b) of request q_req[t] (0 when q_req[t] lies outside
+// [0, n_req)); at most max_n, at least 0.
+struct RowLens {
+    const int32_t* n_valid;
+    const int64_t* kv_off;
+    const int32_t* q_req;
+    const int32_t* q_pos;
+    int64_t max_n;
+    int32_t n_req;
+};
+
+__device__ __forceinline__ int64_t topk_row_len(int t, const RowLens& rl) {
     int64_t n_row;
-    if (n_valid) {
-        n_row = n_valid[t];
-    } else {
-        const int b = q_req[t];
-        const int64_t s_b = kv_off[b + 1] - kv_off[b];
-        n_row = static_cast<int64_t>(q_pos[t]) + 1;
-        n_row = n_row < s_b ? n_row : s_b;
+    if (rl.n_valid) {
+        n_row = rl.n_valid[t];
+        n_row = n_row < rl.max_n ? n_row : rl.max_n;
+        return n_row > 0 ? n_row : 0;
     }
-    n_row = n_row < max_n ? n_row : max_n;
-    return n_row > 0 ? n_row : 0;
+    return admissible_count(rl.kv_off, query_request(rl.q_req, t, rl.n_req), rl.q_pos[t], rl.max_n);
 }
 
 // Rows selected by a persistent block (one per CU, looping over rows) have the first
@@ -260,9 +263,7 @@ __device__ __forceinline__ void topk_prefetch(f32x4* pre, const float* row, int6
 template <int E, bool STREAM, bool VEC, int MODE, bool PRE>
 __device__ __forceinline__ void topk_select(
     TopkSmem& sm, const int t, const int part, const int64_t ob,
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
-    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
-    const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids,
+    const float* __restrict__ scores, int64_t ld, const RowLens& rl, int32_t* __restrict__ ids,
     int32_t parts, int64_t chunk, const int32_t* __restrict__ cands,
     f32x4* pre, bool pre_rd, const float* next_row, int64_t n_next, f32x4* nxt, bool nxt_rd,
     bool* nxt_issued) {
@@ -278,7 +279,7 @@ __device__ __forceinline__ void topk_select(
     if constexpr (PRE) __asm__ volatile("" : "+v"(tid), "+v"(lane));
     const int wave = PRE ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
 
-    const int64_t n_row = topk_row_len(t, n_valid, kv_off, q_req, q_pos, max_n);
+    const int64_t n_row = topk_row_len(t, rl);
     int64_t n = n_row;  // elements this block selects from (element index p < n)
     if (MODE == kParts) {
         n = n_row - part * chunk;
@@ -722,17 +723,15 @@ __device__ __forceinline__ void topk_select(
 // depend on how many blocks are resident at once.
 template <int E, bool STREAM, bool VEC, int MODE, bool PRE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_valid,
-    const int64_t* __restrict__ kv_off, const int32_t* __restrict__ q_req,
-    const int32_t* __restrict__ q_pos, int64_t max_n, int32_t* __restrict__ ids,
+    const float* __restrict__ scores, int64_t ld, const RowLens rl, int32_t* __restrict__ ids,
     int32_t parts, int64_t chunk, const int32_t* __restrict__ cands, int32_t n_rows) {
     __shared__ TopkSmem sm;
     if constexpr (!PRE) {
         const int b = static_cast<int>(blockIdx.x);
         const int t = MODE == kParts ? b / parts : b;
         const int part = MODE == kParts ? b - t * parts : 0;
-        topk_select<E, STREAM, VEC, MODE, false>(sm, t, part, b, scores, ld, n_valid, kv_off,
-                                                 q_req, q_pos, max_n, ids, parts, chunk, cands,
+        topk_select<E, STREAM, VEC, MODE, false>(sm, t, part, b, scores, ld, rl, ids, parts,
+                                                 chunk, cands,
                                                  nullptr, false, nullptr, 0, nullptr, false,
                                                  nullptr);
     } else {
@@ -749,11 +748,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             }
             const int tn = t + step;
             const float* next = tn < n_rows ? scores + static_cast<int64_t>(tn) * ld : nullptr;
-            const int64_t n_next = next ? topk_row_len(tn, n_valid, kv_off, q_req, q_pos, max_n) : 0;
+            const int64_t n_next = next ? topk_row_len(tn, rl) : 0;
             bool issued = false;
-            topk_select<E, STREAM, VEC, MODE, true>(sm, t, 0, t, scores, ld, n_valid, kv_off,
-                                                    q_req, q_pos, max_n, ids, parts, chunk,
-                                                    cands, pre, has_pre, next, n_next, nxt,
+            topk_select<E, STREAM, VEC, MODE, true>(sm, t, 0, t, scores, ld, rl, ids, parts,
+                                                    chunk, cands, pre, has_pre, next, n_next, nxt,
                                                     has_pre && nxt_rd, &issued);
             nxt_rd = issued;
         }
@@ -761,18 +759,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 }
 
 template <int E, bool STREAM, int MODE>
-static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, const int32_t* n_valid,
-                          const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
-                          int64_t max_n, int32_t* ids, int32_t parts, int64_t chunk,
-                          const int32_t* cands, bool vec, hipStream_t stream) {
+static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, const RowLens& rl,
+                          int32_t* ids, int32_t parts, int64_t chunk, const int32_t* cands,
+                          bool vec, hipStream_t stream) {
     if (vec)
         hipLaunchKernelGGL((topk_kernel<E, STREAM, true, MODE, false>), dim3(blocks),
-                           dim3(kTopkThreads), 0, stream, scores, ld, n_valid, kv_off, q_req,
-                           q_pos, max_n, ids, parts, chunk, cands, 0);
+                           dim3(kTopkThreads), 0, stream, scores, ld, rl, ids, parts, chunk,
+                           cands, 0);
     else
         hipLaunchKernelGGL((topk_kernel<E, STREAM, false, MODE, false>), dim3(blocks),
-                           dim3(kTopkThreads), 0, stream, scores, ld, n_valid, kv_off, q_req,
-                           q_pos, max_n, ids, parts, chunk, cands, 0);
+                           dim3(kTopkThreads), 0, stream, scores, ld, rl, ids, parts, chunk,
+                           cands, 0);
 }
 
 // Compute units of the current device (the persistent grid size), looked up once per device
@@ -793,27 +790,26 @@ static int device_cus() {
 // One selection pass over rows (or parts) of at most `len` elements each.
 template <int MODE>
 static void launch_pass(unsigned blocks, int64_t len, const float* scores, int64_t ld,
-                        const int32_t* n_valid, const int64_t* kv_off, const int32_t* q_req,
-                        const int32_t* q_pos, int64_t max_n, int32_t* ids, int32_t parts,
-                        int64_t chunk, bool vec, hipStream_t stream) {
+                        const RowLens& rl, int32_t* ids, int32_t parts, int64_t chunk, bool vec,
+                        hipStream_t stream) {
     if (len <= 4 * kTopkThreads)
-        launch_topk_e<4, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<4, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
     else if (len <= 8 * kTopkThreads)
-        launch_topk_e<8, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<8, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
     else if (len <= 16 * kTopkThreads)
-        launch_topk_e<16, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<16, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
     else if (len <= 32 * kTopkThreads)
-        launch_topk_e<32, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<32, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
     else if (len <= 64 * kTopkThreads && MODE == kRow && vec) {
         // persistent blocks with the next row's LDS prefetch (one block per CU)
         const unsigned grid = std::min(blocks, static_cast<unsigned>(device_cus()));
         hipLaunchKernelGGL((topk_kernel<64, false, true, kRow, true>), dim3(grid),
-                           dim3(kTopkThreads), 0, stream, scores, ld, n_valid, kv_off, q_req,
-                           q_pos, max_n, ids, parts, chunk, nullptr, static_cast<int32_t>(blocks));
+                           dim3(kTopkThreads), 0, stream, scores, ld, rl, ids, parts, chunk,
+                           nullptr, static_cast<int32_t>(blocks));
     } else if (len <= 64 * kTopkThreads)
-        launch_topk_e<64, false, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<64, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
     else
-        launch_topk_e<16, true, MODE>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<16, true, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
 }
 
 // Parts per row for the two-stage selection: rows are split while fewer than 256 blocks
@@ -832,35 +828,35 @@ size_t topk_workspace_bytes(int32_t T, int64_t max_n) {
     return p > 1 ? static_cast<size_t>(T) * p * kTopK * sizeof(int32_t) : 0;
 }
 
-// Either n_valid (explicit row lengths) or (kv_off, q_req, q_pos) gives each row's length.
-// With a candidate workspace (topk_workspace_bytes) rows may be split into parts.
+// Either n_valid (explicit row lengths) or (kv_off, q_req, q_pos) of B requests gives each
+// row's length.  With a candidate workspace (topk_workspace_bytes) rows may be split into parts.
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
                        const int64_t* kv_off, const int32_t* q_req, const int32_t* q_pos,
-                       int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream,
+                       int32_t B, int32_t T, int64_t max_n, int32_t* ids, hipStream_t stream,
                        int32_t* cand_ws) {
+    const RowLens rl{n_valid, kv_off, q_req, q_pos, max_n, B};
     const bool vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (ld % 4 == 0);
     const int parts = cand_ws ? topk_parts(T, max_n) : 1;
     if (parts == 1) {
-        launch_pass<kRow>(static_cast<unsigned>(T), max_n, scores, ld, n_valid, kv_off, q_req,
-                          q_pos, max_n, ids, 1, 0, vec, stream);
+        launch_pass<kRow>(static_cast<unsigned>(T), max_n, scores, ld, rl, ids, 1, 0, vec, stream);
         return hipGetLastError();
     }
     // parts start 16-byte aligned: chunk is a multiple of 4096 elements
     int64_t chunk = (max_n + parts - 1) / parts;
     chunk = (chunk + 4095) & ~static_cast<int64_t>(4095);
-    launch_pass<kParts>(static_cast<unsigned>(T * parts), chunk, scores, ld, n_valid, kv_off,
-                        q_req, q_pos, max_n, cand_ws, parts, chunk, vec, stream);
+    launch_pass<kParts>(static_cast<unsigned>(T * parts), chunk, scores, ld, rl, cand_ws, parts,
+                        chunk, vec, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned blocks = static_cast<unsigned>(T);
     if (parts == 2)
-        launch_topk_e<4, false, kMerge>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, cand_ws, false, stream);
+        launch_topk_e<4, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, false, stream);
     else if (parts == 4)
-        launch_topk_e<8, false, kMerge>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, cand_ws, false, stream);
+        launch_topk_e<8, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, false, stream);
     else if (parts == 8)
-        launch_topk_e<16, false, kMerge>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, cand_ws, false, stream);
+        launch_topk_e<16, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, false, stream);
     else
-        launch_topk_e<32, false, kMerge>(blocks, scores, ld, n_valid, kv_off, q_req, q_pos, max_n, ids, parts, chunk, cand_ws, false, stream);
+        launch_topk_e<32, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, false, stream);
     return hipGetLastError();
 }
 

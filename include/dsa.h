@@ -35,10 +35,21 @@
  *    status code and sets a thread-local message (dsa_last_error); nothing is launched.
  *    A failed launch returns DSA_ERR_HIP.  The library never aborts.
  *  - Zero-sized work (T == 0, n_rows == 0) returns DSA_OK without touching any pointer.
- *  - Device-resident metadata (kv_off, q_req, q_pos, ids, n_valid) cannot be checked on the
- *    host without a synchronisation; the kernels clamp it so that every memory access stays
- *    inside the buffers whose sizes the host arguments describe.  Values that break the
- *    documented contract give unspecified (but memory-safe) results.
+ *  - Device-resident metadata cannot be checked on the host without a synchronisation.  The
+ *    kernels bound what indexes other arrays:
+ *      q_req    a query whose q_req[t] lies outside [0, B) has no admissible position: its
+ *               scores are not written, its ID row is all -1, its read is zero, lse -inf;
+ *      q_pos    any value (n_t is clamped to [0, min(S_b, max_S)]);
+ *      n_valid  clamped to [0, max_n];
+ *      ids      any value outside [0, S_b) is padding;
+ *      paged    no page-table entry past a request's max_pages is read: the indexer scores
+ *               positions at or beyond max_pages * page_size against pool page 0 and the
+ *               read treats them as padding.
+ *    Two things are trusted, and breaking them is undefined behaviour (the library is never
+ *    told the cache sizes):
+ *      kv_off   0 <= kv_off[0] <= kv_off[1] <= ... <= kv_off[B] <= rows of every cache
+ *               array the call reads;
+ *      pages    every page-table entry a request uses names a page inside the pools.
  *
  * Request layout (stages 2-4).  B requests; request b owns the key/latent rows
  * [kv_off[b], kv_off[b+1]) of the packed caches, so its length is S_b = kv_off[b+1]-kv_off[b].

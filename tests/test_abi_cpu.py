@@ -157,6 +157,124 @@ def test_binding_refuses_host_tensors():
         dsa.index_keys_layernorm(torch.zeros(4, 128), torch.ones(128), torch.zeros(128))
 
 
+def _binding_calls(torch):
+    """Well-formed arguments for every binding entry point, as CPU tensors (the GPU check
+    comes last, so each call below reaches every shape and dtype check and then stops)."""
+    bf, i32, i64, f32, u8 = torch.bfloat16, torch.int32, torch.int64, torch.float32, torch.uint8
+    z = torch.zeros
+    T, B, S = 4, 2, 100
+    lay = dict(kv_off=z(B + 1, dtype=i64), q_req=z(T, dtype=i32), q_pos=z(T, dtype=i32))
+    iq = dict(q_idx=z(T, 32, 128, dtype=bf), w=z(T, 32, dtype=bf))
+    mla = dict(q=z(T, 96, 576, dtype=bf), latent=z(S, 512, dtype=bf), kpe=z(S, 64, dtype=bf),
+               kv_off=lay["kv_off"], q_req=lay["q_req"], ids=z(T, 2048, dtype=i32))
+    f8 = dict(codes=z(S, 128, dtype=u8), scales=z(S, dtype=f32))
+    return {
+        "index_keys_layernorm": (dsa.index_keys_layernorm, dict(
+            raw=z(S, 128, dtype=f32), gamma=z(128, dtype=f32), beta=z(128, dtype=f32),
+            keys=z(S, 128, dtype=bf))),
+        "indexer_scores": (dsa.indexer_scores, dict(
+            **iq, keys=z(S, 128, dtype=bf), **lay, max_s=S, scores=z(T, S, dtype=f32))),
+        "topk": (dsa.topk, dict(scores=z(T, S, dtype=f32), n_valid=z(T, dtype=i32),
+                                ids=z(T, 2048, dtype=i32))),
+        "indexer_topk": (dsa.indexer_topk, dict(
+            **iq, keys=z(S, 128, dtype=bf), **lay, max_s=S, ids=z(T, 2048, dtype=i32),
+            workspace=z(1 << 20, dtype=u8))),
+        "sparse_mla_attn": (dsa.sparse_mla_attn, dict(
+            **mla, scale=0.07, out=z(T, 96, 512, dtype=bf), lse=z(T, 96, dtype=f32))),
+        "value_gate": (dsa.value_gate, dict(o=z(T, 96, 512, dtype=bf), w_uv=z(96, 128, 512, dtype=bf),
+                                            gate=z(T, 96, 128, dtype=bf), out=z(T, 96, 128, dtype=bf))),
+        "indexer_project": (dsa.indexer_project, dict(
+            c_q=z(T, 1536, dtype=bf), h=z(T, 7168, dtype=bf), w_qi=z(4096, 1536, dtype=bf),
+            w_k=z(128, 7168, dtype=bf), w_w=z(32, 7168, dtype=bf), gamma=z(128, dtype=f32),
+            beta=z(128, dtype=f32), eps=1e-6, keys=z(S, 128, dtype=bf), key_rows=z(T, dtype=i64),
+            q_idx=z(T, 32, 128, dtype=bf), w=z(T, 32, dtype=bf))),
+        "quantize_index_keys_fp8": (dsa.quantize_index_keys_fp8, dict(keys=z(S, 128, dtype=bf), **f8)),
+        "indexer_scores_fp8": (dsa.indexer_scores_fp8, dict(
+            **iq, **f8, **lay, max_s=S, scores=z(T, S, dtype=f32))),
+        "indexer_topk_fp8": (dsa.indexer_topk_fp8, dict(
+            **iq, **f8, **lay, max_s=S, ids=z(T, 2048, dtype=i32))),
+        "indexer_topk_paged": (dsa.indexer_topk_paged, dict(
+            **iq, key_pool=z(128, 128, dtype=bf), page_table=z(B, 2, dtype=i32), page_size=64,
+            **lay, max_s=S, ids=z(T, 2048, dtype=i32))),
+        "sparse_mla_attn_paged": (dsa.sparse_mla_attn_paged, dict(
+            q=mla["q"], latent_pool=z(128, 512, dtype=bf), kpe_pool=z(128, 64, dtype=bf),
+            page_table=z(B, 2, dtype=i32), page_size=64, kv_off=lay["kv_off"],
+            q_req=lay["q_req"], ids=mla["ids"], scale=0.07)),
+    }
+
+
+# (entry point, argument, replacement builder, exception): one bad argument per case; each
+# must be refused by the binding with a message naming the argument, before any launch.
+_BAD_ARGS = [
+    ("index_keys_layernorm", "raw", lambda t: t.zeros(100, 64), ValueError),
+    ("index_keys_layernorm", "raw", lambda t: t.zeros(100, 128, dtype=t.float64), TypeError),
+    ("index_keys_layernorm", "gamma", lambda t: t.zeros(64), ValueError),
+    ("index_keys_layernorm", "keys", lambda t: t.zeros(99, 128, dtype=t.bfloat16), ValueError),
+    ("indexer_scores", "q_idx", lambda t: t.zeros(4, 32, 64, dtype=t.bfloat16), ValueError),
+    ("indexer_scores", "w", lambda t: t.zeros(3, 32, dtype=t.bfloat16), ValueError),
+    ("indexer_scores", "q_req", lambda t: t.zeros(4, dtype=t.int64), TypeError),
+    ("indexer_scores", "q_pos", lambda t: t.zeros(5, dtype=t.int32), ValueError),
+    ("indexer_scores", "kv_off", lambda t: t.zeros(3, dtype=t.int32), TypeError),
+    ("indexer_scores", "keys", lambda t: t.zeros(100, 64, dtype=t.bfloat16), ValueError),
+    ("indexer_scores", "scores", lambda t: t.zeros(4, 50), ValueError),
+    ("indexer_scores", "scores", lambda t: t.zeros(100, 4).t(), ValueError),
+    ("topk", "n_valid", lambda t: t.zeros(4, dtype=t.int64), TypeError),
+    ("topk", "n_valid", lambda t: t.zeros(3, dtype=t.int32), ValueError),
+    ("topk", "ids", lambda t: t.zeros(4, 1024, dtype=t.int32), ValueError),
+    ("topk", "ids", lambda t: t.zeros(4, 2048, dtype=t.int64), TypeError),
+    ("indexer_topk", "ids", lambda t: t.zeros(3, 2048, dtype=t.int32), ValueError),
+    ("indexer_topk", "workspace", lambda t: t.zeros(16, dtype=t.uint8), ValueError),
+    ("sparse_mla_attn", "q", lambda t: t.zeros(4, 96, 512, dtype=t.bfloat16), ValueError),
+    ("sparse_mla_attn", "latent", lambda t: t.zeros(100, 256, dtype=t.bfloat16), ValueError),
+    ("sparse_mla_attn", "kpe", lambda t: t.zeros(100, 64, dtype=t.float32), TypeError),
+    ("sparse_mla_attn", "ids", lambda t: t.zeros(4, 2048, dtype=t.int64), TypeError),
+    ("sparse_mla_attn", "ids", lambda t: t.zeros(4, 1024, dtype=t.int32), ValueError),
+    ("sparse_mla_attn", "q_req", lambda t: t.zeros(5, dtype=t.int32), ValueError),
+    ("sparse_mla_attn", "out", lambda t: t.zeros(4, 96, 512, dtype=t.float16), TypeError),
+    ("sparse_mla_attn", "out", lambda t: t.zeros(4, 96, 128, dtype=t.bfloat16), ValueError),
+    ("sparse_mla_attn", "lse", lambda t: t.zeros(4, 96, dtype=t.bfloat16), TypeError),
+    ("sparse_mla_attn", "lse", lambda t: t.zeros(96, 4).t(), ValueError),
+    ("value_gate", "gate", lambda t: t.zeros(4, 96, 64, dtype=t.bfloat16), ValueError),
+    ("value_gate", "out", lambda t: t.zeros(4, 96, 128, dtype=t.float32), TypeError),
+    ("indexer_project", "h", lambda t: t.zeros(4, 4096, dtype=t.bfloat16), ValueError),
+    ("indexer_project", "key_rows", lambda t: t.zeros(4, dtype=t.int32), TypeError),
+    ("indexer_project", "w", lambda t: t.zeros(4, 16, dtype=t.bfloat16), ValueError),
+    ("quantize_index_keys_fp8", "codes", lambda t: t.zeros(99, 128, dtype=t.uint8), ValueError),
+    ("quantize_index_keys_fp8", "scales", lambda t: t.zeros(100, dtype=t.float64), TypeError),
+    ("indexer_scores_fp8", "scales", lambda t: t.zeros(99), ValueError),
+    ("indexer_topk_fp8", "codes", lambda t: t.zeros(100, 128, dtype=t.int8), TypeError),
+    ("indexer_topk_paged", "page_table", lambda t: t.zeros(3, 2, dtype=t.int32), ValueError),
+    ("indexer_topk_paged", "page_table", lambda t: t.zeros(2, 2, dtype=t.int64), TypeError),
+    ("sparse_mla_attn_paged", "latent_pool", lambda t: t.zeros(128, 500, dtype=t.bfloat16), ValueError),
+    ("sparse_mla_attn_paged", "page_table", lambda t: t.zeros(2, dtype=t.int32), ValueError),
+]
+
+
+def test_binding_checks_every_entry_point_before_any_launch():
+    torch = pytest.importorskip("torch")
+    for name, (fn, kw) in _binding_calls(torch).items():
+        with pytest.raises(TypeError, match="on the GPU"):
+            fn(**kw)  # well-formed: stops at the device check, nothing launched
+
+
+@pytest.mark.parametrize("name,arg,bad,exc", _BAD_ARGS, ids=[f"{c[0]}-{c[1]}-{i}" for i, c in enumerate(_BAD_ARGS)])
+def test_binding_refuses_a_malformed_argument(name, arg, bad, exc):
+    torch = pytest.importorskip("torch")
+    fn, kw = _binding_calls(torch)[name]
+    kw = dict(kw)
+    kw[arg] = bad(torch)
+    with pytest.raises(exc, match=arg):
+        fn(**kw)
+
+
+def test_value_gate_clears_an_earlier_error():
+    lib = dsa.library()
+    assert lib.dsa_value_gate(P(0), P(0), P(0), -1, 96, P(0), P(0)) == INVALID
+    assert last_error()
+    assert lib.dsa_value_gate(P(0), P(0), P(0), 0, 96, P(0), P(0)) == OK
+    assert last_error() == ""
+
+
 def test_value_gate_validation():
     lib = dsa.library()
     vg = lambda o=fake(), w=fake(), g=fake(), T=2, H=96, out=fake(): lib.dsa_value_gate(o, w, g, T, H, out, P(0))
