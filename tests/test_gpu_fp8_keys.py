@@ -159,8 +159,8 @@ def test_indexer_topk_fp8_matches_standalone_topk_and_oracle():
 
 def test_indexer_topk_fp8_long_rows_many_queries():
     """300 chunk queries with 33,001..33,300 admissible positions (more rows than CUs, so the
-    persistent selection): the FP8 selection equals the standalone top-k of the FP8 scores bit
-    for bit, and sampled queries match the oracle over the same codes."""
+    persistent selection): every row's FP8 selection equals the oracle's top-k of the GPU's
+    own FP8 scores bit for bit, and sampled queries match the oracle over the same codes."""
     print("[fp8] indexer_topk long rows", flush=True)
     dsa = dsa_mod()
     lay = synth.prefill_layout("f8p2", 17, 33300, 33000, 300)
@@ -171,17 +171,21 @@ def test_indexer_topk_fp8_long_rows_many_queries():
             dev(lay.q_req), dev(lay.q_pos))
     ids = dsa.indexer_topk_fp8(*args, lay.max_s)
     scores = dsa.indexer_scores_fp8(*args, lay.max_s)
-    n_valid = np.minimum(lay.q_pos + 1, lay.s_len[lay.q_req]).astype(np.int32)
-    ids2 = dsa.topk(scores, dev(n_valid), max_n=lay.max_s)
     torch.cuda.synchronize()
-    assert torch.equal(ids, ids2)
     got = ids.cpu().numpy()
+    s_gpu = scores.cpu().numpy()
+    n_valid = np.minimum(lay.q_pos + 1, lay.s_len[lay.q_req])
+    # every row: the fused selection equals the oracle's top-k of the GPU's own fp32 FP8
+    # scores, bit for bit (identical score arrays)
+    for t in range(lay.T):
+        assert np.array_equal(got[t], O.topk_ids(s_gpu[t, :n_valid[t]])), f"row {t}"
+    # sampled rows: the scores themselves against the oracle over the same codes
     for t in (0, 150, 299):
         one = synth.Layout("f8p2one", 17, [lay.N], np.zeros(1, np.int32), lay.q_pos[t:t + 1])
         ref = O.indexer_scores_fp8(d["q_idx"][t:t + 1], d["w"][t:t + 1], codes, scales,
                                    one.kv_off, one.q_req, one.q_pos)[0]
         valid = got[t][got[t] >= 0]
-        assert len(valid) == 2048 and np.all(got[t][2048:] == -1)
+        assert len(valid) == 2048
         diff = set(valid.tolist()) ^ set(O.topk_ids(ref)[:2048].tolist())
         assert diff <= set(O.selection_band(ref).tolist()), f"query {t}"
 

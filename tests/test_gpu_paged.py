@@ -2,9 +2,10 @@
 
 The paged entry points run the same arithmetic as the contiguous ones on the same logical
 cache, so their results must be identical bit for bit (decode layouts: both use the streaming
-scoring kernel).  A prefill-shaped call, which the contiguous path scores with the prefill
-kernel (another summation order), is checked against the oracle over the unpaged cache:
-selected sets up to the 1e-3 band of the k-th score.
+scoring kernel).  Every paged result is also checked against the oracle over the cache
+unpaged from the pool (the pool read back from the GPU and gathered through the page table
+by the oracle's own routine): selected sets up to the 1e-3 band of the k-th score, and the
+read within 1e-2 (+ half a bf16 ulp for a bf16 output) of the oracle's read of the same IDs.
 """
 import numpy as np
 import pytest
@@ -58,6 +59,30 @@ def page_layout(s_len, page_size, seed, spare=5):
     return pt, len(perm) * page_size, np.concatenate(row_of)
 
 
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_selection_vs_oracle(got, ref):
+    """got [T,2048] GPU IDs, ref: oracle score rows."""
+    for t in range(len(ref)):
+        m = min(len(ref[t]), 2048)
+        valid = got[t][got[t] >= 0]
+        assert len(valid) == m and np.all(got[t][m:] == -1) and np.all(np.diff(valid) > 0), t
+        diff = set(valid.tolist()) ^ set(O.topk_ids(ref[t])[:m].tolist())
+        assert diff <= set(O.selection_band(ref[t]).tolist()), f"query {t}"
+
+
+def check_read_vs_oracle(q_bits, lat_c, kpe_c, kv_off, q_req, ids, got_o, got_l, f32):
+    """The paged read against the oracle's read of the same IDs over the unpaged rows."""
+    ref_o, ref_l = O.sparse_mla(q_bits, lat_c, kpe_c, kv_off, q_req, ids, synth.ATTN_SCALE)
+    half_ulp = 0.0 if f32 else np.where(ref_o != 0, np.ldexp(1.0, np.frexp(np.abs(ref_o))[1] - 9), 0.0)
+    assert np.all(np.abs(got_o - ref_o) <= 1e-2 + half_ulp), f"max err {np.abs(got_o - ref_o).max()}"
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(got_l))
+    assert np.all(np.abs(got_l[fin] - ref_l[fin]) <= 1e-3 * np.maximum(1, np.abs(ref_l[fin])))
+
+
 def to_pool(contig, pool_rows, row_of):
     pool = torch.zeros((pool_rows,) + tuple(contig.shape[1:]), dtype=contig.dtype, device=DEV)
     pool[torch.as_tensor(row_of, device=DEV)] = contig
@@ -83,6 +108,9 @@ def test_indexer_topk_paged_equals_contiguous(page_size, s_len):
     ids_p = dsa.indexer_topk_paged(*args, pool, dev(pt), page_size, *lay_args, lay.max_s)
     torch.cuda.synchronize()
     assert torch.equal(ids, ids_p)
+    unpaged = O.unpage_rows(host_bits(pool), pt, page_size, lay.kv_off)
+    ref = O.indexer_scores(d["q_idx"], d["w"], unpaged, lay.kv_off, lay.q_req, lay.q_pos)
+    check_selection_vs_oracle(ids_p.cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("page_size,packed,f32", [(64, False, False), (128, True, True),
@@ -111,6 +139,10 @@ def test_sparse_mla_paged_equals_contiguous(page_size, packed, f32):
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16) if not f32 else o, op.view(torch.int16) if not f32 else op)
     assert torch.equal(l, lp)
+    lat_c = O.unpage_rows(host_bits(lat_p), pt, page_size, lay.kv_off)
+    kpe_c = O.unpage_rows(host_bits(kpe_p), pt, page_size, lay.kv_off)
+    check_read_vs_oracle(d["q"], lat_c, kpe_c, lay.kv_off, lay.q_req, ids.cpu().numpy(),
+                         op.float().cpu().numpy(), lp.cpu().numpy(), f32)
 
 
 def test_paged_prefill_chunk_against_oracle():
@@ -139,7 +171,8 @@ def test_paged_prefill_chunk_against_oracle():
 
 def test_paged_decode_full_size_equals_contiguous():
     """The 64 x 32768 decode batch, keys and latent in 64-position pages of a permuted pool:
-    the paged selection and read equal the contiguous ones bit for bit."""
+    the paged selection and read equal the contiguous ones bit for bit, and four sampled
+    queries match the oracle over the rows gathered from the pools."""
     print("[paged] full-size decode", flush=True)
     dsa = dsa_mod()
     lay = synth.workload("decode_b64_s32768")
@@ -151,7 +184,6 @@ def test_paged_decode_full_size_equals_contiguous():
     lay_args = (dg["kv_off"], dg["q_req"], dg["q_pos"])
     ids = dsa.indexer_topk(dg["q_idx"], dg["w"], keys, *lay_args, lay.max_s)
     ids_p = dsa.indexer_topk_paged(dg["q_idx"], dg["w"], key_pool, dev(pt), 64, *lay_args, lay.max_s)
-    del key_pool
     lat_pool = to_pool(dg["latent"], pool_rows, row_of)
     kpe_pool = to_pool(dg["kpe"], pool_rows, row_of)
     o, l = dsa.sparse_mla_attn(dg["q"], dg["latent"], dg["kpe"], dg["kv_off"], dg["q_req"], ids,
@@ -161,3 +193,25 @@ def test_paged_decode_full_size_equals_contiguous():
     torch.cuda.synchronize()
     assert torch.equal(ids, ids_p)
     assert torch.equal(o.view(torch.int16), op.view(torch.int16)) and torch.equal(l, lp)
+    # sampled queries against the oracle over rows gathered from the pools by the oracle
+    got = ids_p.cpu().numpy()
+    for t in (0, 21, 42, 63):
+        s_b = int(lay.s_len[t])
+        one_off = np.array([0, s_b], np.int64)
+        n_pages = -(-s_b // 64)
+        # the request's pages, copied out of each pool in page-table order, form a small pool
+        # whose page table is 0 .. n_pages - 1; the oracle unpages that
+        phys = torch.as_tensor(pt[t, :n_pages].astype(np.int64) * 64, device=DEV)
+        idx = (phys[:, None] + torch.arange(64, device=DEV)[None, :]).reshape(-1)
+        pt_local = np.arange(n_pages, dtype=np.int32)[None, :]
+
+        def unpaged(pool):
+            return O.unpage_rows(host_bits(pool[idx]), pt_local, 64, one_off)
+
+        ref = O.indexer_scores(synth.to_bits_np(dg["q_idx"][t:t + 1]),
+                               synth.to_bits_np(dg["w"][t:t + 1]), unpaged(key_pool), one_off,
+                               np.zeros(1, np.int32), np.array([s_b - 1], np.int32))
+        check_selection_vs_oracle(got[t:t + 1], ref)
+        check_read_vs_oracle(synth.to_bits_np(dg["q"][t:t + 1]), unpaged(lat_pool),
+                             unpaged(kpe_pool), one_off, np.zeros(1, np.int32), got[t:t + 1],
+                             op[t:t + 1].float().cpu().numpy(), lp[t:t + 1].cpu().numpy(), False)

@@ -284,6 +284,104 @@ def test_indexer_topk_two_stage_long_rows_bit_exact():
         assert np.array_equal(got[t], O.topk_ids(ref[t])), f"row {t}"
 
 
+def _int_index_inputs(g, t, n_keys):
+    """Integer index queries and keys in {-2..2} and signed power-of-two head weights: every
+    score is exact in fp32 (and in the oracle's fp64), and the scores take few distinct
+    values, so the k-th score is shared by many positions."""
+    q = synth.bf16_bits_from_f32(g.integers(-2, 3, size=(t, 32, 128)))
+    w = synth.bf16_bits_from_f32(2.0 ** g.integers(-4, 2, size=(t, 32)) *
+                                 g.choice([-1, 1], size=(t, 32)))
+    keys = synth.bf16_bits_from_f32(g.integers(-2, 3, size=(n_keys, 128)))
+    return q, w, keys
+
+
+@pytest.mark.parametrize("s_total,q_pos,parts", [
+    (1_048_576, [1_048_575, 1_048_574, 1_000_000, 70_000], 16),
+    (600_000, [599_999, 450_000], 8)])
+def test_indexer_topk_multi_part_merge_bit_exact(s_total, q_pos, parts):
+    """Few rows of up to 1,048,576 positions run the two-stage selection in 8 or 16 parts of
+    >= 65,536 positions, then the merge of the part lists.  All queries read one request, so
+    the rows share their keys; with exact integer scores and many ties across part borders the
+    IDs must equal the oracle's top-2048 (ties to the lower position) bit for bit.  Shorter
+    rows leave trailing parts partly or wholly empty."""
+    print(f"[indexer_topk] {parts}-part merge S={s_total}", flush=True)
+    dsa = dsa_mod()
+    g = np.random.default_rng(18 + parts)
+    lay = synth.Layout(f"merge{parts}", 18, [s_total], np.zeros(len(q_pos), np.int32),
+                       np.array(q_pos, np.int32))
+    assert lay.T < 8 * lay.B  # the streaming scoring kernel, as decode uses
+    q, w, keys = _int_index_inputs(g, lay.T, lay.N)
+    ws = dsa.indexer_topk_workspace_size(lay.T, lay.max_s)
+    assert ws - (lay.T * lay.max_s * 4) >= lay.T * parts * 2048 * 4  # candidate lists of `parts`
+    args = (dev(q), dev(w), dev(keys), dev(lay.kv_off), dev(lay.q_req), dev(lay.q_pos))
+    ids = dsa.indexer_topk(*args, lay.max_s)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    ref = O.indexer_scores(q, w, keys, lay.kv_off, lay.q_req, lay.q_pos)
+    for t in range(lay.T):
+        want = O.topk_ids(ref[t])
+        kth = ref[t][want[-1]] if len(ref[t]) > 2048 else None
+        ties = int(np.sum(ref[t] == np.min(ref[t][want]))) if kth is not None else 0
+        print(f"  row {t}: n={len(ref[t])} ties at the k-th score: {ties}", flush=True)
+        assert np.array_equal(got[t], want), f"row {t}"
+
+
+def test_queries_outside_the_batch_select_and_read_nothing():
+    """q_req values outside [0, B) (B itself and -1): such a query has no admissible position.
+    Its scores are not written, its ID row is all -1 and its read is zero with lse -inf; the
+    other queries' results equal those of a call without the stray queries.  Both scoring
+    kernels (streaming decode and the prefill kernel) and the FP8 variant are covered."""
+    print("[contract] q_req outside [0, B)", flush=True)
+    dsa = dsa_mod()
+    # streaming decode kernel: 3 requests, 5 queries, two of them outside the batch
+    lay = synth.Layout("stray", 19, [3000, 2500, 5000], np.array([0, 3, 1, -1, 2], np.int32),
+                       np.array([2999, 100, 2499, 7, 4999], np.int32))
+    d, keys = idx_inputs(lay, 19)
+    good = [0, 2, 4]
+    base = synth.Layout("stray_ok", 19, [3000, 2500, 5000], lay.q_req[good], lay.q_pos[good])
+    args = (dev(d["q_idx"]), dev(d["w"]), dev(keys), dev(lay.kv_off), dev(lay.q_req), dev(lay.q_pos))
+    s = dsa.indexer_scores(*args, lay.max_s)
+    ids = dsa.indexer_topk(*args, lay.max_s)
+    codes, scales = dsa.quantize_index_keys_fp8(dev(keys))
+    s8 = dsa.indexer_scores_fp8(dev(d["q_idx"]), dev(d["w"]), codes, scales, dev(lay.kv_off),
+                                dev(lay.q_req), dev(lay.q_pos), lay.max_s)
+    ids_ok = dsa.indexer_topk(dev(d["q_idx"][good]), dev(d["w"][good]), dev(keys),
+                              dev(base.kv_off), dev(base.q_req), dev(base.q_pos), base.max_s)
+    dm = synth.inputs_np(lay, parts=("mla",))
+    out, lse = dsa.sparse_mla_attn(dev(dm["q"]), dev(dm["latent"]), dev(dm["kpe"]),
+                                   dev(lay.kv_off), dev(lay.q_req), ids, synth.ATTN_SCALE)
+    out_ok, lse_ok = dsa.sparse_mla_attn(dev(dm["q"][good]), dev(dm["latent"]), dev(dm["kpe"]),
+                                         dev(base.kv_off), dev(base.q_req), ids_ok,
+                                         synth.ATTN_SCALE)
+    torch.cuda.synchronize()
+    for t in (1, 3):
+        assert torch.isnan(s[t]).all() and torch.isnan(s8[t]).all()
+        assert (ids[t] == -1).all()
+        assert (out[t].float() == 0).all() and torch.isneginf(lse[t]).all()
+    assert torch.equal(ids[good], ids_ok)
+    assert torch.equal(out[good].view(torch.int16), out_ok.view(torch.int16))
+    assert torch.equal(lse[good], lse_ok)
+    # prefill kernel (T >= 8 B): one request, 24 queries, four of them outside the batch
+    req = np.zeros(24, np.int32)
+    req[[0, 5, 17, 23]] = [1, -1, 7, 1]
+    pl = synth.Layout("stray_pf", 20, [2000], req, (1900 + np.arange(24)).astype(np.int32))
+    pd, pkeys = idx_inputs(pl, 20)
+    pargs = (dev(pd["q_idx"]), dev(pd["w"]), dev(pkeys), dev(pl.kv_off), dev(pl.q_req),
+             dev(pl.q_pos))
+    ps = dsa.indexer_scores(*pargs, pl.max_s)
+    pids = dsa.indexer_topk(*pargs, pl.max_s)
+    torch.cuda.synchronize()
+    ps_h = ps.cpu().numpy()
+    ok_rows = [t for t in range(pl.T) if pl.q_req[t] == 0]
+    ref = O.indexer_scores(pd["q_idx"], pd["w"], pkeys, pl.kv_off, pl.q_req, pl.q_pos,
+                           rows=ok_rows)
+    for i, t in enumerate(ok_rows):
+        n = len(ref[i])
+        assert np.all(np.abs(ps_h[t, :n] - ref[i]) <= 1e-3 * np.maximum(np.abs(ref[i]), O.row_scale(ref[i])))
+    for t in (0, 5, 17, 23):
+        assert np.all(np.isnan(ps_h[t])) and (pids[t] == -1).all()
+
+
 def test_indexer_topk_prefill():
     print("[indexer_topk] prefill", flush=True)
     dsa = dsa_mod()
