@@ -15,7 +15,8 @@ __all__ = ["DsaError", "library", "index_keys_layernorm", "indexer_scores", "top
            "indexer_project", "indexer_project_workspace_size", "Q_LATENT", "RESIDUAL",
            "quantize_index_keys_fp8", "indexer_scores_fp8", "indexer_topk_fp8",
            "indexer_topk_paged", "sparse_mla_attn_paged",
-           "indexer_topk", "indexer_topk_workspace_size", "sparse_mla_attn",
+           "indexer_topk", "indexer_topk_workspace_size", "indexer_topk_noalloc",
+           "NOALLOC_SCRATCH_BYTES", "sparse_mla_attn",
            "sparse_mla_workspace_size", "INDEX_HEADS", "INDEX_DIM", "TOPK", "MLA_HEADS",
            "LATENT_DIM", "COMPANION_DIM", "VALUE_DIM"]
 
@@ -23,6 +24,7 @@ INDEX_HEADS, INDEX_DIM, TOPK = 32, 128, 2048
 MLA_HEADS, LATENT_DIM, COMPANION_DIM, VALUE_DIM = 96, 512, 64, 128
 QK_DIM = LATENT_DIM + COMPANION_DIM
 Q_LATENT, RESIDUAL = 1536, 7168
+NOALLOC_SCRATCH_BYTES = 32 << 20  # DSA_NOALLOC_SCRATCH_BYTES of include/dsa.h
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_amd.so")
 
@@ -55,6 +57,8 @@ _SIGNATURES = {
     "dsa_indexer_topk_workspace_size": ([_i32, _i64], _sz),
     "dsa_indexer_topk": ([_p, _p, _p, _p, _p, _p, _i32, _i32, _i64, _i32, _i32, _i32, _p, _p, _sz,
                           _p], ctypes.c_int),
+    "dsa_indexer_topk_noalloc": ([_p, _p, _p, _p, _p, _p, _i32, _i32, _i64, _i32, _i32, _i32, _p,
+                                  _p], ctypes.c_int),
     "dsa_sparse_mla_workspace_size": ([_i32, _i32, _i32], _sz),
     "dsa_sparse_mla_attn": ([_p, _p, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _i32, _i32, _f32, _p,
                              _i32, _p, _p, _sz, _p], ctypes.c_int),
@@ -287,6 +291,22 @@ def indexer_topk(q_idx, w, keys, kv_off, q_req, q_pos, max_s: int, k: int = TOPK
         _ptr(q_idx), _ptr(w), _ptr(keys), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b,
         int(max_s), INDEX_HEADS, INDEX_DIM, k, _ptr(ids), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return ids
+
+
+def indexer_topk_noalloc(q_idx, w, keys, kv_off, q_req, q_pos, max_s: int, k: int = TOPK,
+                         ids=None, stream=None):
+    """Stages 2+3 as indexer_topk, with no workspace: the library's own per-GPU scratch array
+    (NOALLOC_SCRATCH_BYTES) holds the scores.  For callers that cannot allocate; calls that
+    overlap on one GPU race.  `ids` may be passed to keep the call itself allocation-free."""
+    t = _index_queries(q_idx, w)
+    b = _layout(kv_off, q_req, q_pos, t)
+    _bits16(keys, "keys", (None, INDEX_DIM))
+    ids = _ids(ids, t, k, q_idx.device)
+    _same_device(q_idx, w, keys, kv_off, q_req, q_pos, ids)
+    _check("dsa_indexer_topk_noalloc", library().dsa_indexer_topk_noalloc(
+        _ptr(q_idx), _ptr(w), _ptr(keys), _ptr(kv_off), _ptr(q_req), _ptr(q_pos), t, b,
+        int(max_s), INDEX_HEADS, INDEX_DIM, k, _ptr(ids), _stream(stream)))
     return ids
 
 

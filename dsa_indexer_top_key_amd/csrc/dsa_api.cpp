@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <mutex>
 
 #include "dsa.h"
 
@@ -201,13 +202,50 @@ static dsa_status_t check_pages(const char* fn, const int32_t* page_table, int32
     return DSA_OK;
 }
 
+// Scratch of the allocation-free entry point (dsa_indexer_topk_noalloc): a file-scope device
+// array that stands in for the caller's workspace.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code the array's name is only a host-side stand-in, so
+// the device address is looked up once per device (with that device current) and only that
+// address is handed to kernels.  The scores and candidate lists it holds are fully written
+// before they are read within one call, so nothing needs clearing between calls; calls that
+// overlap on one GPU share the array and race.
+constexpr size_t kNoAllocScratch = DSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on a device's first call).
+static dsa_status_t scratch_address(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    DSA_REQUIRE(dev >= 0 && dev < kMaxDevices, DSA_ERR_UNSUPPORTED,
+                "%s: device %d beyond the %d devices the scratch table covers", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(DSA_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed: %s", fn,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
+
+// Stages 2+3.  With use_scratch the caller's workspace is ignored and this file's scratch
+// array of the current device is used instead (after every other argument has been checked).
 static dsa_status_t indexer_topk_impl(const char* fn, const uint16_t* q_idx, const uint16_t* w,
                                       const uint16_t* keys, const int64_t* kv_off,
                                       const int32_t* q_req, const int32_t* q_pos, int32_t T,
                                       int32_t B, int64_t max_S, int32_t n_heads, int32_t head_dim,
                                       int32_t topk, int32_t* ids, void* workspace,
                                       size_t workspace_bytes, void* stream,
-                                      const int32_t* page_table, int lg_page, int max_pages) {
+                                      const int32_t* page_table, int lg_page, int max_pages,
+                                      bool use_scratch = false) {
     DSA_REQUIRE(T >= 0, DSA_ERR_INVALID_ARG, "%s: T=%d is negative", fn, T);
     DSA_REQUIRE(topk == DSA_TOPK, DSA_ERR_UNSUPPORTED, "%s: topk=%d unsupported (only %d)", fn,
                 topk, DSA_TOPK);
@@ -217,6 +255,15 @@ static dsa_status_t indexer_topk_impl(const char* fn, const uint16_t* q_idx, con
     if (st != DSA_OK) return st;
     DSA_REQUIRE(ids && aligned(ids, 4), DSA_ERR_INVALID_ARG, "%s: ids null or misaligned", fn);
     const size_t need = dsa_indexer_topk_workspace_size(T, max_S);
+    if (use_scratch) {
+        DSA_REQUIRE(need <= kNoAllocScratch, DSA_ERR_UNSUPPORTED,
+                    "%s: T=%d, max_S=%lld need %zu bytes of scratch, more than the %zu bytes this "
+                    "entry point holds per GPU (use dsa_indexer_topk with a workspace)", fn, T,
+                    static_cast<long long>(max_S), need, kNoAllocScratch);
+        const dsa_status_t st2 = scratch_address(fn, &workspace);
+        if (st2 != DSA_OK) return st2;
+        workspace_bytes = kNoAllocScratch;
+    }
     DSA_REQUIRE(workspace && aligned(workspace, kAlign), DSA_ERR_WORKSPACE,
                 "%s: workspace null or not %zu-byte aligned", fn, kAlign);
     DSA_REQUIRE(workspace_bytes >= need, DSA_ERR_WORKSPACE,
@@ -243,6 +290,17 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
     return indexer_topk_impl("dsa_indexer_topk", q_idx, w, keys, kv_off, q_req, q_pos, T, B,
                              max_S, n_heads, head_dim, topk, ids, workspace, workspace_bytes,
                              stream, nullptr, 0, 0);
+}
+
+dsa_status_t dsa_indexer_topk_noalloc(const uint16_t* q_idx, const uint16_t* w,
+                                      const uint16_t* keys, const int64_t* kv_off,
+                                      const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                      int32_t B, int64_t max_S, int32_t n_heads,
+                                      int32_t head_dim, int32_t topk, int32_t* ids,
+                                      void* stream) {
+    return indexer_topk_impl("dsa_indexer_topk_noalloc", q_idx, w, keys, kv_off, q_req, q_pos, T,
+                             B, max_S, n_heads, head_dim, topk, ids, nullptr, 0, stream, nullptr,
+                             0, 0, /*use_scratch=*/true);
 }
 
 dsa_status_t dsa_indexer_topk_paged(const uint16_t* q_idx, const uint16_t* w,

@@ -161,6 +161,26 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* w, const ui
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Stages 2+3 without any allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, kernels and results as dsa_indexer_topk, without the workspace: the scores and
+ * candidate lists go to a device array of DSA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends (its address is looked up on a device's first
+ * call, with that device current).  The call itself allocates and frees nothing.
+ * Limit: dsa_indexer_topk_workspace_size(T, max_S) <= DSA_NOALLOC_SCRATCH_BYTES (32 MiB: e.g.
+ * 256 queries x 32,768 positions, or 64 x 65,536), else UNSUPPORTED before anything runs.
+ * Calls that overlap on one GPU (different streams, or host threads) share that array and
+ * race; serialise them.  Launch on a stream of the current device.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+dsa_status_t dsa_indexer_topk_noalloc(const uint16_t* q_idx, const uint16_t* w,
+                                      const uint16_t* keys, const int64_t* kv_off,
+                                      const int32_t* q_req, const int32_t* q_pos, int32_t T,
+                                      int32_t B, int64_t max_S, int32_t n_heads,
+                                      int32_t head_dim, int32_t topk, int32_t* ids,
+                                      void* stream);
+
+/*
  * Paged page-pool cache layout (a cache layout variant).  Page "Kimi K3.1 Pro: Sparse-
  * Zugriffe, keine kleinere Historie", section "Warum Top-2048 keinen 2048-Token-Cache
  * bedeutet": page allocation changes the physical cache while the logical [T,2048] position

@@ -110,6 +110,29 @@ def test_indexer_topk_validation_and_workspace():
     assert "required" in last_error()
 
 
+def test_indexer_topk_noalloc_validation():
+    """Every argument check runs before the scratch lookup (the first HIP call), so each
+    malformed call is refused here without a GPU; sizes beyond the scratch array are refused
+    with a message naming the limit."""
+    lib = dsa.library()
+
+    def call(a, k=2048, ids=fake()):
+        return lib.dsa_indexer_topk_noalloc(a["q"], a["w"], a["k"], a["off"], a["req"], a["pos"],
+                                            a["T"], a["B"], a["max_s"], a["H"], a["D"], k, ids, P(0))
+    assert call(idx_args(T=0, q=P(0))) == OK
+    assert call(idx_args(T=-1)) == INVALID
+    assert call(idx_args(), k=1024) == UNSUPPORTED
+    assert call(idx_args(H=16)) == UNSUPPORTED
+    assert call(idx_args(q=P(0))) == INVALID
+    assert call(idx_args(), ids=P(0)) == INVALID
+    assert call(idx_args(max_s=0)) == INVALID
+    # 256 x 32768 fits the 32 MiB array exactly; one more position per row does not
+    assert lib.dsa_indexer_topk_workspace_size(256, 32768) == dsa.NOALLOC_SCRATCH_BYTES
+    assert call(idx_args(T=256, B=256, max_s=32769)) == UNSUPPORTED
+    assert "scratch" in last_error() and str(dsa.NOALLOC_SCRATCH_BYTES) in last_error()
+    assert call(idx_args(T=4, B=4, max_s=1 << 22)) == UNSUPPORTED
+
+
 def test_topk_validation():
     f = dsa.library().dsa_topk
     assert f(P(0), 10, P(0), 0, 10, 2048, P(0), P(0)) == OK
@@ -176,6 +199,8 @@ def _binding_calls(torch):
             **iq, keys=z(S, 128, dtype=bf), **lay, max_s=S, scores=z(T, S, dtype=f32))),
         "topk": (dsa.topk, dict(scores=z(T, S, dtype=f32), n_valid=z(T, dtype=i32),
                                 ids=z(T, 2048, dtype=i32))),
+        "indexer_topk_noalloc": (dsa.indexer_topk_noalloc, dict(
+            **iq, keys=z(S, 128, dtype=bf), **lay, max_s=S, ids=z(T, 2048, dtype=i32))),
         "indexer_topk": (dsa.indexer_topk, dict(
             **iq, keys=z(S, 128, dtype=bf), **lay, max_s=S, ids=z(T, 2048, dtype=i32),
             workspace=z(1 << 20, dtype=u8))),
