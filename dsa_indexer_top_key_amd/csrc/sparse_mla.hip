@@ -68,13 +68,23 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(lds_u16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
+// Output staging (bf16 output): row h of the [96][512] result at stage + h * kStageLd, so the
+// four rows one paired store instruction writes (R, R + 1, R + 4, R + 5) fall at 64-byte bank
+// offsets 0, 64, 0, 64 (two-way at most); the block then leaves it in full 1 KB rows.
+constexpr int kStageLd = kLatent + 32;
+
 // One ring slot: 32 latent rows (1072-byte stride: the rows read by one A-operand fetch, and
 // the four rows behind each 16-lane group of a transposing V read, fall in distinct banks)
 // and 32 companion rows of 128 B whose 16-byte chunks are XOR-swizzled by (row % 8) for the
 // same reason.
 struct MlaSmem {
-    uint16_t lat[kNBuf][kTile * kLatStride];
-    uint16_t kpe[kNBuf][kTile * kCompanion];
+    union {
+        struct {  // the ring
+            uint16_t lat[kNBuf][kTile * kLatStride];
+            uint16_t kpe[kNBuf][kTile * kCompanion];
+        };
+        uint16_t stage[kMlaHeads * kStageLd];  // after the last step: the block's bf16 result
+    };
     int32_t rows[kTopK];                     // the split's IDs, padding replaced by ID 0
     uint32_t tmask[kTopK / kTile];           // per tile: bit r set if row r holds a real ID
     u32x4 pfrag[2][3][64][2];                // P (bf16) in A-operand layout, per head group,
@@ -83,30 +93,55 @@ struct MlaSmem {
     uint32_t wend[4];                        // per wave: 1 + index of its last real ID
     uint32_t redo;                           // some logit exceeded its reference by > 2^32
 };
+static_assert(kMlaHeads * kStageLd <= kNBuf * kTile * (kLatStride + kCompanion),
+              "the output stage fits in the ring");
 
-// Ring copies of one tile (32 rows; padding rows copy row 0 of the request, so every slot
-// holds finite data and every tile is exactly 36 copies).  Every wave copies eight latent
-// rows (rows 8 wave .. 8 wave + 7); the head-group waves interleave theirs with their S^T
-// MFMAs, wave 3 also copies the four blocks of eight companion rows.  Spreading the copies
-// over all four waves keeps enough of them in flight: one wave alone reaches about half the
-// gather rate.
-constexpr bool kGatherNt = false;  // cache hint of the ring copies (rows may repeat across queries)
-constexpr int kConsRows = kTile / 4;            // latent rows per wave (8)
-constexpr int kHelpCopies = kConsRows + kTile / 8;  // wave 3: 8 latent rows + 4 companion blocks
-
-__device__ __forceinline__ void copy_latent_row(int64_t row, const uint16_t* latent,
-                                                int64_t ld_lat, uint32_t lds, int lane) {
-    copy_to_lds<kGatherNt>(latent + row * ld_lat + 8 * lane, lds);
+// Paired bf16 store of one 32 x 32 accumulator tile into the LDS stage (the layout of
+// store_tile_bf16, with LDS row stride kStageLd).  Lane 2j holds column c and lane 2j + 1
+// column c + 1, each for rows R and R + 1 (v[r], v[r + 1]); one DPP swap gives the even lane
+// row R of both columns and the odd lane row R + 1.  Everything is selects and one hardware
+// conversion (v_cvt_pk_bf16_f32, round to nearest even): no branches.
+__device__ __forceinline__ void stage_tile_bf16(uint16_t* stage, int row0, int col0,
+                                                const float (&v)[16], int lane) {
+    const bool odd = lane & 1;
+    const int hh = (lane >> 5) & 1;
+    uint16_t* base = stage + (row0 + 4 * hh + (odd ? 1 : 0)) * kStageLd + col0 + (lane & 30);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        const float send = odd ? v[r] : v[r + 1];
+        const float recv = __uint_as_float(dpp_u32<kDppQuadXor1>(0u, __float_as_uint(send)));
+        const float lo = odd ? recv : v[r];
+        const float hi = odd ? v[r + 1] : recv;
+        const bf16x2 pk = __builtin_convertvector((f32x2{lo, hi}), bf16x2);
+        const int row = 8 * (r >> 2) + (r & 3);
+        *reinterpret_cast<bf16x2*>(base + row * kStageLd) = pk;
+    }
 }
 
-// Companion block kb of a tile: rows 8 kb .. 8 kb + 7, lane -> row 8 kb + lane / 8; the
-// lane's LDS slot holds logical chunk (lane % 8) ^ (row % 8).
-__device__ __forceinline__ void copy_companion_block(int64_t row, int kb, const uint16_t* kpe,
-                                                     int64_t ld_kpe, uint32_t lds, int lane) {
-    const int r = 8 * kb + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    copy_to_lds<kGatherNt>(kpe + row * ld_kpe + 8 * c, lds);
+// The staged [96][512] bf16 result to global memory (dst: 96 contiguous rows of 512): every
+// thread moves 16-byte pieces, a wave one whole 1 KB row per instruction.
+__device__ __forceinline__ void stage_out(const uint16_t* stage, uint16_t* dst, int tid) {
+#pragma unroll 4
+    for (int c = tid; c < kMlaHeads * (kLatent / 8); c += 256) {
+        const int row = c >> 6, piece = c & 63;
+        *reinterpret_cast<u32x4*>(dst + row * kLatent + 8 * piece) =
+            *reinterpret_cast<const u32x4*>(stage + row * kStageLd + 8 * piece);
+    }
 }
+
+// Ring fill of one tile (32 rows; padding rows load row 0 of the request, so every slot holds
+// finite data).  Every wave loads eight latent rows (rows 8 wave .. 8 wave + 7; lane l holds 16
+// bytes at offset 16 l of each 1 KB row) into registers at the start of a step and writes them
+// into the slot at its end; wave 3 also loads the four blocks of eight companion rows.  Plain
+// loads into registers, not direct global->LDS copies: on these random 1 KB rows a gather-only
+// probe moved 2.45 TB/s from HBM with register loads and 1.8 TB/s with the copies (5.2 and
+// 3.1 TB/s from the Infinity Cache), at any ring depth.
+constexpr int kConsRows = kTile / 4;  // latent rows per wave (8)
+
+struct TileRegs {
+    u32x4 lat[kConsRows];   // this wave's latent rows
+    u32x4 kp[kTile / 8];    // wave 3: companion block kb, lane -> row 8 kb + lane / 8
+};
 
 // The per-step base of the transposing V reads, made opaque to the compiler.  Left visible,
 // the compiler splits base + constant into a loop-invariant register per read and re-adds
@@ -164,20 +199,6 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     const int hh = lane >> 5;  // lane half
     const int hl = lane & 31;  // head column (S^T) / A-operand row
     const int L = kTopK >> lsplit;
-    // Head-group waves load their 32 absorbed queries first, so the loads overlap the ID phase.
-    u32x4 qf[kKSteps];
-    if (wave < 3) {
-        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
-#pragma unroll
-        for (int s = 0; s < kKSteps; ++s) {
-            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
-            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
-            // the last kQfInAcc fragments live in accumulation registers (MFMA reads its B
-            // operand from there directly), leaving VGPRs for deep LDS prefetch
-            if (s >= kKSteps - kQfInAcc) asm volatile("" : "+a"(qf[s]));
-        }
-    }
-
     // ---- the split's IDs into LDS: padding (ID < 0 or >= S_b) becomes row 0 of the request
     // (real data, so every ring slot stays finite) and is masked out of the softmax through a
     // per-tile bit mask.  Tiles after the last real ID are not processed.  The ID loads are
@@ -223,51 +244,70 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     if (lane == 0) sm.wend[wave] = end;
     lds_barrier();
     end = max(max(sm.wend[0], sm.wend[1]), max(sm.wend[2], sm.wend[3]));
+    // The head-group waves' 32 absorbed queries, loaded once the ID phase is over and issued
+    // just before the first ring copies, so both travel together.  (Issued earlier, they held
+    // up the ID phase: the compiler cannot count the loads of a branch that only some waves
+    // take, so it waited for all of them before using the first ID.)
+    u32x4 qf[kKSteps];
+    if (wave < 3) {
+        const uint16_t* qh = q + (static_cast<int64_t>(t) * kMlaHeads + 32 * wave + hl) * kQK;
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+            const int d = s < kLatSteps ? 256 * hh + 8 * s : kLatent + 32 * hh + 8 * (s - kLatSteps);
+            qf[s] = *reinterpret_cast<const u32x4*>(qh + d);
+        }
+    }
     const int n_tiles = static_cast<int>((end + kTile - 1) / kTile);
     const int q16 = lane & 15;
     const int vrow = 4 * hh + (q16 >> 2);
     const int vcol = 16 * ((lane >> 4) & 1) + 4 * (q16 & 3);
     const int64_t ps = static_cast<int64_t>(t) * nsplit + split;
 
-    // Ring copies: wave w < 3 copies latent rows 8w .. 8w + 7 of a tile, wave 3 rows 24 .. 31
-    // and the four companion blocks; copies of a tile go to ring slot tile % 3.
+    // Ring fill: wave w < 3 loads latent rows 8w .. 8w + 7 of a tile, wave 3 rows 24 .. 31 and
+    // the four companion blocks (whose 16-byte chunks it XOR-swizzles by row: lane l of block kb
+    // holds chunk (l % 8) ^ (row % 8) of row 8 kb + l / 8); a tile goes to ring slot tile % 3.
     const int row0 = kConsRows * wave;
-    // lanes 0..31 hold the tile's 32 row IDs (the copies read them with readlane)
+    // lanes 0..31 hold the tile's 32 row IDs (the loads read them with readlane)
     auto tile_ids = [&](int tile) -> int { return sm.rows[tile * kTile + (lane & 31)]; };
-    auto copy_row_k = [&](int tile, int rid, int k) {  // k-th latent row of this wave's share
-        const int r = row0 + k;
-        const int64_t row = base + __builtin_amdgcn_readlane(rid, r);
-        copy_latent_row(row, latent, ld_lat,
-                        lds_offset(sm.lat[tile % kNBuf] + r * kLatStride), lane);
-    };
-    auto copy_companions = [&](int tile) {  // wave 3 only
-#pragma unroll
-        for (int kb = 0; kb < kTile / 8; ++kb) {
-            const int64_t row = base + sm.rows[tile * kTile + 8 * kb + (lane >> 3)];
-            copy_companion_block(row, kb, kpe, ld_kpe,
-                                 lds_offset(sm.kpe[tile % kNBuf] + kb * 8 * kCompanion), lane);
-        }
-    };
-    auto copy_all = [&](int tile) {  // this wave's whole share of a tile, back to back
+    auto load_tile = [&](int tile, TileRegs& tr) {
         const int rid = tile_ids(tile);
 #pragma unroll
-        for (int k = 0; k < kConsRows; ++k) copy_row_k(tile, rid, k);
-        if (wave == 3) copy_companions(tile);
-    };
-    // Start of a pass: tiles 0 and 1 in flight, tile 0 published by the first barrier; each
-    // wave's copies of tile 1 land before X_0.
-    auto prologue = [&]() {
-        if (n_tiles > 0) copy_all(0);
-        if (n_tiles > 1) {
-            copy_all(1);
-            if (wave < 3)
-                wait_vmcnt<kConsRows>();
-            else
-                wait_vmcnt<kHelpCopies>();
-        } else {
-            wait_vmcnt<0>();
+        for (int k = 0; k < kConsRows; ++k) {
+            const int64_t row = base + __builtin_amdgcn_readlane(rid, row0 + k);
+            tr.lat[k] = *reinterpret_cast<const u32x4*>(latent + row * ld_lat + 8 * lane);
         }
+        if (wave == 3) {
+#pragma unroll
+            for (int kb = 0; kb < kTile / 8; ++kb) {
+                const int r = 8 * kb + (lane >> 3);
+                const int64_t row = base + sm.rows[tile * kTile + r];
+                tr.kp[kb] = *reinterpret_cast<const u32x4*>(kpe + row * ld_kpe + 8 * ((lane & 7) ^ (r & 7)));
+            }
+        }
+    };
+    auto store_tile = [&](int tile, const TileRegs& tr) {
+        uint16_t* lat_slot = sm.lat[tile % kNBuf];
+#pragma unroll
+        for (int k = 0; k < kConsRows; ++k)
+            *reinterpret_cast<u32x4*>(lat_slot + (row0 + k) * kLatStride + 8 * lane) = tr.lat[k];
+        if (wave == 3) {
+#pragma unroll
+            for (int kb = 0; kb < kTile / 8; ++kb)
+                *reinterpret_cast<u32x4*>(sm.kpe[tile % kNBuf] + kb * 8 * kCompanion + 8 * lane) = tr.kp[kb];
+        }
+    };
+    // Start of a pass: tiles 0 and 1 loaded, tile 0 written and published by the first barrier;
+    // tile 1 is written before X_0.
+    TileRegs tr1;
+    auto prologue = [&]() {
+        TileRegs tr0;
+        if (n_tiles > 0) load_tile(0, tr0);
+        if (n_tiles > 1) load_tile(1, tr1);
+        if (n_tiles > 0) store_tile(0, tr0);
         lds_barrier();  // tile 0 published
+    };
+    auto prologue_end = [&]() {  // before X_0
+        if (n_tiles > 1) store_tile(1, tr1);
     };
 
     // Software pipeline, one barrier per step.  X_i (i >= 0) publishes tile i+1 (ring slot
@@ -284,10 +324,12 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
 #pragma unroll
                 for (int ht = 0; ht < kHelpTiles; ++ht) orest[hg][ht] = f32x16{};
             prologue();
-            wait_vmcnt<0>();
+            prologue_end();
             lds_barrier();  // X_0
             for (int i = 0; i < n_tiles; ++i) {
-                if (i + 2 < n_tiles) copy_all(i + 2);
+                TileRegs trn;
+                const bool fill = i + 2 < n_tiles;
+                if (fill) load_tile(i + 2, trn);
                 // all operands first (one LDS latency), then the 30 MFMAs back to back
                 lds_u16* vbase = opaque_lds((lds_u16*)sm.lat[i % kNBuf] + vrow * kLatStride + vcol);
                 u32x4 pf[3][2];
@@ -307,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
 #pragma unroll
                     for (int hg = 0; hg < 3; ++hg)
                         orest[hg][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pf[hg][c]), vf[c][ht], orest[hg][ht], 0, 0, 0);
-                wait_vmcnt<0>();
+                if (fill) store_tile(i + 2, trn);
                 lds_barrier();  // X_{i+1}
             }
             if (pass == 0) {
@@ -315,10 +357,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
                 if (sm.redo == 0) break;
             }
         }
-        lds_barrier();  // the head groups have published 1/l
+        lds_barrier();  // the head groups have published 1/l (the ring is idle from here on)
         // destination: the output (one split) or this split's partial, [96][512] either way
         const int64_t dbase = (nsplit > 1 ? ps : static_cast<int64_t>(t)) * kMlaHeads * kLatent;
         void* dst = nsplit > 1 ? part_o : out;
+        uint16_t* stage = sm.stage;
 #pragma unroll
         for (int hg = 0; hg < 3; ++hg)
 #pragma unroll
@@ -329,8 +372,12 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
                 if (out_f32)
                     store_tile_f32(static_cast<float*>(dst) + dbase, kLatent, 32 * hg, 32 * (kConsTiles + ht), v, lane);
                 else
-                    store_tile_bf16(static_cast<uint16_t*>(dst) + dbase, kLatent, 32 * hg, 32 * (kConsTiles + ht), v, lane);
+                    stage_tile_bf16(stage, 32 * hg, 32 * (kConsTiles + ht), v, lane);
             }
+        if (!out_f32) {  // (uniform)
+            lds_barrier();  // the whole result is staged
+            stage_out(stage, static_cast<uint16_t*>(dst) + dbase, tid);
+        }
         return;
     }
 
@@ -347,8 +394,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     // registers (one accumulation chain: a second one measured no faster and pushed output
     // accumulators out of the AGPRs).  When copy_tile >= 0 this wave's latent rows of that
     // tile are copied one every four K-steps.
-    auto qk_tile = [&](int tile, int copy_tile) -> f32x16 {
-        const int rid = copy_tile >= 0 ? tile_ids(copy_tile) : 0;
+    auto qk_tile = [&](int tile) -> f32x16 {
         const uint16_t* lat_row = sm.lat[tile % kNBuf] + hl * kLatStride + 256 * hh;
         const uint16_t* kpe_row = sm.kpe[tile % kNBuf] + hl * kCompanion;
         // A fragment of K-step s (same K order as qf); companion chunks are swizzled
@@ -365,7 +411,6 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         for (int s = 0; s < kKSteps; ++s) {
             const u32x4 cur = abuf[s % kPrefA];
             if (s + kPrefA < kKSteps) abuf[s % kPrefA] = afrag(s + kPrefA);
-            if ((s & 3) == 1 && (s >> 2) < kConsRows && copy_tile >= 0) copy_row_k(copy_tile, rid, s >> 2);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qf[s]), sacc, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -441,21 +486,35 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         l_run = 0.f;
         overflow = false;
         prologue();
+        // The last kQfInAcc query fragments move to accumulation registers (MFMA reads its B
+        // operand from there directly), leaving VGPRs for deep LDS prefetch.  This is done only
+        // here, after the prologue has waited for tile 0 (and so for the query loads issued
+        // before it): an asm operand makes the compiler wait for the load, and placed right
+        // after each load those waits serialised eleven round trips to memory.
+        if (pass == 0) {
+#pragma unroll
+            for (int s = kKSteps - kQfInAcc; s < kKSteps; ++s) asm volatile("" : "+a"(qf[s]));
+        }
         if (n_tiles > 0) {
             u32x4 p0, p1;
-            softmax_tile(qk_tile(0, -1), p0, p1);
+            softmax_tile(qk_tile(0), p0, p1);
             sm.pfrag[0][wave][lane][0] = p0;
             sm.pfrag[0][wave][lane][1] = p1;
         }
-        wait_vmcnt<0>();
+        prologue_end();
         lds_barrier();  // X_0
         for (int i = 0; i < n_tiles; ++i) {
             // one copy of each part in the loop body (two code paths doubled the register
             // footprint of the output accumulators)
             const bool next = i + 1 < n_tiles;
             u32x4 pn0 = {0u, 0u, 0u, 0u}, pn1 = {0u, 0u, 0u, 0u};
+            // this wave's rows of tile i + 2 are loaded at the start of the step (they have the
+            // whole step to arrive) and written into their slot at its end
+            TileRegs trn;
+            const bool fill = i + 2 < n_tiles;
+            if (fill) load_tile(i + 2, trn);
             if (next) {
-                const f32x16 s_next = qk_tile(i + 1, i + 2 < n_tiles ? i + 2 : -1);
+                const f32x16 s_next = qk_tile(i + 1);
                 softmax_tile(s_next, pn0, pn1);
             }
             pv_tile(i);
@@ -463,7 +522,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
                 sm.pfrag[(i + 1) & 1][wave][lane][0] = pn0;
                 sm.pfrag[(i + 1) & 1][wave][lane][1] = pn1;
             }
-            wait_vmcnt<0>();
+            if (fill) store_tile(i + 2, trn);
             lds_barrier();  // X_{i+1}
         }
         if (pass == 0) {
@@ -495,6 +554,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
     for (int r = 0; r < 16; ++r) ir[r] = __shfl(inv, 8 * (r >> 2) + 4 * hh + (r & 3));
     const int64_t dbase = (nsplit > 1 ? ps : static_cast<int64_t>(t)) * kMlaHeads * kLatent;
     void* dst = nsplit > 1 ? part_o : out;
+    uint16_t* stage = sm.stage;
 #pragma unroll
     for (int nt = 0; nt < kConsTiles; ++nt) {
         float v[16];
@@ -503,7 +563,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(
         if (out_f32)
             store_tile_f32(static_cast<float*>(dst) + dbase, kLatent, head0, 32 * nt, v, lane);
         else
-            store_tile_bf16(static_cast<uint16_t*>(dst) + dbase, kLatent, head0, 32 * nt, v, lane);
+            stage_tile_bf16(stage, head0, 32 * nt, v, lane);
+    }
+    if (!out_f32) {  // (uniform)
+        lds_barrier();  // the whole result is staged
+        stage_out(stage, static_cast<uint16_t*>(dst) + dbase, tid);
     }
 }
 
