@@ -195,9 +195,10 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m, uint32_t acc) {
 // What a launch of topk_kernel selects from:
 //  kRow   -- row t of the score matrix (positions 0 .. n_t-1); writes the positions;
 //  kParts -- part q of row t (block t*P + q): positions q*chunk .. q*chunk+chunk-1 of the
-//            row; writes the part's top-2048 as part-local positions to cand;
-//  kMerge -- the P part lists of row t (P*2048 candidates in ascending position order, the
-//            scores gathered again from the row); writes the selected positions.
+//            row; writes the part's top-2048 as part-local positions to cand, and their keys
+//            (read back from the part's scores, which are in the L2) to cand_keys;
+//  kMerge -- the P part lists of row t (P*2048 candidates in ascending position order, with
+//            their keys); writes the selected positions.
 // A row's top-2048 is always inside the union of its parts' top-2048 lists (an element
 // beaten by 2048 others in its own part is beaten by them in the row), and the tie rule
 // (equal scores: lower position first) is the same at both levels, so the merge is exact.
@@ -264,7 +265,7 @@ template <int E, bool STREAM, bool VEC, int MODE, bool PRE>
 __device__ __forceinline__ void topk_select(
     TopkSmem& sm, const int t, const int part, const int64_t ob,
     const float* __restrict__ scores, int64_t ld, const RowLens& rl, int32_t* __restrict__ ids,
-    int32_t parts, int64_t chunk, const int32_t* __restrict__ cands,
+    int32_t parts, int64_t chunk, const int32_t* __restrict__ cands, uint32_t* __restrict__ cand_keys,
     f32x4* pre, bool pre_rd, const float* next_row, int64_t n_next, f32x4* nxt, bool nxt_rd,
     bool* nxt_issued) {
     static_assert(E % 4 == 0, "elements come in groups of four consecutive positions");
@@ -296,6 +297,11 @@ __device__ __forceinline__ void topk_select(
             *nxt_issued = false;
         }
         for (int i = tid; i < kTopK; i += kTopkThreads) out[i] = i < n_short ? i : -1;
+        if constexpr (MODE == kParts) {
+            const float* prow = scores + static_cast<int64_t>(t) * ld + part * chunk;
+            for (int i = tid; i < kTopK; i += kTopkThreads)
+                cand_keys[ob * kTopK + i] = i < n_short ? score_key(prow[i]) : 0u;
+        }
         return;
     }
     const float* row = scores + static_cast<int64_t>(t) * ld + (MODE == kParts ? part * chunk : 0);
@@ -309,14 +315,15 @@ __device__ __forceinline__ void topk_select(
         for (int g = 0; g < kGroups; ++g) {
             const int64_t p = ch * kChunk + tbase + 256 * g;
             if constexpr (MODE == kMerge) {
+                // the candidates' positions and keys, both read contiguously
+                const int q = static_cast<int>(p / kTopK);  // a group never straddles two lists
+                const int64_t ci = (static_cast<int64_t>(t) * parts + q) * kTopK + (p - q * kTopK);
+                const i32x4 local = *reinterpret_cast<const i32x4*>(cands + ci);
+                const u32x4 kk = *reinterpret_cast<const u32x4*>(cand_keys + ci);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const int64_t pc = p + c;
-                    const int q = static_cast<int>(pc / kTopK);
-                    const int32_t local = cands[(static_cast<int64_t>(t) * parts + q) * kTopK + (pc - q * kTopK)];
-                    const int32_t pos = local >= 0 ? static_cast<int32_t>(q * chunk + local) : -1;
-                    cpos[4 * g + c] = pos;
-                    key[4 * g + c] = pos >= 0 ? score_key(row[pos]) : 0u;
+                    cpos[4 * g + c] = local[c] >= 0 ? static_cast<int32_t>(q * chunk + local[c]) : -1;
+                    key[4 * g + c] = local[c] >= 0 ? kk[c] : 0u;
                 }
             } else if (PRE && g < kPreGroups && pre_rd &&
                        static_cast<int64_t>(wave) * 64 * E + 256 * g + 256 <= n) {  // wave-uniform
@@ -714,8 +721,13 @@ __device__ __forceinline__ void topk_select(
     // (scattered 4-byte stores straight to global memory measured slightly slower)
     lds_barrier();
 #pragma unroll
-    for (int i = static_cast<int>(threadIdx.x); i < kTopK; i += kTopkThreads)
-        out[i] = static_cast<int32_t>(sm.hist[i]);
+    for (int i = static_cast<int>(threadIdx.x); i < kTopK; i += kTopkThreads) {
+        const int32_t v = static_cast<int32_t>(sm.hist[i]);
+        out[i] = v;
+        // a part hands the merge its candidates' keys too (two loads per thread from the part's
+        // scores, just read, so in the L2), sparing the merge 2048 * parts scattered reads
+        if constexpr (MODE == kParts) cand_keys[ob * kTopK + i] = score_key(row[v]);
+    }
 }
 
 // One block per row (or part); PRE: a persistent grid of one block per CU, block b taking
@@ -724,14 +736,15 @@ __device__ __forceinline__ void topk_select(
 template <int E, bool STREAM, bool VEC, int MODE, bool PRE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, const RowLens rl, int32_t* __restrict__ ids,
-    int32_t parts, int64_t chunk, const int32_t* __restrict__ cands, int32_t n_rows) {
+    int32_t parts, int64_t chunk, const int32_t* __restrict__ cands, uint32_t* __restrict__ cand_keys,
+    int32_t n_rows) {
     __shared__ TopkSmem sm;
     if constexpr (!PRE) {
         const int b = static_cast<int>(blockIdx.x);
         const int t = MODE == kParts ? b / parts : b;
         const int part = MODE == kParts ? b - t * parts : 0;
         topk_select<E, STREAM, VEC, MODE, false>(sm, t, part, b, scores, ld, rl, ids, parts,
-                                                 chunk, cands,
+                                                 chunk, cands, cand_keys,
                                                  nullptr, false, nullptr, 0, nullptr, false,
                                                  nullptr);
     } else {
@@ -751,7 +764,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             const int64_t n_next = next ? topk_row_len(tn, rl) : 0;
             bool issued = false;
             topk_select<E, STREAM, VEC, MODE, true>(sm, t, 0, t, scores, ld, rl, ids, parts,
-                                                    chunk, cands, pre, has_pre, next, n_next, nxt,
+                                                    chunk, cands, cand_keys, pre, has_pre, next, n_next, nxt,
                                                     has_pre && nxt_rd, &issued);
             nxt_rd = issued;
         }
@@ -761,15 +774,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 template <int E, bool STREAM, int MODE>
 static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, const RowLens& rl,
                           int32_t* ids, int32_t parts, int64_t chunk, const int32_t* cands,
-                          bool vec, hipStream_t stream) {
+                          uint32_t* cand_keys, bool vec, hipStream_t stream) {
     if (vec)
         hipLaunchKernelGGL((topk_kernel<E, STREAM, true, MODE, false>), dim3(blocks),
                            dim3(kTopkThreads), 0, stream, scores, ld, rl, ids, parts, chunk,
-                           cands, 0);
+                           cands, cand_keys, 0);
     else
         hipLaunchKernelGGL((topk_kernel<E, STREAM, false, MODE, false>), dim3(blocks),
                            dim3(kTopkThreads), 0, stream, scores, ld, rl, ids, parts, chunk,
-                           cands, 0);
+                           cands, cand_keys, 0);
 }
 
 // Compute units of the current device (the persistent grid size), looked up once per device
@@ -790,26 +803,26 @@ static int device_cus() {
 // One selection pass over rows (or parts) of at most `len` elements each.
 template <int MODE>
 static void launch_pass(unsigned blocks, int64_t len, const float* scores, int64_t ld,
-                        const RowLens& rl, int32_t* ids, int32_t parts, int64_t chunk, bool vec,
-                        hipStream_t stream) {
+                        const RowLens& rl, int32_t* ids, int32_t parts, int64_t chunk,
+                        uint32_t* cand_keys, bool vec, hipStream_t stream) {
     if (len <= 4 * kTopkThreads)
-        launch_topk_e<4, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<4, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
     else if (len <= 8 * kTopkThreads)
-        launch_topk_e<8, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<8, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
     else if (len <= 16 * kTopkThreads)
-        launch_topk_e<16, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<16, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
     else if (len <= 32 * kTopkThreads)
-        launch_topk_e<32, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<32, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
     else if (len <= 64 * kTopkThreads && MODE == kRow && vec) {
         // persistent blocks with the next row's LDS prefetch (one block per CU)
         const unsigned grid = std::min(blocks, static_cast<unsigned>(device_cus()));
         hipLaunchKernelGGL((topk_kernel<64, false, true, kRow, true>), dim3(grid),
                            dim3(kTopkThreads), 0, stream, scores, ld, rl, ids, parts, chunk,
-                           nullptr, static_cast<int32_t>(blocks));
+                           nullptr, nullptr, static_cast<int32_t>(blocks));
     } else if (len <= 64 * kTopkThreads)
-        launch_topk_e<64, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<64, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
     else
-        launch_topk_e<16, true, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, vec, stream);
+        launch_topk_e<16, true, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
 }
 
 // Parts per row for the two-stage selection: rows are split while fewer than 256 blocks
@@ -823,9 +836,11 @@ int topk_parts(int32_t T, int64_t max_n) {
     return p;
 }
 
+// Candidate lists of a split selection: positions [T * parts, 2048] int32, then their keys
+// [T * parts, 2048] u32.
 size_t topk_workspace_bytes(int32_t T, int64_t max_n) {
     const int p = topk_parts(T, max_n);
-    return p > 1 ? static_cast<size_t>(T) * p * kTopK * sizeof(int32_t) : 0;
+    return p > 1 ? static_cast<size_t>(T) * p * kTopK * 2 * sizeof(int32_t) : 0;
 }
 
 // Either n_valid (explicit row lengths) or (kv_off, q_req, q_pos) of B requests gives each
@@ -838,25 +853,27 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* n_valid,
     const bool vec = (reinterpret_cast<uintptr_t>(scores) % 16 == 0) && (ld % 4 == 0);
     const int parts = cand_ws ? topk_parts(T, max_n) : 1;
     if (parts == 1) {
-        launch_pass<kRow>(static_cast<unsigned>(T), max_n, scores, ld, rl, ids, 1, 0, vec, stream);
+        launch_pass<kRow>(static_cast<unsigned>(T), max_n, scores, ld, rl, ids, 1, 0, nullptr, vec,
+                          stream);
         return hipGetLastError();
     }
     // parts start 16-byte aligned: chunk is a multiple of 4096 elements
     int64_t chunk = (max_n + parts - 1) / parts;
     chunk = (chunk + 4095) & ~static_cast<int64_t>(4095);
+    uint32_t* cand_keys = reinterpret_cast<uint32_t*>(cand_ws + static_cast<int64_t>(T) * parts * kTopK);
     launch_pass<kParts>(static_cast<unsigned>(T * parts), chunk, scores, ld, rl, cand_ws, parts,
-                        chunk, vec, stream);
+                        chunk, cand_keys, vec, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned blocks = static_cast<unsigned>(T);
     if (parts == 2)
-        launch_topk_e<4, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, false, stream);
+        launch_topk_e<4, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, cand_keys, false, stream);
     else if (parts == 4)
-        launch_topk_e<8, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, false, stream);
+        launch_topk_e<8, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, cand_keys, false, stream);
     else if (parts == 8)
-        launch_topk_e<16, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, false, stream);
+        launch_topk_e<16, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, cand_keys, false, stream);
     else
-        launch_topk_e<32, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, false, stream);
+        launch_topk_e<32, false, kMerge>(blocks, scores, ld, rl, ids, parts, chunk, cand_ws, cand_keys, false, stream);
     return hipGetLastError();
 }
 
