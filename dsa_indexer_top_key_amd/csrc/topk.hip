@@ -79,8 +79,8 @@ constexpr uint32_t kFastCand = 64;  // threshold bins up to this size are resolv
 
 // Exclusive prefix sum over the block (thread order); returns this thread's exclusive sum
 // and writes the block total to *total (all threads).  Contains barriers.
-__device__ __forceinline__ uint32_t block_exclusive_scan(TopkSmem& sm, uint32_t v,
-                                                         uint32_t* total) {
+template <class Smem>
+__device__ __forceinline__ uint32_t block_exclusive_scan(Smem& sm, uint32_t v, uint32_t* total) {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const uint32_t incl = wave_inclusive_scan(v);
     if (lane == 63) sm.wtot[wave] = incl;
@@ -99,7 +99,8 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(TopkSmem& sm, uint32_t 
 
 // Find the bin b* holding the need-th largest candidate: count(bins > b*) < need <=
 // count(bins >= b*).  Writes b* to prm[0] and count(bins > b*) to prm[1].
-__device__ __forceinline__ void find_threshold_bin(TopkSmem& sm, uint32_t need) {
+template <class Smem>
+__device__ __forceinline__ void find_threshold_bin(Smem& sm, uint32_t need) {
     const int tid = threadIdx.x;
     const int hb = kBins - 1 - 2 * tid, lb = hb - 1;
     const uint32_t ch = sm.hist[hb], cl = sm.hist[lb];
@@ -120,7 +121,8 @@ __device__ __forceinline__ void find_threshold_bin(TopkSmem& sm, uint32_t need) 
 }
 
 // Block-wide min/max of up to four u32 values (results broadcast to all threads).
-__device__ __forceinline__ void block_minmax(TopkSmem& sm, uint32_t& a_min, uint32_t& a_max,
+template <class Smem>
+__device__ __forceinline__ void block_minmax(Smem& sm, uint32_t& a_min, uint32_t& a_max,
                                              uint32_t& b_min, uint32_t& b_max) {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     a_min = wave_min_u32(a_min);
@@ -771,6 +773,410 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
 }
 
+// ---- rows of 65537 .. 2^20 elements ------------------------------------------------------
+// Streamed once per radix level (statistics, level 0, refinements, compaction), such a row
+// is read five or more times.  Here it is read about 1.1 times:
+//  pass 1   the max key of every segment of `seg` consecutive positions goes to LDS (seg = 16,
+//           32 or 64, so that a row has 4097 .. 16384 segments);
+//  theta    a value-linear histogram level over the segment maxima (then key-bit levels while
+//           its threshold bin is wide) gives a key theta such that at least 2048 and at most
+//           kSelSegs segments have a maximum >= theta.  Each such
+//           segment holds an element >= theta, so at least 2048 elements are >= theta: the
+//           row's top-2048 lies among them, and all of them lie in those segments;
+//  pass 2   those segments (about 2048: an eighth of a 2^20 row at seg 64) are read again and
+//           their elements >= theta gathered in LDS as (key, list position), where a list
+//           position is the segment's index in the ascending segment list times seg plus the
+//           offset inside the segment -- ascending list position is ascending row position;
+//  select   radix levels over the gathered keys (in registers) find the exact threshold key;
+//           selection bitmaps indexed by list position are ranked by a popcount scan, ties at
+//           the threshold taken in position order, as in the register-resident path.
+// Rows whose maxima are flat (more than kSelSegs segments at or above theta, e.g. many equal
+// scores) or that gather more than kCandCap candidates fall back to the streamed selection,
+// as do rows longer than 2^20; rows of at most 65536 elements take the register path.
+constexpr int kSegSlots = 16384;  // segment maxima of one row
+constexpr int kSelSegs = 4096;    // segments read in pass 2
+constexpr int kCandCap = 8192;    // gathered candidates
+constexpr int64_t kLongMaxN = static_cast<int64_t>(kSegSlots) * 64;
+constexpr int kLongBatch = 8;     // 1 KB loads in flight per wave
+
+struct LongSmem {
+    uint32_t hist[kBins];  // histogram; at the end the output row being staged
+    uint32_t wtot[kTopkWaves];
+    uint32_t red[4][kTopkWaves];
+    uint32_t prm[8];
+    union {
+        uint32_t segmax[kSegSlots];          // pass 1: max key per segment
+        uint32_t bm[2][kSelSegs * 64 / 32];  // (above, tie) bits by list position
+    };
+    uint32_t seglist[kSelSegs];  // segments with maximum >= theta, ascending
+    uint32_t ckey[kCandCap];     // gathered keys ...
+    uint32_t cpos[kCandCap];     // ... and their list positions
+};
+static_assert(sizeof(LongSmem) <= 160 * 1024, "fits the LDS of one CU");
+
+// Max over aligned groups of 2^lg lanes (lg = 2, 3 or 4, block-uniform); every lane of a group
+// receives the group's maximum.
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v, int lg) {
+    v = max(v, dpp_u32<kDppQuadXor1>(v, v));
+    v = max(v, dpp_u32<kDppQuadXor2>(v, v));
+    if (lg >= 3) v = max(v, dpp_u32<kDppRowHalfMirror>(v, v));
+    if (lg >= 4) v = max(v, dpp_u32<kDppRowMirror>(v, v));
+    return v;
+}
+
+// Keys of positions p .. p+3 of a row of n elements (0 for positions >= n), element by element.
+__device__ __forceinline__ u32x4 keys4_guarded(const float* row, int64_t p, int64_t n) {
+    u32x4 k;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k[c] = p + c < n ? score_key(row[p + c]) : 0u;
+    return k;
+}
+
+template <bool VEC, bool NT>
+__device__ __forceinline__ u32x4 keys4(const float* row, int64_t p) {
+    u32x4 k;
+    if constexpr (VEC) {
+        const f32x4* a = reinterpret_cast<const f32x4*>(row + p);
+        const f32x4 v = NT ? __builtin_nontemporal_load(a) : *a;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) k[c] = score_key(v[c]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) k[c] = score_key(row[p + c]);
+    }
+    return k;
+}
+
+// Selection of a row (kRow) or part (kParts) of n elements, 65536 < n <= 2^20; false (the
+// block-uniform verdict) when the row must take the streamed selection instead.
+template <int MODE, bool VEC>
+__device__ __forceinline__ bool long_select(LongSmem& sm, const float* __restrict__ row, const int64_t n,
+                            int32_t* __restrict__ out, uint32_t* __restrict__ out_keys) {
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = n > 4 * 65536 ? 4 : n > 2 * 65536 ? 3 : 2;  // log2 of lanes per segment
+    const int seg_sh = lg + 2;                                   // log2(seg)
+    const int nseg = static_cast<int>((n + (1 << seg_sh) - 1) >> seg_sh);
+
+    // ---- pass 1: one 1 KB load instruction covers positions 256u .. 256u + 255
+    const int n_ins = static_cast<int>((n + 255) >> 8);
+    const int n_full = static_cast<int>(n >> 8);  // instructions wholly inside the row
+    auto emit = [&](int u, const u32x4 k) {
+        const uint32_t m = group_max_u32(max(max(k[0], k[1]), max(k[2], k[3])), lg);
+        if ((lane & ((1 << lg) - 1)) == 0) sm.segmax[(256 * u + 4 * lane) >> seg_sh] = m;
+    };
+    int u = wave;
+    for (; u + (kLongBatch - 1) * kTopkWaves < n_full; u += kLongBatch * kTopkWaves) {
+        u32x4 k[kLongBatch];
+#pragma unroll
+        for (int j = 0; j < kLongBatch; ++j)
+            k[j] = keys4<VEC, true>(row, 256 * static_cast<int64_t>(u + j * kTopkWaves) + 4 * lane);
+#pragma unroll
+        for (int j = 0; j < kLongBatch; ++j) emit(u + j * kTopkWaves, k[j]);
+    }
+    for (; u < n_ins; u += kTopkWaves)  // the last instructions, the partial one included
+        emit(u, keys4_guarded(row, 256 * static_cast<int64_t>(u) + 4 * lane, n));
+    lds_barrier();
+
+    // ---- theta: thread i holds the maxima of segments 16i .. 16i + 15
+    uint32_t sk[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int s = 16 * tid + i;
+        sk[i] = s < nseg ? sm.segmax[s] : 0u;  // every segment below nseg holds an element
+    }
+    uint32_t amin = ~0u, amax = 0u, fmin = ~0u, fmax = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t k = sk[i];
+        amin = min(amin, k - 1u);  // absent (0) wraps to the top
+        amax = max(amax, k);
+        if (k > kKeyNegInf && k < kKeyPosInf) {
+            fmin = min(fmin, k);
+            fmax = max(fmax, k);
+        }
+    }
+    for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;  // ordered by the barriers below
+    if (tid == 0) sm.prm[4] = 0u;                                     // gathered candidates
+    block_minmax(sm, amin, amax, fmin, fmax);
+    amin += 1u;
+    bool value_mode = false;
+    float scale = 0.f, off = 0.f;
+    if (fmin < fmax) {
+        const float lo = key_to_score(fmin);
+        scale = static_cast<float>(kBins) / (key_to_score(fmax) - lo);
+        off = -lo * scale;
+        value_mode = isfinite(scale) && scale > 0.f && isfinite(off);
+    }
+    const int ksh = value_mode ? 0 : shift_for(amax - amin);
+    auto bin_of = [&](uint32_t k) {
+        return value_mode ? value_bin(k, scale, off) : static_cast<int>((k - amin) >> ksh);
+    };
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (sk[i]) atomicAdd(&sm.hist[bin_of(sk[i])], 1u);
+    lds_barrier();
+    find_threshold_bin(sm, kTopK);  // nseg > 4096 maxima, so the bin exists
+    const int bstar = static_cast<int>(sm.prm[0]);
+    uint32_t above = sm.prm[1];     // maxima above the threshold bin
+    uint32_t cand = sm.hist[bstar];  // maxima in it
+    uint32_t rlo, rhi;               // key range of the threshold bin
+    if (value_mode) {                // block-uniform: the keys present in the bin
+        rlo = ~0u;
+        rhi = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (sk[i] && bin_of(sk[i]) == bstar) {
+                rlo = min(rlo, sk[i]);
+                rhi = max(rhi, sk[i]);
+            }
+        uint32_t d0 = ~0u, d1 = 0u;
+        block_minmax(sm, rlo, rhi, d0, d1);
+    } else {
+        const uint64_t lo = static_cast<uint64_t>(amin) + (static_cast<uint64_t>(bstar) << ksh);
+        const uint64_t hi = lo + ((1ull << ksh) - 1);
+        rlo = static_cast<uint32_t>(lo);
+        rhi = hi < amax ? static_cast<uint32_t>(hi) : amax;
+        lds_barrier();  // (hist read above)
+    }
+    // Keys >= rlo number above + cand.  A wide threshold bin (flat or heavy-tailed maxima) is
+    // narrowed by key-bit levels until at most kSelSegs segments remain or it is one key.
+    uint32_t need = kTopK - above;
+    for (int level = 0; level < 4 && above + cand > static_cast<uint32_t>(kSelSegs) && rlo != rhi;
+         ++level) {
+        const int sh = shift_for(rhi - rlo);
+        for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (sk[i] - rlo <= rhi - rlo) atomicAdd(&sm.hist[(sk[i] - rlo) >> sh], 1u);
+        lds_barrier();
+        find_threshold_bin(sm, need);
+        const uint32_t bs = sm.prm[0];
+        above += sm.prm[1];
+        need -= sm.prm[1];
+        cand = sm.hist[bs];
+        const uint64_t nlo = static_cast<uint64_t>(rlo) + (static_cast<uint64_t>(bs) << sh);
+        const uint64_t nhi = nlo + ((1ull << sh) - 1);
+        rlo = static_cast<uint32_t>(nlo);
+        rhi = nhi < rhi ? static_cast<uint32_t>(nhi) : rhi;
+        lds_barrier();
+    }
+    if (above + cand > static_cast<uint32_t>(kSelSegs)) return false;  // block-uniform
+    const uint32_t theta = rlo;  // >= 1: the range holds present maxima only
+    // (at least 2048 maxima are >= theta, each the key of an element of its segment)
+
+    // ---- the segment list, in ascending segment order
+    uint32_t flags = 0u, nf = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const bool f = sk[i] >= theta;  // theta >= 1: absent maxima never pass
+        flags |= (f ? 1u : 0u) << i;
+        nf += f ? 1u : 0u;
+    }
+    uint32_t nsel;  // == above + cand
+    uint32_t slot = block_exclusive_scan(sm, nf, &nsel);  // (all segmax reads are done)
+    if (nsel > static_cast<uint32_t>(kSelSegs)) return false;  // (never: a guard only)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if ((flags >> i) & 1u) sm.seglist[slot++] = static_cast<uint32_t>(16 * tid + i);
+    const int n_words = static_cast<int>(((nsel << seg_sh) + 31) >> 5);
+    for (int i = tid; i < n_words; i += kTopkThreads) {
+        sm.bm[0][i] = 0u;
+        sm.bm[1][i] = 0u;
+    }
+    lds_barrier();
+
+    // ---- pass 2: instruction w covers list entries spi*w .. spi*w + spi - 1 (spi segments of
+    // 2^lg lanes each); lanes past the list, and a partial last segment, are handled apart
+    const int spi = 64 >> lg;
+    const int n_ins2 = static_cast<int>((nsel + spi - 1) / spi);
+    const int my_off = 4 * (lane & ((1 << lg) - 1));
+    for (int w = wave; w < n_ins2; w += kLongBatch * kTopkWaves) {
+        u32x4 k[kLongBatch];
+        int pos[kLongBatch];
+        bool part[kLongBatch];
+#pragma unroll
+        for (int j = 0; j < kLongBatch; ++j) {
+            const int e = spi * (w + j * kTopkWaves) + (lane >> lg);
+            const bool in = e < static_cast<int>(nsel);
+            pos[j] = in ? (static_cast<int>(sm.seglist[e]) << seg_sh) + my_off : -1;
+            const bool whole = in && pos[j] + 3 < n;
+            part[j] = in && !whole;
+            // lanes without a whole group read the row's first group (in bounds) and discard it
+            k[j] = keys4<VEC, false>(row, whole ? pos[j] : 0);
+            if (!whole) k[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < kLongBatch; ++j) {
+            if (part[j]) k[j] = keys4_guarded(row, pos[j], n);
+            uint64_t m[4];
+            uint32_t cnt = 0u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                m[c] = __ballot(k[j][c] >= theta);  // (absent elements are 0 < theta)
+                cnt += static_cast<uint32_t>(__popcll(m[c]));
+            }
+            if (cnt == 0u) continue;  // wave-uniform
+            uint32_t base = 0u;
+            if (lane == 0) base = atomicAdd(&sm.prm[4], cnt);
+            base = __builtin_amdgcn_readfirstlane(base);
+            const uint32_t lp0 = static_cast<uint32_t>(spi * (w + j * kTopkWaves) + (lane >> lg)) << seg_sh;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t at = mbcnt64(m[c], base);
+                if (((m[c] >> lane) & 1u) && at < static_cast<uint32_t>(kCandCap)) {
+                    sm.ckey[at] = k[j][c];
+                    sm.cpos[at] = lp0 + static_cast<uint32_t>(my_off + c);
+                }
+                base += static_cast<uint32_t>(__popcll(m[c]));
+            }
+        }
+    }
+    lds_barrier();
+    const uint32_t n_cand = sm.prm[4];  // >= nsel >= 2048: each listed segment gives its maximum
+    if (n_cand > static_cast<uint32_t>(kCandCap)) return false;  // block-uniform
+
+    // ---- the exact threshold among the candidates (thread i holds candidates i + 1024 j)
+    constexpr int kCpt = kCandCap / kTopkThreads;
+    uint32_t kc[kCpt];
+    rlo = ~0u;
+    rhi = 0u;
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+        const uint32_t i = static_cast<uint32_t>(tid + kTopkThreads * j);
+        kc[j] = i < n_cand ? sm.ckey[i] : 0u;
+        rlo = min(rlo, kc[j] - 1u);
+        rhi = max(rhi, kc[j]);
+    }
+    {
+        uint32_t d0 = ~0u, d1 = 0u;
+        block_minmax(sm, rlo, rhi, d0, d1);
+    }
+    rlo += 1u;
+    need = kTopK;
+    cand = n_cand;
+    for (int level = 0; level < 4 && cand != need && rlo != rhi; ++level) {
+        const int sh = shift_for(rhi - rlo);
+        for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < kCpt; ++j)
+            if (kc[j] - rlo <= rhi - rlo) atomicAdd(&sm.hist[(kc[j] - rlo) >> sh], 1u);  // in [rlo, rhi]
+        lds_barrier();
+        find_threshold_bin(sm, need);
+        const uint32_t bs = sm.prm[0];
+        need -= sm.prm[1];
+        cand = sm.hist[bs];
+        const uint64_t nlo = static_cast<uint64_t>(rlo) + (static_cast<uint64_t>(bs) << sh);
+        const uint64_t nhi = nlo + ((1ull << sh) - 1);
+        rlo = static_cast<uint32_t>(nlo);
+        rhi = nhi < rhi ? static_cast<uint32_t>(nhi) : rhi;
+        lds_barrier();
+    }
+    // keys above the final range are taken, the range too when taken whole (cand == need);
+    // else it is the single key rlo, of which the first `need` in position order are taken
+    const bool take_all = cand == need;
+    const uint32_t above_min = take_all ? rlo : rlo + 1u;
+    const uint32_t tie_key = take_all ? 0xFFFFFFFFu : rlo;  // never a key when take_all
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+        const uint32_t i = static_cast<uint32_t>(tid + kTopkThreads * j);
+        if (i < n_cand) {
+            const uint32_t lp = sm.cpos[i];
+            if (kc[j] >= above_min) atomicOr(&sm.bm[0][lp >> 5], 1u << (lp & 31));
+            else if (kc[j] == tie_key) atomicOr(&sm.bm[1][lp >> 5], 1u << (lp & 31));
+        }
+    }
+    lds_barrier();
+
+    // ---- ranking: thread i owns bitmap words 8i .. 8i + 7 (list-position order)
+    constexpr int kWpt = kSelSegs * 64 / 32 / kTopkThreads;
+    const int w0 = kWpt * tid;
+    uint32_t sel[kWpt];
+#pragma unroll
+    for (int q = 0; q < kWpt; ++q) sel[q] = w0 + q < n_words ? sm.bm[0][w0 + q] : 0u;
+    if (!take_all) {  // block-uniform: keep the first `need` tie bits
+        uint32_t tw[kWpt], tc = 0u, ttot;
+#pragma unroll
+        for (int q = 0; q < kWpt; ++q) {
+            tw[q] = w0 + q < n_words ? sm.bm[1][w0 + q] : 0u;
+            tc += static_cast<uint32_t>(__popc(tw[q]));
+        }
+        uint32_t before = block_exclusive_scan(sm, tc, &ttot);
+#pragma unroll
+        for (int q = 0; q < kWpt; ++q) {
+            uint32_t x = tw[q];
+            while (x) {
+                const uint32_t low = x & (0u - x);
+                if (before >= need) tw[q] &= ~low;
+                ++before;
+                x &= x - 1u;
+            }
+            sel[q] |= tw[q];
+        }
+    }
+    uint32_t cnt = 0u, stot;
+#pragma unroll
+    for (int q = 0; q < kWpt; ++q) cnt += static_cast<uint32_t>(__popc(sel[q]));
+    uint32_t rank = block_exclusive_scan(sm, cnt, &stot);  // stot == 2048
+    const uint32_t seg_mask = (1u << seg_sh) - 1u;
+#pragma unroll
+    for (int q = 0; q < kWpt; ++q) {
+        uint32_t x = sel[q];
+        while (x) {
+            const uint32_t lp = 32u * static_cast<uint32_t>(w0 + q) + static_cast<uint32_t>(__builtin_ctz(x));
+            const uint32_t p = (sm.seglist[lp >> seg_sh] << seg_sh) + (lp & seg_mask);
+            if (rank < kTopK) sm.hist[rank] = p;
+            ++rank;
+            x &= x - 1u;
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = tid; i < kTopK; i += kTopkThreads) {
+        const int32_t v = static_cast<int32_t>(sm.hist[i]);
+        out[i] = v;
+        if constexpr (MODE == kParts) out_keys[i] = v >= 0 && v < n ? score_key(row[v]) : 0u;
+    }
+    return true;
+}
+
+// One block per row (or part) of a launch whose rows hold up to 2^20 elements.
+template <int MODE, bool VEC>
+__global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(
+    const float* __restrict__ scores, int64_t ld, const RowLens rl, int32_t* __restrict__ ids,
+    int32_t parts, int64_t chunk, uint32_t* __restrict__ cand_keys) {
+    __shared__ union {
+        TopkSmem ts;
+        LongSmem ls;
+    } sm;
+    const int b = static_cast<int>(blockIdx.x);
+    const int t = MODE == kParts ? b / parts : b;
+    const int part = MODE == kParts ? b - t * parts : 0;
+    int64_t n = topk_row_len(t, rl);
+    if (MODE == kParts) {
+        n -= part * chunk;
+        n = n < chunk ? n : chunk;
+        n = n > 0 ? n : 0;
+    }
+    if (n <= 65536) {
+        topk_select<64, false, VEC, MODE, false>(sm.ts, t, part, b, scores, ld, rl, ids, parts, chunk,
+                                                 nullptr, cand_keys, nullptr, false, nullptr, 0,
+                                                 nullptr, false, nullptr);
+        return;
+    }
+    const float* row = scores + static_cast<int64_t>(t) * ld + (MODE == kParts ? part * chunk : 0);
+    if (n <= kLongMaxN &&
+        long_select<MODE, VEC>(sm.ls, row, n, ids + static_cast<int64_t>(b) * kTopK,
+                               cand_keys ? cand_keys + static_cast<int64_t>(b) * kTopK : nullptr))
+        return;
+    lds_barrier();  // the fast path's last LDS reads are done
+    topk_select<16, true, VEC, MODE, false>(sm.ts, t, part, b, scores, ld, rl, ids, parts, chunk,
+                                            nullptr, cand_keys, nullptr, false, nullptr, 0, nullptr,
+                                            false, nullptr);
+}
+
 template <int E, bool STREAM, int MODE>
 static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, const RowLens& rl,
                           int32_t* ids, int32_t parts, int64_t chunk, const int32_t* cands,
@@ -821,6 +1227,12 @@ static void launch_pass(unsigned blocks, int64_t len, const float* scores, int64
                            nullptr, nullptr, static_cast<int32_t>(blocks));
     } else if (len <= 64 * kTopkThreads)
         launch_topk_e<64, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
+    else if (len <= kLongMaxN && vec)
+        hipLaunchKernelGGL((topk_long_kernel<MODE, true>), dim3(blocks), dim3(kTopkThreads), 0,
+                           stream, scores, ld, rl, ids, parts, chunk, cand_keys);
+    else if (len <= kLongMaxN)
+        hipLaunchKernelGGL((topk_long_kernel<MODE, false>), dim3(blocks), dim3(kTopkThreads), 0,
+                           stream, scores, ld, rl, ids, parts, chunk, cand_keys);
     else
         launch_topk_e<16, true, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
 }

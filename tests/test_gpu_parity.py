@@ -194,7 +194,8 @@ def test_topk_bit_exact_on_identical_scores(kind):
                                     (65536, "ints"), (65536, "special"), (65536, "coarse"),
                                     (40000, "coarse"), (40001, "gauss"), (33000, "coarse"),
                                     (50000, "heavy_tail"), (70001, "gauss"),
-                                    (70001, "two_valued"), (200000, "special")])
+                                    (70001, "two_valued"), (200000, "special"),
+                                    (1_000_001, "coarse"), (1_100_000, "gauss")])
 def test_topk_bit_exact_long_rows(n, kind):
     print(f"[topk long] n={n} {kind}", flush=True)
     dsa = dsa_mod()
@@ -205,6 +206,32 @@ def test_topk_bit_exact_long_rows(n, kind):
     got = ids.cpu().numpy()
     for t in range(2):
         assert np.array_equal(got[t], O.topk_ids(rows[t, :n_valid[t]])), f"row {t}"
+
+
+# Row lengths around every switch of the selection of rows of up to 2^20 elements: segments of
+# 64, 32 and 16 positions, rows of at most 65536 (register path), short and empty rows.
+SEGMENT_ROW_LENGTHS = [1 << 20, (1 << 20) - 5, 262_145, 262_144, 200_001, 131_073, 131_072,
+                       65_537, 65_536, 2_049, 0]
+
+
+@pytest.mark.parametrize("kind", ["gauss", "coarse", "special", "heavy_tail", "ints",
+                                  "sorted_up", "sorted_down", "zeros_signed"])
+def test_topk_segment_maxima_rows_bit_exact(kind):
+    """Rows of 65537 .. 2^20 elements select from the elements at or above a threshold taken
+    from segment maxima.  Gaussian, coarse and heavy-tailed rows take that path at every
+    length (coarse ones with ties at the k-th key); sorted rows gather too many candidates and
+    fall back to the streamed selection, and integer, special and signed-zero rows take either
+    path depending on their length (flat maxima fall back).  Every row must equal the oracle."""
+    print(f"[topk segments] {kind}", flush=True)
+    dsa = dsa_mod()
+    ld = 1 << 20
+    n_valid = np.array(SEGMENT_ROW_LENGTHS, np.int32)
+    rows = synth.score_rows_np(41, kind, len(n_valid), ld)
+    ids = dsa.topk(dev(rows), dev(n_valid), max_n=ld)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for t in range(len(rows)):
+        assert np.array_equal(got[t], O.topk_ids(rows[t, :n_valid[t]])), f"row {t} (n={n_valid[t]})"
 
 
 def test_topk_persistent_rows_bit_exact():
