@@ -776,8 +776,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 // ---- rows of 65537 .. 2^20 elements ------------------------------------------------------
 // Streamed once per radix level (statistics, level 0, refinements, compaction), such a row
 // is read five or more times.  Here it is read about 1.1 times:
-//  pass 1   the max key of every segment of `seg` consecutive positions goes to LDS (seg = 16,
-//           32 or 64, so that a row has 4097 .. 16384 segments);
+//  pass 1   the max key of every segment of `seg` consecutive positions goes to LDS (seg = 8 ..
+//           64, the smallest power of two that leaves at most 16384 segments: 8193 .. 16384);
 //  theta    a value-linear histogram level over the segment maxima (then key-bit levels while
 //           its threshold bin is wide) gives a key theta such that at least 2048 and at most
 //           kSelSegs segments have a maximum >= theta.  Each such
@@ -798,6 +798,9 @@ constexpr int kSelSegs = 4096;    // segments read in pass 2
 constexpr int kCandCap = 8192;    // gathered candidates
 constexpr int64_t kLongMaxN = static_cast<int64_t>(kSegSlots) * 64;
 constexpr int kLongBatch = 8;     // 1 KB loads in flight per wave
+// Launches for longer rows take this path.  Register-resident rows select faster: 64 rows of
+// 32768 took 47 us here against 29 us, 4096 rows of up to 65536 took 727 us against 412 us.
+constexpr int64_t kLongMinLaunch = 64 * kTopkThreads;
 
 struct LongSmem {
     uint32_t hist[kBins];  // histogram; at the end the output row being staged
@@ -814,11 +817,11 @@ struct LongSmem {
 };
 static_assert(sizeof(LongSmem) <= 160 * 1024, "fits the LDS of one CU");
 
-// Max over aligned groups of 2^lg lanes (lg = 2, 3 or 4, block-uniform); every lane of a group
+// Max over aligned groups of 2^lg lanes (lg = 0 .. 4, block-uniform); every lane of a group
 // receives the group's maximum.
 __device__ __forceinline__ uint32_t group_max_u32(uint32_t v, int lg) {
-    v = max(v, dpp_u32<kDppQuadXor1>(v, v));
-    v = max(v, dpp_u32<kDppQuadXor2>(v, v));
+    if (lg >= 1) v = max(v, dpp_u32<kDppQuadXor1>(v, v));
+    if (lg >= 2) v = max(v, dpp_u32<kDppQuadXor2>(v, v));
     if (lg >= 3) v = max(v, dpp_u32<kDppRowHalfMirror>(v, v));
     if (lg >= 4) v = max(v, dpp_u32<kDppRowMirror>(v, v));
     return v;
@@ -854,7 +857,10 @@ __device__ __forceinline__ bool long_select(LongSmem& sm, const float* __restric
                             int32_t* __restrict__ out, uint32_t* __restrict__ out_keys) {
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lg = n > 4 * 65536 ? 4 : n > 2 * 65536 ? 3 : 2;  // log2 of lanes per segment
+    // log2 of lanes per segment: the smallest segments (4 << lg positions) that give at most
+    // kSegSlots segments
+    int lg = 0;
+    while (n > (static_cast<int64_t>(kSegSlots) * 4 << lg)) ++lg;
     const int seg_sh = lg + 2;                                   // log2(seg)
     const int nseg = static_cast<int>((n + (1 << seg_sh) - 1) >> seg_sh);
 
@@ -916,7 +922,7 @@ __device__ __forceinline__ bool long_select(LongSmem& sm, const float* __restric
     for (int i = 0; i < 16; ++i)
         if (sk[i]) atomicAdd(&sm.hist[bin_of(sk[i])], 1u);
     lds_barrier();
-    find_threshold_bin(sm, kTopK);  // nseg > 4096 maxima, so the bin exists
+    find_threshold_bin(sm, kTopK);  // more than 8192 maxima, so the bin exists
     const int bstar = static_cast<int>(sm.prm[0]);
     uint32_t above = sm.prm[1];     // maxima above the threshold bin
     uint32_t cand = sm.hist[bstar];  // maxima in it
@@ -1160,7 +1166,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(
         n = n < chunk ? n : chunk;
         n = n > 0 ? n : 0;
     }
-    if (n <= 65536) {
+    if (n <= 64 * kTopkThreads) {  // (the register path is faster for such rows)
         topk_select<64, false, VEC, MODE, false>(sm.ts, t, part, b, scores, ld, rl, ids, parts, chunk,
                                                  nullptr, cand_keys, nullptr, false, nullptr, 0,
                                                  nullptr, false, nullptr);
@@ -1217,6 +1223,9 @@ static void launch_pass(unsigned blocks, int64_t len, const float* scores, int64
         launch_topk_e<8, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
     else if (len <= 16 * kTopkThreads)
         launch_topk_e<16, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
+    else if (len > kLongMinLaunch && len <= kLongMaxN && vec)
+        hipLaunchKernelGGL((topk_long_kernel<MODE, true>), dim3(blocks), dim3(kTopkThreads), 0,
+                           stream, scores, ld, rl, ids, parts, chunk, cand_keys);
     else if (len <= 32 * kTopkThreads)
         launch_topk_e<32, false, MODE>(blocks, scores, ld, rl, ids, parts, chunk, nullptr, cand_keys, vec, stream);
     else if (len <= 64 * kTopkThreads && MODE == kRow && vec) {

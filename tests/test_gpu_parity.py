@@ -209,7 +209,7 @@ def test_topk_bit_exact_long_rows(n, kind):
 
 
 # Row lengths around every switch of the selection of rows of up to 2^20 elements: segments of
-# 64, 32 and 16 positions, rows of at most 65536 (register path), short and empty rows.
+# 64, 32, 16 and 8 positions, rows of at most 65536 (register path), short and empty rows.
 SEGMENT_ROW_LENGTHS = [1 << 20, (1 << 20) - 5, 262_145, 262_144, 200_001, 131_073, 131_072,
                        65_537, 65_536, 2_049, 0]
 
