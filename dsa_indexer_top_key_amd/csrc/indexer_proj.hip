@@ -20,9 +20,11 @@
 // spreads the weight stream over hundreds of blocks; each split writes fp32 partial sums, and
 // one epilogue block per token adds the splits in a fixed order (deterministic), rounds q_idx
 // and w to bf16, and normalises the key in fp32 (mean, biased variance, rsqrt(var + eps),
-// gamma, beta) before rounding it into the cache.  A register-direct variant (each wave
-// loading its operands in MFMA layout, 64 lanes over 64 cache lines per load) measured 3.8x
-// slower at 4096 tokens (480 vs 126 us per call) and 15% slower at 64 (35 vs 30 us).
+// gamma, beta) before rounding it into the cache.  An unsplit query product (large T) rounds
+// its sums to bf16 q_idx in the product kernel itself (no fp32 round trip).  A
+// register-direct variant (each wave loading its operands in MFMA layout, 64 lanes over 64
+// cache lines per load) measured 3.8x slower at 4096 tokens (480 vs 126 us per call) and 15%
+// slower at 64 (35 vs 30 us).
 //
 // Roofline: decode (T = 64) streams 15 MB of weights once -- HBM-bound; a prefill chunk
 // (T = 4096) is 61 GFLOP of contraction -- bound by the matrix cores.
@@ -62,10 +64,16 @@ static ProjSplits proj_splits(int32_t T) {
     return p;
 }
 
+// fp32 partial sums of the query product (none when it is unsplit: its blocks round their sums
+// to bf16 q_idx themselves).
+static size_t q_partial_bytes(const ProjSplits& p, int32_t T) {
+    return p.q_splits > 1 ? static_cast<size_t>(p.q_splits) * T * kQOut * sizeof(float) : 0;
+}
+
 size_t proj_workspace_bytes(int32_t T) {
     if (T <= 0) return 0;
     const ProjSplits p = proj_splits(T);
-    const size_t q = static_cast<size_t>(p.q_splits) * T * kQOut * sizeof(float);
+    const size_t q = q_partial_bytes(p, T);
     const size_t kw = static_cast<size_t>(p.kw_splits) * T * kKWOut * sizeof(float);
     return ((q + 255) & ~static_cast<size_t>(255)) + kw;
 }
@@ -75,14 +83,16 @@ size_t proj_workspace_bytes(int32_t T) {
 // block tile: its A rows and weight rows stream through LDS, shared by the block's four waves
 // (2 x 2, each a 64 x 64 tile of four accumulators), so every operand byte is read from L2
 // once per block.
-// K moves in 64-wide chunks (four MFMA steps, 128 bytes per row) through a three-slot ring
-// filled by direct global->LDS copies two chunks ahead; one barrier per chunk.  Row r of a
+// K moves in 64-wide chunks (four MFMA steps, 128 bytes per row) through a two-slot ring
+// filled by direct global->LDS copies one chunk ahead; one barrier per chunk.  The ring takes
+// 64 KB, so two blocks share a CU and each covers the other's copy latency and barriers (a
+// three-slot ring, one block per CU, measured 5% slower at 4096 tokens and 18% at 64).  Row r of a
 // slot occupies 128 bytes; its 16-byte piece p sits at position p ^ ((r / 2) % 8), so the 16
 // rows an operand read touches (same p) fall in 16 distinct 16-byte bank groups.  Copy d of a
 // chunk moves rows 8d..8d+7 (A rows for d < 16, weight rows for d >= 16): lane 8 rr + c loads
 // piece c ^ ((row / 2) % 8) of row 8d + rr into position c.  At step s lane l supplies
 // row l % 32 and the dims [32 (l / 32) + 8 s, +8) of the chunk, for both operands.
-constexpr int kLdsRing = 3;
+constexpr int kLdsRing = 2;
 constexpr int kLdsSlot = 2 * kLdsTile * kLdsChunk;  // bf16 elements per slot (A then weight)
 constexpr int kLdsCopies = 2 * kLdsTile / 8 / 4;  // 1 KB copies per wave per chunk: 8
 
@@ -93,6 +103,8 @@ struct ProjProduct {
     int n_b0, N, K, cps;
     int col_tiles, row_tiles, blocks;  // blocks = col_tiles * row_tiles * splits
     float* part;         // [splits, M, N]
+    uint16_t* out_bf16;  // unsplit product with N a multiple of 128: [M, N] bf16 written here
+                         // (rounded to nearest even) instead of part
 };
 
 // Both products run in one launch: blocks [0, p0.blocks) take the first product, the rest the
@@ -153,14 +165,15 @@ __global__ __launch_bounds__(256) void proj_gemm_lds_kernel(ProjProduct p0, Proj
     };
 
     f32x16 acc[2][2] = {};
-    issue(0);
-    issue(1);
+#pragma unroll
+    for (int j = 0; j < kLdsRing - 1; ++j) issue(j);
     for (int i = 0; i < n_chunks; ++i) {
-        // this wave's copies of chunk i are done once only the copies of chunk i+1 remain
-        // outstanding; the barrier covers every wave's copies and frees slot (i + 2) % 3
-        wait_vmcnt<kLdsCopies>();
+        // this wave's copies of chunk i are done once only the copies of the kLdsRing - 2
+        // later chunks remain outstanding; the barrier covers every wave's copies and frees
+        // slot (i + kLdsRing - 1) % kLdsRing, chunk i - 1's
+        wait_vmcnt<(kLdsRing - 2) * kLdsCopies>();
         lds_barrier();
-        issue(i + 2);
+        issue(i + kLdsRing - 1);
         const uint16_t* sa = ring[i % kLdsRing];
         const uint16_t* sb = sa + kLdsTile * kLdsChunk;
 #pragma unroll
@@ -184,6 +197,19 @@ __global__ __launch_bounds__(256) void proj_gemm_lds_kernel(ProjProduct p0, Proj
     // no copy may still be writing LDS when the block ends
     wait_vmcnt<0>();
 
+    if (pr.out_bf16) {  // block-uniform
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                float v[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[r] = acc[x][y][r];
+                store_tile_bf16(pr.out_bf16, N, m0 + 64 * wr + 32 * x, n0 + 64 * wc + 32 * y, v,
+                                lane, M);
+            }
+        return;
+    }
     float* out = part + static_cast<int64_t>(split) * M * N;
 #pragma unroll
     for (int x = 0; x < 2; ++x)
@@ -215,7 +241,7 @@ __global__ __launch_bounds__(256) void proj_epilogue_kernel(
     const int j = static_cast<int>(blockIdx.x) - t * parts;
     const int tid = threadIdx.x;
     const int64_t q_stride = static_cast<int64_t>(T) * kQOut;
-    const int c_end = (j + 1) * (kQOut / parts);
+    const int c_end = q_splits > 0 ? (j + 1) * (kQOut / parts) : 0;  // 0 splits: q_idx is done
     for (int n = j * (kQOut / parts) + 2 * tid; n < c_end; n += 512) {
         const float* p = pq + static_cast<int64_t>(t) * kQOut + n;
         f32x2 v = *reinterpret_cast<const f32x2*>(p);
@@ -267,20 +293,22 @@ hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uin
                                uint16_t* w, uint16_t* keys, const int64_t* key_rows,
                                void* workspace, hipStream_t stream) {
     const ProjSplits p = proj_splits(T);
-    const size_t q_bytes = static_cast<size_t>(p.q_splits) * T * kQOut * sizeof(float);
+    const size_t q_bytes = q_partial_bytes(p, T);
     float* pq = static_cast<float*>(workspace);
     float* pkw = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           ((q_bytes + 255) & ~static_cast<size_t>(255)));
     const int mt = ceil_div(T, kLdsTile);
     ProjProduct q{c_q, w_qi, w_qi, kQOut, kQOut, kQLatent, p.q_cps, ceil_div(kQOut, kLdsTile), mt, 0, pq};
     q.blocks = q.col_tiles * mt * p.q_splits;
+    if (p.q_splits == 1) q.out_bf16 = q_idx;  // (N = 4096: whole column tiles)
     ProjProduct kw{h, w_k, w_w, kIndexDim, kKWOut, kResidual, p.kw_cps, ceil_div(kKWOut, kLdsTile), mt, 0, pkw};
     kw.blocks = kw.col_tiles * mt * p.kw_splits;
     // the residual product's blocks (K = 7168) are the longest: dispatched first
     hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(q.blocks + kw.blocks), dim3(256), 0, stream, kw, q, T);
     const int parts = epilogue_parts(T);
     hipLaunchKernelGGL(proj_epilogue_kernel, dim3(T * parts), dim3(256), 0, stream, pq,
-                       p.q_splits, pkw, p.kw_splits, T, gamma, beta, eps, q_idx, w, keys, key_rows,
+                       p.q_splits > 1 ? p.q_splits : 0, pkw, p.kw_splits, T, gamma, beta, eps,
+                       q_idx, w, keys, key_rows,
                        parts);
     return hipGetLastError();
 }

@@ -241,20 +241,25 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// Copy this wave's prefetch groups of a row of n elements (only groups lying wholly inside
-// the row) into its LDS slices: group g of wave w holds positions 64E*w + 256g .. +255.
+// Copy prefetch group g of this wave of a row of n elements into its LDS slice (only if the
+// group lies wholly inside the row): group g of wave w holds positions 64E*w + 256g .. +255.
+// The wave's reads of the slice (previous row) must be done (lgkmcnt 0).
 template <int E>
-__device__ __forceinline__ void topk_prefetch(f32x4* pre, const float* row, int64_t n) {
+__device__ __forceinline__ void topk_prefetch_group(f32x4* pre, const float* row, int64_t n, int g) {
     int lane = lane_id();
     __asm__ volatile("" : "+v"(lane));  // (recomputed per row, see topk_select)
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int64_t base = static_cast<int64_t>(wave) * 64 * E + 256 * g;
+    if (base + 256 <= n)
+        copy_to_lds<true>(row + base + 4 * lane, lds_offset(pre + (wave * kPreGroups + g) * 64));
+}
+
+// All of this wave's prefetch groups of a row.
+template <int E>
+__device__ __forceinline__ void topk_prefetch(f32x4* pre, const float* row, int64_t n) {
     wait_lgkmcnt0();  // the wave's reads of the slices (previous row) are done
 #pragma unroll
-    for (int g = 0; g < kPreGroups; ++g) {
-        const int64_t base = static_cast<int64_t>(wave) * 64 * E + 256 * g;
-        if (base + 256 <= n)
-            copy_to_lds<true>(row + base + 4 * lane, lds_offset(pre + (wave * kPreGroups + g) * 64));
-    }
+    for (int g = 0; g < kPreGroups; ++g) topk_prefetch_group<E>(pre, row, n, g);
 }
 
 // Selection of one row (kRow, kMerge) or part (kParts) by the whole block; ob is the output
@@ -366,9 +371,6 @@ __device__ __forceinline__ void topk_select(
         uint32_t d0 = ~0u, d1 = 0u;
         block_minmax(sm, amin, amax, d0, d1);
     }
-    // Every wave's keys are in registers: the next row's copies now stream while this row is
-    // selected (issued earlier, they would compete with the slower waves' loads of this row).
-    if constexpr (PRE) topk_prefetch<E>(pre, next_row, n_next);
     amin += 1u;
     uint32_t fmin = amin, fmax = amax;
     if (amin <= kKeyNegInf || amax >= kKeyPosInf) {  // block-uniform
@@ -420,6 +422,15 @@ __device__ __forceinline__ void topk_select(
                     const int bin = bin_of(k);
                     if (k) atomicAdd(&sm.hist[bin], 1u);
                     if constexpr (kSaveBins) kbin[e] = k ? static_cast<uint32_t>(bin) : 0xFFFFu;
+                    // Every wave's keys are in registers: the next row's copies now stream
+                    // while this row is selected (issued earlier, they would compete with the
+                    // slower waves' loads of this row).  One copy per eight elements counted:
+                    // issued all at once they stalled the wave (2% slower overall).
+                    if constexpr (PRE) {
+                        if (e == 0) wait_lgkmcnt0();  // (this row's slice reads are done)
+                        if (e % (E / kPreGroups) == E / kPreGroups - 1)
+                            topk_prefetch_group<E>(pre, next_row, n_next, e / (E / kPreGroups));
+                    }
                 }
             }
         };

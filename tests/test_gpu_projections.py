@@ -114,11 +114,12 @@ def test_indexer_project_parity(t_count):
     check_untouched(cache, key_rows)
 
 
-@pytest.mark.parametrize("t", [33, 64, 70, 600])
+@pytest.mark.parametrize("t", [33, 64, 70, 600, 1000])
 def test_indexer_project_exact_on_integer_inputs(t):
     """Small integers: every fp32 sum is exact, so q_idx and w equal the oracle bit for bit;
     the keys are the key LayerNorm of the exact integer projection.  33, 64 and 70 tokens: one
-    ragged 128-row tile and many K splits; 600: four full tiles and a ragged one."""
+    ragged 128-row tile and many K splits; 600: four full tiles and a ragged one; 1000: an
+    unsplit query product (its product kernel writes bf16 q_idx itself), ragged last tile."""
     print(f"[project] exact integers T={t}", flush=True)
     g = np.random.default_rng(90 + t)
     bits = synth.bf16_bits_from_f32
