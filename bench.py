@@ -486,6 +486,34 @@ def cpu_baseline(lay, host, n_total, budget_s=12.0):
 
 
 # ---------------------------------------------------------------------------------------
+def profile_f_rows(dsa, synth, torch, dev, ds, cold):
+    """Cold launches of the post-read value gate and the 64-token projections on the decode
+    batch (the inputs of measure_variants)."""
+    lay = ds.lay
+    dg = synth.inputs_torch(lay, dev, parts=("gate",))
+    u_out = torch.empty((lay.T, 96, 128), dtype=torch.bfloat16, device=dev)
+    cold(lambda: dsa.value_gate(ds.out, dg["w_uv"], dg["gate"], out=u_out), 5)
+    dp = synth.inputs_torch(lay, dev, parts=("proj",))
+    p_keys = torch.empty_like(ds.keys)
+    p_rows = torch.as_tensor((lay.kv_off[1:] - 1).astype(np.int64), device=dev)
+    p_ws = torch.empty(dsa.indexer_project_workspace_size(lay.T), dtype=torch.uint8, device=dev)
+    cold(lambda: dsa.indexer_project(dp["c_q"], dp["h"], dp["w_qi"], dp["w_k"], dp["w_w"],
+                                     dp["gamma"], dp["beta"], synth.LN_EPS, p_keys, p_rows,
+                                     workspace=p_ws), 5)
+
+
+def profile_prefill_projections(dsa, synth, torch, dev, cold):
+    """Cold launches of the projections of the 4096-token chunk."""
+    lay = synth.workload("prefill_t4096_s65536")
+    pp = synth.inputs_torch(lay, dev, parts=("proj",))
+    keys = torch.empty((lay.N, 128), dtype=torch.bfloat16, device=dev)
+    rows = torch.as_tensor(lay.q_pos.astype(np.int64), device=dev)
+    ws = torch.empty(dsa.indexer_project_workspace_size(lay.T), dtype=torch.uint8, device=dev)
+    cold(lambda: dsa.indexer_project(pp["c_q"], pp["h"], pp["w_qi"], pp["w_k"], pp["w_w"],
+                                     pp["gamma"], pp["beta"], synth.LN_EPS, keys, rows,
+                                     workspace=ws), 3)
+
+
 def profile_kernels(dsa, synth, torch, dev, names):
     """A few cold launches of every kernel of the named workloads (for rocprofv3): each launch
     follows the 1 GiB overwrite the timed steps use, so traced durations are comparable with
@@ -507,12 +535,16 @@ def profile_kernels(dsa, synth, torch, dev, names):
             cold(lambda: dsa.topk(scores, n_valid, ids=ds.ids), 5)
             if ds.lay.raw_keys:
                 cold(ds.ln_fill, 3)
+            if name == "decode_b64_s32768":
+                profile_f_rows(dsa, synth, torch, dev, ds, cold)
             del ds, scores, n_valid
         else:
             pc = PrefillChunk(dsa, synth, torch, name, dev)
             cold(pc.step, 2)
             cold(pc.scores_only, 2)
             del pc
+            if name == "prefill_t4096_s65536":
+                profile_prefill_projections(dsa, synth, torch, dev, cold)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     del flush

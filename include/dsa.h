@@ -322,7 +322,8 @@ dsa_status_t dsa_value_gate(const uint16_t* o, const uint16_t* w_uv, const uint1
  *           guarantees they are distinct and inside the cache (device data is not checked).
  * Sums are fp32 (bf16 products are exact), split over K in a fixed order (deterministic).
  * workspace >= dsa_indexer_project_workspace_size(T) bytes, 256-byte aligned (fp32 partial
- *           sums of the split contraction).
+ *           sums of the split contractions; the query product needs none from the T at which
+ *           it is no longer split over K, about 900 tokens).
  * Errors: INVALID_ARG for T < 0, a bad eps or null/misaligned pointers when T > 0;
  * WORKSPACE for a missing, misaligned or short workspace.
  */

@@ -319,7 +319,10 @@ def test_indexer_project_validation_and_workspace():
     need = lib.dsa_indexer_project_workspace_size(64)
     assert need > 0 and need % 256 == 0
     assert lib.dsa_indexer_project_workspace_size(0) == 0
-    assert lib.dsa_indexer_project_workspace_size(4096) >= 4096 * (4096 + 160) * 4
+    # 4096 tokens: the query product is not split (its blocks write bf16 q_idx directly), so
+    # only the residual product's fp32 partials remain: at least one [T, 160] set
+    big = lib.dsa_indexer_project_workspace_size(4096)
+    assert 4096 * 160 * 4 <= big < 4096 * 4096 * 4
 
     def pj(T=64, eps=1e-6, ws=fake(), ws_bytes=need, **kw):
         a = dict(c_q=fake(), h=fake(), w_qi=fake(), w_k=fake(), w_w=fake(), gamma=fake(),
