@@ -113,7 +113,8 @@ def measured_traffic(kernel_file, summary_name):
 # ---------------------------------------------------------------------------------------
 class Clock:
     """Per-step HIP-event timing on the launch stream, cold (a 1 GiB overwrite before each
-    step, outside its events) or warm (steps back to back)."""
+    step, outside its events) or warm (steps back to back); either way a GPU spin queued
+    first keeps the GPU behind the host, so only GPU time falls between a step's events."""
 
     def __init__(self, torch, stream, dev):
         self.torch = torch
@@ -124,12 +125,22 @@ class Clock:
         ev = self.torch.cuda.Event
         return [(ev(enable_timing=True), ev(enable_timing=True)) for _ in range(n)]
 
+    def _spin(self, n):
+        """A GPU spin queued ahead of n steps keeps the GPU behind the host while they are
+        enqueued, so host launch cost never falls between a step's events."""
+        try:
+            with self.torch.cuda.stream(self.stream):
+                self.torch.cuda._sleep(int(2e6) * max(1, n // 10))
+        except (AttributeError, RuntimeError):
+            pass
+
     def cold(self, fn, n, warmup=2):
         torch = self.torch
         for _ in range(warmup):
             fn()
         evs = self._events(n)
         torch.cuda.synchronize()
+        self._spin(n)
         for i, (a, b) in enumerate(evs):
             self.flush_buf.fill_(i & 0x7F)  # 1 GiB written: the next step starts cold
             a.record(self.stream)
@@ -139,18 +150,13 @@ class Clock:
         return np.array([a.elapsed_time(b) for a, b in evs])
 
     def warm(self, fn, n, warmup=2):
-        """Back to back, each step between its own events.  A GPU spin queued first keeps the
-        GPU behind the host while the steps are enqueued, so host launch cost is not timed."""
+        """Back to back, each step between its own events."""
         torch = self.torch
         for _ in range(warmup):
             fn()
         evs = self._events(n)
         torch.cuda.synchronize()
-        try:
-            with torch.cuda.stream(self.stream):
-                torch.cuda._sleep(int(2e6) * max(1, n // 10))
-        except (AttributeError, RuntimeError):
-            pass
+        self._spin(n)
         for a, b in evs:
             a.record(self.stream)
             fn()
