@@ -16,15 +16,15 @@
 // their 32 x 576 absorbed queries live in registers for the whole block, as the B operand
 // of  S^T = C . Q^T  (v_mfma_f32_32x32x16_bf16, M = 32 gathered rows, N = 32 heads), which
 // leaves each lane with one head and 16 rows -- exactly the A-operand layout the P . V
-// product needs, so probabilities never leave registers.  The 32 x 384 output of a head
-// group accumulates in its AGPRs across the split.  The selected rows stream into a
-// three-deep LDS ring through gfx950's direct global->LDS copies, two tiles ahead; every wave
-// issues a quarter of each tile (eight latent rows of 1 KB, one copy each with a wave-uniform
-// address, and one block of eight companion rows).  Wave 3 computes the last 128 latent
-// columns of all 96 heads from P fragments the head groups publish in LDS.  The V operand of
-// P . V (rows x latent dims) is read from the row-major LDS tile with the transposing load
-// ds_read_b64_tr_b16.  Barriers order LDS only, so the ring copies stay in flight across them
-// (each wave waits on its own vmcnt before the barrier that publishes a tile).
+// product needs, so probabilities never leave registers.  The 32 x 352 output of a head
+// group (11 of the 16 latent tiles) accumulates in its registers across the split.  The selected rows stream into a
+// three-deep LDS ring: at the start of a step every wave loads its eight latent rows (1 KB
+// each, wave-uniform address) of the tile two ahead into registers, and wave 3 also the four
+// blocks of eight companion rows; they are written into the tile's slot at the end of the
+// step, before the barrier that publishes it.  Wave 3 computes the last 160 latent columns of
+// all 96 heads from P fragments the head groups publish in LDS.  The V operand of P . V (rows
+// x latent dims) is read from the row-major LDS tile with the transposing load
+// ds_read_b64_tr_b16.
 //
 // Softmax (fp32, log2 domain) uses a fixed per-head reference: the maximum logit of the
 // first tile.  Later probabilities p = 2^(x - ref) may exceed 1; that is exact after the
@@ -32,7 +32,7 @@
 // If any logit exceeds its reference by more than 32 (never for sane data), the split is
 // recomputed once with the exact per-head maximum recorded during the first pass, so no
 // accumulator is ever rescaled in the hot loop (which would not fit the register budget:
-// the 32 x 480 accumulators of a head group already fill the 240 AGPRs it owns).
+// the 32 x 352 accumulators of a head group already fill most of its registers).
 // Splits write normalised partials (in the output's precision: bf16 or fp32) and a
 // log2-sum-exp; a small kernel over all CUs merges them (merging inside the last split of
 // each query measured slower: the agent-scope release/acquire and a merge on only one CU per
