@@ -92,18 +92,25 @@ def layernorm_keys(raw, gamma, beta, eps) -> np.ndarray:
     return layernorm64(np.asarray(raw, dtype=np.float32).astype(np.float64), gamma, beta, eps)
 
 
-def layernorm_term_magnitude(raw, gamma, beta, eps) -> np.ndarray:
-    """|normalised x * gamma| + |beta| per element: the size of the two terms whose sum is the
-    output, which bounds the absolute rounding error of any fp32 evaluation of it.  fp32 raw
-    keys are used as given; float64 rows (an exact projection) are used unrounded."""
+def layernorm_error_scale(raw, gamma, beta, eps) -> np.ndarray:
+    """Per element, the quantity whose multiple bounds the error of an fp32 evaluation of the
+    key LayerNorm (page section "Eine Query durch den Indexer verfolgen", adapter paragraph:
+    FP32 key normalisation):  |gamma| * A / sigma + |x_hat * gamma| * (1 + A / sigma) + |beta|,
+    with A the row's mean absolute value and sigma = sqrt(var + eps).  To first order in the
+    unit roundoff u: the rounded mean is off by a few u * A, which every x - mu carries and
+    the division by sigma scales (first term); the variance, and so 1/sigma, inherits a
+    relative error of a few u * (1 + A / sigma) from the same shift and its own sum (second
+    term); the products and the final add cost a few u of the terms (all three).  Rows whose
+    mean is large against their spread (A >> sigma) are where the first two terms matter."""
     x = np.asarray(raw)
     x = x.astype(np.float64) if x.dtype == np.float64 else x.astype(np.float32).astype(np.float64)
     g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
     b = np.asarray(beta, dtype=np.float32).astype(np.float64)
     eps = float(np.float32(eps))
     mu = x.mean(axis=-1, keepdims=True)
-    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
-    return np.abs((x - mu) / np.sqrt(var + eps) * g) + np.abs(b)
+    sigma = np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+    a_over_s = np.abs(x).mean(axis=-1, keepdims=True) / sigma
+    return np.abs(g) * a_over_s + np.abs((x - mu) / sigma * g) * (1.0 + a_over_s) + np.abs(b)
 
 
 def layernorm_keys_bf16(raw, gamma, beta, eps) -> np.ndarray:

@@ -144,7 +144,7 @@ def test_indexer_project_exact_on_integer_inputs(t):
         x = x.astype(np.int32)
         return np.where(x & 0x8000, -(x & 0x7FFF), x)
     ulp1 = np.abs(ordered(got) - ordered(ref_bits)) <= 1
-    close = np.abs(O.bf16_to_f64(got) - ref["key"]) <= 2.0 ** -16 * O.layernorm_term_magnitude(
+    close = np.abs(O.bf16_to_f64(got) - ref["key"]) <= 2.0 ** -20 * O.layernorm_error_scale(
         ref["k_raw"].astype(np.float32), d["gamma"], d["beta"], synth.LN_EPS)
     assert np.all(ulp1 | close)
     check_untouched(cache, key_rows)

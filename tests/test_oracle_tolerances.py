@@ -92,34 +92,37 @@ def test_selection_band_ties_and_short_rows():
 
 
 # ---------------------------------------------------------------------------------------
-# error magnitudes: equal to the value when every term is non-negative; hand-worked mixed signs
+# error scales and magnitudes: hand-worked rows; equal to the value when every term is
+# non-negative (the magnitudes)
 # ---------------------------------------------------------------------------------------
-def test_layernorm_term_magnitude():
-    """Row a = +-1 alternating: mean 0, biased variance 1, so with eps = 0 the normalised row
-    is a itself.  Row b = 10 a + 7 normalises to the same values (a reduction over the wrong
-    axis would not).  gamma = 2, beta = -3: y = 2 a - 3 in {-1, -5}, and the magnitude
-    |2 a| + |-3| = 5 everywhere (|y| would give 1 at half the elements, dropping |beta| 2)."""
+def test_layernorm_error_scale():
+    """The fp32 error scale |gamma| A/sigma + |x_hat gamma| (1 + A/sigma) + |beta| (A: the
+    row's mean absolute value), on rows worked by hand, eps = 0 unless stated:
+    - a = +-1 alternating: mean 0, sigma 1, A 1, x_hat = a.  gamma 2, beta -3:
+      2 * 1 + 2 * 2 + 3 = 9 everywhere;
+    - 10 a + 7 (values 17, -3): mean 7, sigma 10, A 10, so A/sigma = 1 again and x_hat = a: 9
+      (a reduction over the wrong axis would not give it);
+    - a + 9 (values 10, 8): mean 9, sigma 1, A 9: 2 * 9 + 2 * 10 + 3 = 41, and -(a + 9) the
+      same (the signed mean, -9, in place of A would not give it; |mean| in place of A fails
+      on row a, whose mean is 0);
+    - a with eps = 3: sigma 2, A/sigma 1/2, x_hat = a/2: 2 * 0.5 + 1 * 1.5 + 3 = 5.5;
+    - per-element gamma_d, beta_d on a: |gamma_d| + 2 |gamma_d| + |beta_d|."""
     a = np.tile([1.0, -1.0], 64).astype(np.float32)
-    raw = np.stack([a, 10 * a + 7]).astype(np.float32)
+    raw = np.stack([a, 10 * a + 7, a + 9, -(a + 9)]).astype(np.float32)
     gamma = np.full(128, 2.0, np.float32)
     beta = np.full(128, -3.0, np.float32)
-    assert np.array_equal(O.layernorm_keys(raw, gamma, beta, 0.0), np.stack([2 * a - 3] * 2))
-    assert np.array_equal(O.layernorm_term_magnitude(raw, gamma, beta, 0.0), np.full((2, 128), 5.0))
-    # per-element gamma: element d gets |x_hat_d gamma_d| + |beta_d|
+    want = np.stack([np.full(128, 9.0), np.full(128, 9.0), np.full(128, 41.0), np.full(128, 41.0)])
+    assert np.array_equal(O.layernorm_error_scale(raw, gamma, beta, 0.0), want)
+    assert np.array_equal(O.layernorm_error_scale(raw[:1], gamma, beta, 3.0), np.full((1, 128), 5.5))
     gd = np.arange(128, dtype=np.float32) - 64
     bd = np.linspace(-1, 1, 128).astype(np.float32)
-    want = np.abs(a.astype(np.float64) * gd) + np.abs(bd.astype(np.float64))
-    assert np.array_equal(O.layernorm_term_magnitude(raw[:1], gd, bd, 0.0)[0], want)
-    # non-negative terms (gamma_d takes the sign of x_d - mean, beta >= 0): the magnitude is
-    # the value itself
-    g = np.random.default_rng(3)
-    for _ in range(5):
-        x = g.standard_normal((1, 128)).astype(np.float32)
-        mu = x.astype(np.float64).mean()
-        gam = (np.sign(x[0] - mu) * (0.5 + g.random(128))).astype(np.float32)
-        bet = np.abs(g.standard_normal(128)).astype(np.float32)
-        assert np.allclose(O.layernorm_term_magnitude(x, gam, bet, 1e-6),
-                           O.layernorm_keys(x, gam, bet, 1e-6), rtol=1e-15, atol=0)
+    want_d = 3 * np.abs(gd.astype(np.float64)) + np.abs(bd.astype(np.float64))
+    assert np.array_equal(O.layernorm_error_scale(raw[:1], gd, bd, 0.0)[0], want_d)
+    # float64 rows (an exact projection) are taken unrounded: 1 + 2^-30 is not an fp32 value
+    x64 = np.stack([a.astype(np.float64) + 2.0 ** -30 * np.arange(128)])
+    assert O.layernorm_error_scale(x64, gamma, beta, 0.0).dtype == np.float64
+    assert not np.array_equal(O.layernorm_error_scale(x64, gamma, beta, 0.0),
+                              O.layernorm_error_scale(x64.astype(np.float32), gamma, beta, 0.0))
 
 
 def test_value_gate_magnitude():
