@@ -85,6 +85,12 @@ def proj_alg_bytes(t):
     return weights + t * (1536 + 7168) * 2 + t * (4096 + 32 + 128) * 2
 
 
+def value_gate_bytes(t):
+    """Value up-projection + gate of t queries: W_UV once, o and the gate logits read, the gated
+    values written."""
+    return 96 * 128 * 512 * 2 + t * 96 * (512 + 2 * 128) * 2
+
+
 def proj_flops(t):
     return 2 * t * (1536 * 4096 + 7168 * (128 + 32))
 
@@ -401,7 +407,7 @@ def measure_variants(clock, ds, dsa, synth, torch, dev, n, quick):
     def value_gate():
         dsa.value_gate(ds.out, dg["w_uv"], dg["gate"], out=u_out)
 
-    vg_bytes = 96 * 128 * 512 * 2 + lay.T * 96 * (512 + 2 * 128) * 2  # W_UV, o, gate, out
+    vg_bytes = value_gate_bytes(lay.T)
     mv = float(np.median(clock.cold(value_gate, n)))
     out["post_read_value_gate"] = {"ms": round(mv, 5), "bytes": vg_bytes, "GBps": rate(vg_bytes, mv),
                                    "hbm_frac": round(vg_bytes / (mv * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
