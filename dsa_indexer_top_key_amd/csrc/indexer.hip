@@ -31,13 +31,15 @@ constexpr int kDecodeTile = 16;          // keys per wave step: 4 KB, four 1 KB 
 constexpr int kDecodeRing = 3;           // ring slots per wave (two steps in flight)
 constexpr int kDecodeCopies = kDecodeTile / 4;
 constexpr int kDecodeMaxChunk = 4096;    // keys per block at most (their scores: 16 KB of LDS)
-constexpr int kDecodeMinChunk = 1024;
+constexpr int kDecodeMinChunk = 64;      // one block step
 
 // Keys per block: the whole job spread over about two blocks per CU (64 KB of LDS each, so
 // two fit; all blocks then end at about the same time and the score writes leave as one
-// burst), within [1024, 4096] keys and a multiple of one block step (64 keys).  With one
+// burst), within [64, 4096] keys and a multiple of one block step (64 keys).  With one
 // block (four waves) per CU the MFMA and reduction latency of each tile is no longer hidden
-// (8192-key blocks measured 60% slower).
+// (8192-key blocks measured 60% slower).  Small jobs keep the spread too: 4 queries of 4096
+// positions run 256 blocks of 64 keys (with at least 1024 keys per block they ran 16 blocks,
+// and the indexer + top-k took 20.7 instead of 15.6 us).
 static int64_t decode_chunk(int32_t T, int64_t max_s) {
     int64_t c = (static_cast<int64_t>(T) * max_s + 511) / 512;
     c = (c + 63) & ~static_cast<int64_t>(63);

@@ -45,7 +45,7 @@ constexpr int kF8Tile = 16;                 // keys per wave step: 2 KB, two 1 K
 constexpr int kF8Ring = 3;                  // ring slots per wave (two steps in flight)
 constexpr int kF8Copies = kF8Tile / 8;
 constexpr int kF8MaxChunk = 4096;           // keys per block at most (their scores: 16 KB)
-constexpr int kF8MinChunk = 1024;
+constexpr int kF8MinChunk = 64;             // one block step (small jobs spread too)
 
 int64_t f8_chunk(int32_t T, int64_t max_s) {
     int64_t c = (static_cast<int64_t>(T) * max_s + 511) / 512;
