@@ -68,3 +68,20 @@ def test_projection_and_value_gate_bytes():
     # W_UV 96 x 128 x 512 bf16 once; per query 96 x 512 bf16 read and 96 x 128 bf16 gate logits
     # read and gated values written
     assert bench.value_gate_bytes(64) == 12_582_912 + 9_437_184
+
+
+def test_per_position_bytes_match_the_pages_cache_budget():
+    # The pages' budget: 33 KiB per token over the 24 global layers, i.e. 1,408 bytes per token
+    # and layer = the 128-wide index key (scored at every admissible position) + the 512-wide
+    # latent and 64-wide companion key (gathered at each selected position); at 2^20 tokens
+    # the selection of 2048 is 1/512 of the history.
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_arithmetic.json")))
+    per_layer = g["payload_per_token_KiB"] * 1024 // g["global_layers"]
+    one = synth.Layout("one", 0, [1 << 20], [0], [(1 << 20) - 1])
+    alg = bench.decode_alg(one)
+    key_bytes = (alg["bytes_indexer"] - (32 * 128 + 32) * 2) // (1 << 20)
+    row_bytes = (alg["bytes_mla"] - (96 * 576 + 96 * 512) * 2) // g["topk"]
+    assert key_bytes + row_bytes == per_layer == 1408
+    assert (1 << 20) // g["topk"] == g["selected_fraction_denominator"]
