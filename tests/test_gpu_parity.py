@@ -239,6 +239,28 @@ def test_topk_segment_maxima_rows_bit_exact(kind):
         assert np.array_equal(got[t], O.topk_ids(rows[t, :n_valid[t]])), f"row {t} (n={n_valid[t]})"
 
 
+@pytest.mark.parametrize("max_n,kind", [(3000, "gauss"), (6000, "coarse"), (12000, "special"),
+                                        (30000, "gauss"), (30000, "two_valued"),
+                                        (50000, "heavy_tail"), (1_100_001, "gauss")])
+def test_topk_unaligned_rows_bit_exact(max_n, kind):
+    """Score rows that do not start on 16-byte boundaries (a view one float into its buffer)
+    take the element-wise load path of every row class: 4 .. 64 elements per thread and rows
+    streamed per pass beyond 2^20.  Ragged lengths end inside a group of four."""
+    print(f"[topk unaligned] max_n={max_n} {kind}", flush=True)
+    dsa = dsa_mod()
+    rows = synth.score_rows_np(43, kind, 3, max_n + 1)
+    n_valid = np.array([max_n, max_n - 3, 2049 + max_n % 7], np.int32)
+    full = dev(rows)
+    view = full[:, 1:]
+    assert view.data_ptr() % 16 != 0
+    ids = dsa.topk(view, dev(n_valid), max_n=max_n)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for t in range(3):
+        ref = O.topk_ids(rows[t, 1:1 + n_valid[t]])
+        assert np.array_equal(got[t], ref), f"row {t} (n={n_valid[t]})"
+
+
 def test_topk_persistent_rows_bit_exact():
     """More rows than CUs, each of up to 40000 elements: the selection runs one persistent
     block per CU that prefetches its next row into LDS while selecting the current one.  Row
