@@ -109,6 +109,27 @@ def test_scores_fp8_parity(name, make):
     check_scores(lay, d, codes, scales, s.cpu().numpy())
 
 
+def test_scores_fp8_unaligned_rows():
+    """FP8-key scores into rows that do not start on 16-byte boundaries (an odd row stride,
+    one float into the buffer) are stored element by element, and only at positions < n_t."""
+    print("[fp8] scores unaligned rows", flush=True)
+    lay = synth.decode_layout("f8u", 16, [3, 2049, 5001, 4096])
+    lay.q_pos[-1] = 3001
+    d = synth.inputs_np(lay, parts=("index",))
+    keys = synth.bf16_bits_from_f32(np.random.default_rng(16).standard_normal((lay.N, 128)))
+    codes, scales = quantize(keys)
+    buf = torch.full((lay.T, lay.max_s + 2), float("nan"), dtype=torch.float32, device=DEV)
+    view = buf[:, 1:1 + lay.max_s]
+    assert view.data_ptr() % 16 != 0 and view.stride(0) % 4 != 0
+    dsa_mod().indexer_scores_fp8(dev(d["q_idx"]), dev(d["w"]), dev(codes), dev(scales),
+                                 dev(lay.kv_off), dev(lay.q_req), dev(lay.q_pos), lay.max_s,
+                                 scores=view)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    check_scores(lay, d, codes, scales, b[:, 1:1 + lay.max_s])
+    assert np.all(np.isnan(b[:, 0])) and np.all(np.isnan(b[:, -1]))
+
+
 def test_scores_fp8_exact_on_integer_inputs():
     """Integer keys up to 8 quantise exactly (scale 2^-5, codes up to 256) and integer queries
     with power-of-two weights keep every fp32 sum exact: bit-exact scores."""

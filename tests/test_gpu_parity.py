@@ -138,6 +138,26 @@ def test_scores_decode_kernel(name, s_len):
     check_scores(lay, d, keys, run_scores(lay, d, keys))
 
 
+def test_scores_decode_kernel_unaligned_rows():
+    """Score rows that do not start on 16-byte boundaries (an odd row stride, one float into
+    the buffer) are stored element by element: every admissible score is right, and nothing
+    is written past n_t, before the row or after it."""
+    print("[scores decode] unaligned rows", flush=True)
+    dsa = dsa_mod()
+    lay = synth.decode_layout("unal", 12, [3, 2049, 5001, 4096])
+    lay.q_pos[-1] = 3001
+    d, keys = idx_inputs(lay, 12)
+    buf = torch.full((lay.T, lay.max_s + 2), float("nan"), dtype=torch.float32, device=DEV)
+    view = buf[:, 1:1 + lay.max_s]
+    assert view.data_ptr() % 16 != 0 and view.stride(0) % 4 != 0
+    dsa.indexer_scores(dev(d["q_idx"]), dev(d["w"]), dev(keys), dev(lay.kv_off),
+                       dev(lay.q_req), dev(lay.q_pos), lay.max_s, scores=view)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    check_scores(lay, d, keys, b[:, 1:1 + lay.max_s])
+    assert np.all(np.isnan(b[:, 0])) and np.all(np.isnan(b[:, -1]))
+
+
 def test_scores_prefill_kernel_one_request():
     print("[scores prefill] one request", flush=True)
     s = 3000
