@@ -535,8 +535,12 @@ def check_mla(lay, d, ids, got_o, got_l, scale=synth.ATTN_SCALE, f32=False):
     assert np.all(got_l[~fin] == -np.inf) and np.all(got_o[~np.isfinite(ref_l)] == 0)
 
 
+# Query counts that give every split count of the read: 16 (1 and 4 queries), 8 (40), 4 (64),
+# 2 (130) and 1 (300), each merged by its own combine.
 @pytest.mark.parametrize("t_count,packed,f32", [(1, False, False), (4, True, True),
+                                                (40, False, False), (40, True, True),
                                                 (64, False, False), (64, False, True),
+                                                (130, False, True), (130, True, False),
                                                 (300, False, False), (300, True, True)])
 def test_sparse_mla_parity(t_count, packed, f32):
     print(f"[mla] T={t_count} packed={packed} f32={f32}", flush=True)
