@@ -335,6 +335,36 @@ def test_indexer_topk_matches_oracle_and_standalone_topk(name, s_len):
     check_selection(lay, ids.cpu().numpy(), ref)
 
 
+def test_decode_several_queries_per_request():
+    """A decode batch with three queries per request at its last three positions (fewer than
+    eight per request on average, so the per-query scoring kernel runs; the queries of one
+    request see prefixes one position apart).  Scores, the fused selection (equal to the
+    standalone one, and to the oracle's set up to the band) and the read of the selected rows
+    all match the oracle; one request is shorter than 2048 positions."""
+    print("[decode] three queries per request", flush=True)
+    dsa = dsa_mod()
+    s_len = np.array([3000, 2100, 5000, 40, 2049])
+    q_req = np.repeat(np.arange(5), 3).astype(np.int32)
+    q_pos = (s_len[q_req] - 3 + np.tile(np.arange(3), 5)).astype(np.int32)
+    lay = synth.Layout("multi", 21, s_len, q_req, q_pos)
+    assert lay.T < 8 * lay.B
+    d, keys = idx_inputs(lay, 21)
+    check_scores(lay, d, keys, run_scores(lay, d, keys))
+    args = (dev(d["q_idx"]), dev(d["w"]), dev(keys), dev(lay.kv_off), dev(lay.q_req),
+            dev(lay.q_pos), lay.max_s)
+    ids = dsa.indexer_topk(*args)
+    n_valid = np.minimum(lay.q_pos + 1, lay.s_len[lay.q_req]).astype(np.int32)
+    ids2 = dsa.topk(dsa.indexer_scores(*args), dev(n_valid), max_n=lay.max_s)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2)
+    got = ids.cpu().numpy()
+    check_selection(lay, got, O.indexer_scores(d["q_idx"], d["w"], keys, lay.kv_off, lay.q_req,
+                                                lay.q_pos))
+    dm = synth.inputs_np(lay, parts=("mla",))
+    got_o, got_l = run_mla(lay, dm, got)
+    check_mla(lay, dm, got, got_o, got_l)
+
+
 def test_indexer_topk_two_stage_long_rows_bit_exact():
     """Few long rows take the two-stage selection (parts of >= 65536 positions, then a merge
     of the part lists).  Integer inputs make every score exact in fp32 and produce many ties,
