@@ -92,7 +92,8 @@ def to_pool(contig, pool_rows, row_of):
 DECODE = [[1, 63, 64, 65, 2047, 2049, 4096, 5000], [70000, 3, 33000]]
 
 
-@pytest.mark.parametrize("page_size", [64, 256])
+# pages smaller than a scoring block's chunk of keys, and one (4096) at least as large
+@pytest.mark.parametrize("page_size", [64, 256, 4096])
 @pytest.mark.parametrize("s_len", DECODE)
 def test_indexer_topk_paged_equals_contiguous(page_size, s_len):
     print(f"[paged] indexer_topk P={page_size} S={s_len}", flush=True)
@@ -114,7 +115,7 @@ def test_indexer_topk_paged_equals_contiguous(page_size, s_len):
 
 
 @pytest.mark.parametrize("page_size,packed,f32", [(64, False, False), (128, True, True),
-                                                  (64, True, False)])
+                                                  (64, True, False), (4096, False, True)])
 def test_sparse_mla_paged_equals_contiguous(page_size, packed, f32):
     print(f"[paged] sparse read P={page_size} packed={packed} f32={f32}", flush=True)
     dsa = dsa_mod()
