@@ -15,7 +15,9 @@
 // One block per (head h, range of 32-query tiles); the four waves own the four groups of 32
 // value columns.  Each wave keeps its 32 rows of W_UV[h] -- all 512 latent dims, as the B
 // operands of the 32 K-steps -- in registers for the whole block, so the weights are read
-// once per block.  The query tiles stream through a two-slot LDS ring by direct
+// once per block.  Half of them arrive through LDS by whole-line copies (the other half is
+// loaded straight into registers, so that all of W_UV[h] is in flight at once; see the
+// staging below).  The query tiles stream through a two-slot LDS ring by direct
 // global->LDS copies: the 32 rows of o (one 1 KB row per copy instruction, whole 128-byte
 // lines) and the 32 gate rows of head h (four 256-byte rows per copy), one tile ahead.  Per
 // tile a wave runs 32 v_mfma_f32_32x32x16_bf16 (A = query rows of o from LDS at a 1040-byte
@@ -30,6 +32,8 @@ constexpr int kValueDim = 128;          // value head width
 constexpr int kVgRows = 32;             // queries per tile
 constexpr int kVgStride = kLatent + 8;  // LDS row stride of o in bf16 elements (1040 bytes)
 constexpr int kVgCopies = 8 + 2;        // copies per wave and tile: 8 rows of o, 2 x 4 gate rows
+constexpr int kVgQuarter = kLatent / 4;  // latent dims of W_UV per LDS stage
+constexpr int kVgWCopies = kValueDim * kVgQuarter * 2 / 1024 / 4;  // 1 KB copies per wave and quarter (8)
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
@@ -41,6 +45,7 @@ __global__ __launch_bounds__(256, 1) void value_gate_kernel(const uint16_t* __re
                                                             uint16_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][kVgRows * kVgStride];
     __shared__ __attribute__((aligned(16))) uint16_t g_lds[2][kVgRows * kValueDim];
+    __shared__ __attribute__((aligned(16))) uint16_t w_lds[2][kValueDim * kVgQuarter];
     const int h = static_cast<int>(blockIdx.x) % kMlaHeads;
     const int split = static_cast<int>(blockIdx.x) / kMlaHeads;
     const int tt0 = static_cast<int>(static_cast<int64_t>(n_tiles) * split / n_split);
@@ -49,13 +54,34 @@ __global__ __launch_bounds__(256, 1) void value_gate_kernel(const uint16_t* __re
     const int cg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave = column group
     const int r = lane & 31;
     const int hh = lane >> 5;
-    // this wave's W_UV rows: B operand of K-step s is dims 16 s + 8 hh .. +8 of row 32 cg + r
-    u32x4 bw[kLatent / 16];
-    {
-        const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kValueDim + 32 * cg + r) * kLatent + 8 * hh;
+    // The first two quarters of the latent dims of W_UV[h] (128 rows x 256 bytes each) reach
+    // LDS by whole-line global->LDS copies: copy k of a quarter moves rows 4k .. 4k+3, lane l
+    // the 16-byte piece (l % 16) ^ (row % 16) of row 4k + l / 16 into piece slot l % 16.  Each
+    // wave then reads its B operands (row 32 cg + r, piece 2 s' + hh of the quarter) into
+    // registers; eight lanes at a time read eight rows at distinct slots, so the reads are
+    // free of bank conflicts.  Loaded straight into registers, every load instruction gathers
+    // 32 bytes from each of 32 rows; all four quarters through a two-slot ring left only two
+    // in flight at a time, which a cold call paid for twice.
+    const uint16_t* wh = w_uv + static_cast<int64_t>(h) * kValueDim * kLatent;
+    auto stage_w = [&](int q, int b) {
 #pragma unroll
-        for (int s = 0; s < kLatent / 16; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
-    }
+        for (int k = 0; k < kVgWCopies; ++k) {
+            const int c = kVgWCopies * cg + k;  // copy index of the quarter, 0 .. 31
+            const int row = 4 * c + (lane >> 4);
+            const int piece = (lane & 15) ^ (row & 15);
+            copy_to_lds(wh + static_cast<int64_t>(row) * kLatent + kVgQuarter * q + 8 * piece,
+                        lds_offset(w_lds[b] + c * 4 * kVgQuarter));
+        }
+    };
+    u32x4 bw[kLatent / 16];
+    auto read_w = [&](int q, int b) {
+        const int row = 32 * cg + r;
+        const uint16_t* wr = w_lds[b] + row * kVgQuarter;
+#pragma unroll
+        for (int s = 0; s < kVgQuarter / 16; ++s)
+            bw[(kVgQuarter / 16) * q + s] =
+                *reinterpret_cast<const u32x4*>(wr + 8 * ((2 * s + hh) ^ (row & 15)));
+    };
     // copies of tile tt into slot b: rows 8 cg .. 8 cg + 7 of o, gate rows 8 cg .. 8 cg + 7
     // (lane l of a gate copy moves bytes 16 (l % 16) .. of gate row 4 k + l / 16); rows past T
     // copy the last query
@@ -76,7 +102,25 @@ __global__ __launch_bounds__(256, 1) void value_gate_kernel(const uint16_t* __re
                         lds_offset(g_lds[b] + (8 * cg + 4 * k) * kValueDim));
         }
     };
+    // quarters 0 and 1 through LDS, quarters 2 and 3 straight into registers (each lane its 16
+    // bytes of row 32 cg + r per K-step), then the first tile: every byte of W_UV[h] is in
+    // flight at once
+    stage_w(0, 0);
+    stage_w(1, 1);
+    {
+        const uint16_t* wrow = wh + static_cast<int64_t>(32 * cg + r) * kLatent + 8 * hh;
+#pragma unroll
+        for (int s = kLatent / 32; s < kLatent / 16; ++s) bw[s] = *reinterpret_cast<const u32x4*>(wrow + 16 * s);
+    }
     if (tt0 < tt1) stage(tt0, 0);
+    // quarter 0 is in once at most the 8 copies of quarter 1, the 16 register loads and the
+    // tile's copies are outstanding; quarter 1 once only the latter two are
+    if (tt0 < tt1) wait_vmcnt<kVgWCopies + 16 + kVgCopies>(); else wait_vmcnt<kVgWCopies + 16>();
+    lds_barrier();
+    read_w(0, 0);
+    if (tt0 < tt1) wait_vmcnt<16 + kVgCopies>(); else wait_vmcnt<16>();
+    lds_barrier();
+    read_w(1, 1);
     for (int tt = tt0; tt < tt1; ++tt) {
         const int b = (tt - tt0) & 1;
         // tile tt landed once only the copies issued after it may be outstanding
