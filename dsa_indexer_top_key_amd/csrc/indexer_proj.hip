@@ -47,6 +47,7 @@ constexpr int kProjMaxSplits = 32;               // ... with at most this many p
 struct ProjSplits {
     int q_splits, q_cps;    // query product: splits, chunks per split
     int kw_splits, kw_cps;  // residual product
+    int ring;               // LDS ring slots of the product kernel (2 or 4)
 };
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -59,9 +60,22 @@ static void split_k(int blocks_mn, int chunks, int* splits, int* cps) {
     *splits = ceil_div(chunks, *cps);
 }
 
+// Up to 128 tokens (one row tile) the products run on a four-slot ring, one block per CU, with
+// K split into runs of at most four chunks, so that all of a block's chunks are in flight at
+// once: 6 + 28 splits, 192 + 56 = 248 blocks.  (Through the two-slot ring, one chunk ahead,
+// each of a block's three or four chunks cost a round trip to memory.)
+constexpr int kSmallRing = 4;
 static ProjSplits proj_splits(int32_t T) {
     ProjSplits p;
     const int mt = ceil_div(T, kLdsTile);
+    if (mt == 1) {
+        p.ring = kSmallRing;
+        p.q_cps = p.kw_cps = kSmallRing;
+        p.q_splits = ceil_div(kQLatent / kLdsChunk, kSmallRing);
+        p.kw_splits = ceil_div(kResidual / kLdsChunk, kSmallRing);
+        return p;
+    }
+    p.ring = 2;
     split_k(mt * ceil_div(kQOut, kLdsTile), kQLatent / kLdsChunk, &p.q_splits, &p.q_cps);
     split_k(mt * ceil_div(kKWOut, kLdsTile), kResidual / kLdsChunk, &p.kw_splits, &p.kw_cps);
     return p;
@@ -86,16 +100,17 @@ size_t proj_workspace_bytes(int32_t T) {
 // block tile: its A rows and weight rows stream through LDS, shared by the block's four waves
 // (2 x 2, each a 64 x 64 tile of four accumulators), so every operand byte is read from L2
 // once per block.
-// K moves in 64-wide chunks (four MFMA steps, 128 bytes per row) through a two-slot ring
-// filled by direct global->LDS copies one chunk ahead; one barrier per chunk.  The ring takes
-// 64 KB, so two blocks share a CU and each covers the other's copy latency and barriers (a
-// three-slot ring, one block per CU, measured 5% slower at 4096 tokens and 18% at 64).  Row r of a
+// K moves in 64-wide chunks (four MFMA steps, 128 bytes per row) through a ring of RING slots
+// filled by direct global->LDS copies RING - 1 chunks ahead; one barrier per chunk.  Beyond
+// 128 tokens the ring has two slots (64 KB), so two blocks share a CU and each covers the
+// other's copy latency and barriers (a three-slot ring, one block per CU, measured 5% slower
+// at 4096 tokens and 18% at 64 with the older split of K).  Up to 128 tokens it has four
+// (128 KB, one block per CU) and every split has at most four chunks (see proj_splits).  Row r of a
 // slot occupies 128 bytes; its 16-byte piece p sits at position p ^ ((r / 2) % 8), so the 16
 // rows an operand read touches (same p) fall in 16 distinct 16-byte bank groups.  Copy d of a
 // chunk moves rows 8d..8d+7 (A rows for d < 16, weight rows for d >= 16): lane 8 rr + c loads
 // piece c ^ ((row / 2) % 8) of row 8d + rr into position c.  At step s lane l supplies
 // row l % 32 and the dims [32 (l / 32) + 8 s, +8) of the chunk, for both operands.
-constexpr int kLdsRing = 2;
 constexpr int kLdsSlot = 2 * kLdsTile * kLdsChunk;  // bf16 elements per slot (A then weight)
 constexpr int kLdsCopies = 2 * kLdsTile / 8 / 4;  // 1 KB copies per wave per chunk: 8
 
@@ -113,9 +128,21 @@ struct ProjProduct {
 // Both products run in one launch: blocks [0, p0.blocks) take the first product, the rest the
 // second (their latencies overlap; one launch instead of two).  Within a product,
 // block index = (split * row_tiles + row tile) * col_tiles + column tile.
+// This wave's copies of chunk i are done once only those of the chunks issued after it (at
+// most RING - 2) remain outstanding.
+template <int RING>
+__device__ __forceinline__ void wait_chunk(int after) {
+    if constexpr (RING >= 4)
+        if (after >= 2) { wait_vmcnt<2 * kLdsCopies>(); return; }
+    if constexpr (RING >= 3)
+        if (after >= 1) { wait_vmcnt<kLdsCopies>(); return; }
+    wait_vmcnt<0>();
+}
+
+template <int RING>
 __global__ __launch_bounds__(256) void proj_gemm_lds_kernel(ProjProduct p0, ProjProduct p1,
                                                             int M) {
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[kLdsRing][kLdsSlot];
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[RING][kLdsSlot];
     const bool first = static_cast<int>(blockIdx.x) < p0.blocks;  // block-uniform
     const ProjProduct& pr = first ? p0 : p1;
     const int bid = first ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) - p0.blocks;
@@ -159,25 +186,26 @@ __global__ __launch_bounds__(256) void proj_gemm_lds_kernel(ProjProduct p0, Proj
         }
         dst[j] = static_cast<uint32_t>((d >= 16 ? kLdsTile * kLdsChunk : 0) + 8 * (d & 15) * kLdsChunk) * 2;
     }
-    auto issue = [&](int i) {  // copies of the split's chunk i (clamped: past the end re-copy
-        const int c = c_begin + (i < n_chunks ? i : n_chunks - 1);  // its last chunk)
-        const uint32_t base = lds_offset(ring[i % kLdsRing]);
+    auto issue = [&](int i) {  // copies of the split's chunk i into slot i % RING
+        const int c = c_begin + i;
+        const uint32_t base = lds_offset(ring[i % RING]);
 #pragma unroll
         for (int j = 0; j < kLdsCopies; ++j)
             copy_to_lds(src[j] + static_cast<int64_t>(c) * kLdsChunk, base + dst[j]);
     };
 
     f32x16 acc[2][2] = {};
-#pragma unroll
-    for (int j = 0; j < kLdsRing - 1; ++j) issue(j);
+    // RING - 1 chunks ahead (all of them when the split has no more); a chunk past the split's
+    // end is never issued
+    const int ahead = n_chunks < RING - 1 ? n_chunks : RING - 1;  // block-uniform
+    for (int j = 0; j < ahead; ++j) issue(j);
     for (int i = 0; i < n_chunks; ++i) {
-        // this wave's copies of chunk i are done once only the copies of the kLdsRing - 2
-        // later chunks remain outstanding; the barrier covers every wave's copies and frees
-        // slot (i + kLdsRing - 1) % kLdsRing, chunk i - 1's
-        wait_vmcnt<(kLdsRing - 2) * kLdsCopies>();
+        // the barrier covers every wave's copies of chunk i and frees slot
+        // (i + RING - 1) % RING, chunk i - 1's
+        wait_chunk<RING>(n_chunks - 1 - i < RING - 2 ? n_chunks - 1 - i : RING - 2);
         lds_barrier();
-        issue(i + kLdsRing - 1);
-        const uint16_t* sa = ring[i % kLdsRing];
+        if (i + RING - 1 < n_chunks) issue(i + RING - 1);
+        const uint16_t* sa = ring[i % RING];
         const uint16_t* sb = sa + kLdsTile * kLdsChunk;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -307,7 +335,12 @@ hipError_t launch_indexer_proj(const uint16_t* c_q, const uint16_t* h, const uin
     ProjProduct kw{h, w_k, w_w, kIndexDim, kKWOut, kResidual, p.kw_cps, ceil_div(kKWOut, kLdsTile), mt, 0, pkw};
     kw.blocks = kw.col_tiles * mt * p.kw_splits;
     // the residual product's blocks (K = 7168) are the longest: dispatched first
-    hipLaunchKernelGGL(proj_gemm_lds_kernel, dim3(q.blocks + kw.blocks), dim3(256), 0, stream, kw, q, T);
+    if (p.ring == kSmallRing)
+        hipLaunchKernelGGL(proj_gemm_lds_kernel<kSmallRing>, dim3(q.blocks + kw.blocks), dim3(256), 0,
+                           stream, kw, q, T);
+    else
+        hipLaunchKernelGGL(proj_gemm_lds_kernel<2>, dim3(q.blocks + kw.blocks), dim3(256), 0,
+                           stream, kw, q, T);
     const int parts = epilogue_parts(T);
     hipLaunchKernelGGL(proj_epilogue_kernel, dim3(T * parts), dim3(256), 0, stream, pq,
                        p.q_splits > 1 ? p.q_splits : 0, pkw, p.kw_splits, T, gamma, beta, eps,
