@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/dsa.h: argument validation (before any HIP
-// call), workspace sizing, launch dispatch and error reporting.  No allocation, no host
-// synchronisation, no state kept between calls.
+// call), workspace sizing, launch dispatch and error reporting.  No allocation and no host
+// synchronisation; between calls only per-device lookups are kept (the scratch array's
+// address here, the CU count in the top-k launcher).
 #include <hip/hip_runtime.h>
 
 #include <cmath>

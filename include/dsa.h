@@ -25,8 +25,10 @@
  * Conventions shared by every entry point
  *  - Every array argument is a DEVICE pointer (memory on the GPU the stream belongs to).
  *    The caller allocates and owns all buffers, inputs, outputs and workspaces.  The
- *    library allocates nothing, frees nothing and keeps no state between calls, so calls
- *    on different streams are independent.
+ *    library allocates nothing and frees nothing; between calls it keeps only per-device
+ *    lookups (compute-unit count, the address of dsa_indexer_topk_noalloc's scratch array),
+ *    so calls on different streams are independent (except dsa_indexer_topk_noalloc calls
+ *    on one GPU, which share its scratch array).
  *  - bf16 tensors are passed as uint16_t bit patterns; all layouts are row-major and
  *    densely packed unless a leading dimension (ld, in ELEMENTS) is given.
  *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the null
