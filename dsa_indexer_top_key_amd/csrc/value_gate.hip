@@ -84,21 +84,22 @@ __global__ __launch_bounds__(256, 1) void value_gate_kernel(const uint16_t* __re
     };
     // copies of tile tt into slot b: rows 8 cg .. 8 cg + 7 of o, gate rows 8 cg .. 8 cg + 7
     // (lane l of a gate copy moves bytes 16 (l % 16) .. of gate row 4 k + l / 16); rows past T
-    // copy the last query
+    // copy the last query.  Each row is read by this block only: the copies carry the
+    // non-temporal hint (cold calls 14.4 -> 13.7 us at 64 queries, 35.4 -> 31.3 us at 300).
     auto stage = [&](int tt, int b) {
         const int t0 = tt * kVgRows;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int row = 8 * cg + k;
             const int tq = t0 + row < T ? t0 + row : T - 1;
-            copy_to_lds(o + (static_cast<int64_t>(tq) * kMlaHeads + h) * kLatent + 8 * lane,
+            copy_to_lds<true>(o + (static_cast<int64_t>(tq) * kMlaHeads + h) * kLatent + 8 * lane,
                         lds_offset(a_lds[b] + row * kVgStride));
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int row = 8 * cg + 4 * k + (lane >> 4);
             const int tq = t0 + row < T ? t0 + row : T - 1;
-            copy_to_lds(gate + (static_cast<int64_t>(tq) * kMlaHeads + h) * kValueDim + 8 * (lane & 15),
+            copy_to_lds<true>(gate + (static_cast<int64_t>(tq) * kMlaHeads + h) * kValueDim + 8 * (lane & 15),
                         lds_offset(g_lds[b] + (8 * cg + 4 * k) * kValueDim));
         }
     };
