@@ -14,6 +14,10 @@
 
 namespace dsa {
 
+// The keys are written once and not read back by this call: non-temporal stores (2 M keys,
+// cold: 361 -> 345 us), like the non-temporal loads of the raw rows.
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float half_wave_sum(float v) {
 #pragma unroll
     for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 32);
@@ -51,11 +55,11 @@ __global__ __launch_bounds__(256) void ln_keys_kernel(const float* __restrict__ 
         uint2 ox, oy;
         ox.x = pack_bf16x2(dx.x * rx * g.x + b.x, dx.y * rx * g.y + b.y);
         ox.y = pack_bf16x2(dx.z * rx * g.z + b.z, dx.w * rx * g.w + b.w);
-        reinterpret_cast<uint2*>(keys + row * kIndexDim)[sub] = ox;
+        __builtin_nontemporal_store(u32x2v{ox.x, ox.y}, reinterpret_cast<u32x2v*>(keys + row * kIndexDim) + sub);
         if (has2) {
             oy.x = pack_bf16x2(dy.x * ry * g.x + b.x, dy.y * ry * g.y + b.y);
             oy.y = pack_bf16x2(dy.z * ry * g.z + b.z, dy.w * ry * g.w + b.w);
-            reinterpret_cast<uint2*>(keys + row2 * kIndexDim)[sub] = oy;
+            __builtin_nontemporal_store(u32x2v{oy.x, oy.y}, reinterpret_cast<u32x2v*>(keys + row2 * kIndexDim) + sub);
         }
     }
 }
