@@ -141,8 +141,10 @@ class Clock:
             pass
 
     def cold(self, fn, n, warmup=2):
+        """Warmup steps are cold steps too (the overwrite, then the step), untimed."""
         torch = self.torch
-        for _ in range(warmup):
+        for i in range(warmup):
+            self.flush_buf.fill_(i & 0x7F)
             fn()
         evs = self._events(n)
         torch.cuda.synchronize()
