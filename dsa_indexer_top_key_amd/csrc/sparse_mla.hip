@@ -132,10 +132,11 @@ __device__ __forceinline__ void stage_out(const uint16_t* stage, uint16_t* dst, 
 // Ring fill of one tile (32 rows; padding rows load row 0 of the request, so every slot holds
 // finite data).  Every wave loads eight latent rows (rows 8 wave .. 8 wave + 7; lane l holds 16
 // bytes at offset 16 l of each 1 KB row) into registers at the start of a step and writes them
-// into the slot at its end; wave 3 also loads the four blocks of eight companion rows.  Plain
-// loads into registers, not direct global->LDS copies: on these random 1 KB rows a gather-only
-// probe moved 2.45 TB/s from HBM with register loads and 1.8 TB/s with the copies (5.2 and
-// 3.1 TB/s from the Infinity Cache), at any ring depth.
+// into the slot at its end; wave 3 also loads the four blocks of eight companion rows.  Loads
+// into registers, not direct global->LDS copies: on these random 1 KB rows a gather-only probe
+// moved 2.45 TB/s from HBM with plain register loads and 1.8 TB/s with the copies (5.2 and
+// 3.1 TB/s from the Infinity Cache); with the non-temporal hint the register loads move
+// 5.1 TB/s from HBM (missed rows are then not installed in the Infinity Cache).
 constexpr int kConsRows = kTile / 4;  // latent rows per wave (8)
 
 struct TileRegs {
