@@ -470,10 +470,23 @@ __device__ __forceinline__ void topk_select(
             cand = sm.prm[5];
         };
         if (kSaveBins && value_mode && cand <= kFastCand) {  // block-uniform
-            // the saved bins name the threshold bin's keys
+            // the saved bins name the threshold bin's keys (saved bins imply one register-resident
+            // chunk); one wave-uniform branch per group of four elements
 #pragma unroll
-            for (int e = 0; e < E; ++e)  // (saved bins imply one register-resident chunk)
-                if (kbin[kSaveBins ? e : 0] == bstar) sm.cbuf[atomicAdd(&sm.prm[4], 1u)] = key[e];
+            for (int g = 0; g < kGroups; ++g) {
+                bool in[4];
+                uint64_t any = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    in[c] = kbin[kSaveBins ? 4 * g + c : 0] == bstar;
+                    any |= __ballot(in[c]);
+                }
+                if (any) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (in[c]) sm.cbuf[atomicAdd(&sm.prm[4], 1u)] = key[4 * g + c];
+                }
+            }
             lds_barrier();
             resolve_small_bin();
         } else if (value_mode) {
