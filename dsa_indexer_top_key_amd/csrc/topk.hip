@@ -23,6 +23,7 @@
 // per-(element, wave) counts across the block) that writes the selected positions in
 // ascending order; ties at the threshold key are ranked by position with the same scan.
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 
@@ -412,16 +413,28 @@ __device__ __forceinline__ void topk_select(
         uint32_t kbin[kSaveBins ? E : 1];
         const int sh = value_mode ? 0 : shift_for(rhi - rlo);
         // one loop per binning (a per-element select on the block-uniform mode compiled into
-        // a branch per element)
+        // a branch per element).  Absent elements (key 0, positions past n) are not counted:
+        // a wave whose positions of the chunk all lie below n has none and counts without the
+        // per-element guard (which costs a compare, an exec-mask save and restore and two
+        // branches); only the wave that holds the row's end, and a merge (whose absent
+        // candidates lie anywhere), keep it.  (Counting them into bin 0 and subtracting their
+        // number instead made rows shorter than the chunk slower: their atomics all hit one
+        // address.)
         auto count = [&](auto bin_of) {
             for (int ch = 0; ch < n_chunks; ++ch) {
                 if (STREAM) load(ch);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
+                const bool full = MODE != kMerge &&
+                                  static_cast<int64_t>(ch) * kChunk + static_cast<int64_t>(wave + 1) * 64 * E <= n;
+                auto one = [&](int e, auto guarded) {
                     const uint32_t k = key[e];
                     const int bin = bin_of(k);
-                    if (k) atomicAdd(&sm.hist[bin], 1u);
-                    if constexpr (kSaveBins) kbin[e] = k ? static_cast<uint32_t>(bin) : 0xFFFFu;
+                    if constexpr (decltype(guarded)::value) {
+                        if (k) atomicAdd(&sm.hist[bin], 1u);
+                        if constexpr (kSaveBins) kbin[e] = k ? static_cast<uint32_t>(bin) : 0xFFFFu;
+                    } else {
+                        atomicAdd(&sm.hist[bin], 1u);
+                        if constexpr (kSaveBins) kbin[e] = static_cast<uint32_t>(bin);
+                    }
                     // Every wave's keys are in registers: the next row's copies now stream
                     // while this row is selected (issued earlier, they would compete with the
                     // slower waves' loads of this row).  One copy per eight elements counted:
@@ -431,6 +444,13 @@ __device__ __forceinline__ void topk_select(
                         if (e % (E / kPreGroups) == E / kPreGroups - 1)
                             topk_prefetch_group<E>(pre, next_row, n_next, e / (E / kPreGroups));
                     }
+                };
+                if (full) {  // wave-uniform
+#pragma unroll
+                    for (int e = 0; e < E; ++e) one(e, std::false_type{});
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) one(e, std::true_type{});
                 }
             }
         };
