@@ -303,6 +303,32 @@ def test_topk_persistent_rows_bit_exact():
         assert np.array_equal(got[t], O.topk_ids(rows[t, :n_valid[t]])), f"row {t} (n={n_valid[t]})"
 
 
+# Row lengths that end exactly on, or one position around, the span of one wave of a block
+# (64 E positions: 2048 for rows of up to 32768, 4096 for rows of up to 65536).  A wave whose
+# span lies wholly below the row length counts its level-0 bins without the per-element check
+# for absent positions; the wave holding the row's end keeps it.
+WAVE_EDGE_LENGTHS = {32768: [2049, 4095, 4096, 4097, 30719, 30720, 30721, 32767, 32768],
+                     65536: [32769, 36863, 36864, 36865, 61439, 61440, 61441, 65535, 65536]}
+
+
+@pytest.mark.parametrize("max_n", [32768, 65536])
+@pytest.mark.parametrize("kind", ["gauss", "coarse", "special"])
+def test_topk_rows_ending_at_wave_spans_bit_exact(max_n, kind):
+    """Every row equals the oracle.  At 65536 the 300 rows run the persistent grid (more rows
+    than CUs), so each length also follows other lengths inside a block."""
+    print(f"[topk wave edges] max_n={max_n} {kind}", flush=True)
+    dsa = dsa_mod()
+    lengths = WAVE_EDGE_LENGTHS[max_n]
+    t_count = len(lengths) if max_n == 32768 else 300
+    rows = synth.score_rows_np(47, kind, t_count, max_n)
+    n_valid = np.array([lengths[t % len(lengths)] for t in range(t_count)], np.int32)
+    ids = dsa.topk(dev(rows), dev(n_valid), max_n=max_n)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for t in range(t_count):
+        assert np.array_equal(got[t], O.topk_ids(rows[t, :n_valid[t]])), f"row {t} (n={n_valid[t]})"
+
+
 def check_selection(lay, ids, ref_scores):
     for t in range(lay.T):
         row = ids[t]
