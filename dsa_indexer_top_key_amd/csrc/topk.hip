@@ -38,11 +38,14 @@ constexpr uint32_t kKeyPosInf = 0xFF800000u;  // key of +inf
 
 // Order-preserving key: larger score -> larger key; -0 and +0 share a key; every NaN maps
 // to 1 (below -inf); 0 is never produced (it marks an absent element).
+// Six VALU operations: x + 0 turns -0 into +0 and leaves every other non-NaN value as it is
+// (fp32 denormals are kept: the kernels run with denormals preserved), the sign mask flips
+// the bits, and a class test catches NaN.  (The same map as testing NaN and -0 on the bits,
+// which took eight; equal on all 2^32 patterns.)
 __device__ __forceinline__ uint32_t score_key(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(x + 0.0f);
+    const uint32_t k = u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+    return __builtin_isnan(x) ? 1u : k;
 }
 
 // Score of a key: keys with the top bit set are non-negative scores (their sign bit was set),
