@@ -194,4 +194,7 @@ __device__ __forceinline__ void store_tile_bf16(uint16_t* dst, int64_t ld, int r
     }
 }
 
+// Compute units of the current device, looked up once per device (defined in topk.hip).
+int device_cus();
+
 }  // namespace dsa

@@ -8,8 +8,8 @@
 // HBM-bound streaming (512 B read + 256 B written per row).  Half a wave (32 lanes) owns
 // one row: each lane holds four consecutive floats (one 16-byte load), the mean and the
 // biased variance are reduced across the 32 lanes with xor-shuffles, and each lane stores
-// four bf16 (8 bytes).  Every load and store is fully coalesced; a grid-stride loop keeps
-// enough rows in flight to cover HBM latency.
+// four bf16 (8 bytes).  Every load and store is fully coalesced; a grid-stride loop over four
+// blocks per CU keeps enough rows in flight to cover HBM latency.
 #include "common.h"
 
 namespace dsa {
@@ -66,9 +66,13 @@ __global__ __launch_bounds__(256) void ln_keys_kernel(const float* __restrict__ 
 
 hipError_t launch_ln_keys(const float* raw, const float* gamma, const float* beta, float eps,
                           uint16_t* keys, int64_t n_rows, hipStream_t stream) {
-    // 8 rows per 256-thread block per pass; cap the grid at 16 blocks per CU (grid-stride)
+    // 8 rows per 256-thread block per pass, two passes per iteration; at most 4 blocks per CU
+    // (grid-stride): on 2 M keys, cold, 4 per CU took 285 us, 3 per CU 323, 2 per CU 392, 6
+    // per CU 295, 8 per CU 333 and 16 per CU 349 (more resident waves than needed to cover
+    // the latency only slowed the mixed read/write stream)
     const int64_t want = (n_rows + 15) / 16;
-    const int blocks = static_cast<int>(want < 4096 ? (want < 1 ? 1 : want) : 4096);
+    const int64_t cap = 4 * static_cast<int64_t>(device_cus());
+    const int blocks = static_cast<int>(want < cap ? (want < 1 ? 1 : want) : cap);
     hipLaunchKernelGGL(ln_keys_kernel, dim3(blocks), dim3(256), 0, stream, raw, gamma, beta,
                        eps, keys, n_rows);
     return hipGetLastError();

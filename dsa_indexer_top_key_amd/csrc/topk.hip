@@ -1244,9 +1244,10 @@ static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, cons
                            cands, cand_keys, 0);
 }
 
-// Compute units of the current device (the persistent grid size), looked up once per device
-// (threads that race on the first lookup store the same value).
-static int device_cus() {
+// Compute units of the current device (the persistent grid size, and the grid bound of the
+// LayerNorm cache fill), looked up once per device (threads that race on the first lookup
+// store the same value).
+int device_cus() {
     static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
