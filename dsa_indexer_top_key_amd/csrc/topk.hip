@@ -38,10 +38,11 @@ constexpr uint32_t kKeyPosInf = 0xFF800000u;  // key of +inf
 
 // Order-preserving key: larger score -> larger key; -0 and +0 share a key; every NaN maps
 // to 1 (below -inf); 0 is never produced (it marks an absent element).
-// Six VALU operations: x + 0 turns -0 into +0 and leaves every other non-NaN value as it is
-// (fp32 denormals are kept: the kernels run with denormals preserved), the sign mask flips
-// the bits, and a class test catches NaN.  (The same map as testing NaN and -0 on the bits,
-// which took eight; equal on all 2^32 patterns.)
+// Five VALU instructions: x + 0 turns -0 into +0 and leaves every other non-NaN value as it is
+// (fp32 denormals are kept: the kernels run with denormals preserved), an arithmetic shift and
+// one three-input bit operation (v_bitop3_b32) flip the bits, and an ordered self-compare with
+// a select sends NaN to 1.  (The same map as testing NaN and -0 on the bits, which took
+// eight; equal on all 2^32 patterns.)
 __device__ __forceinline__ uint32_t score_key(float x) {
     const uint32_t u = __float_as_uint(x + 0.0f);
     const uint32_t k = u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
