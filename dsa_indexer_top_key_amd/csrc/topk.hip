@@ -36,6 +36,12 @@ constexpr int kBinBits = 11;
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // key of -inf
 constexpr uint32_t kKeyPosInf = 0xFF800000u;  // key of +inf
 
+// The keys below need IEEE -0 and NaN semantics (x + 0 must not fold to x, isnan must not
+// fold to false).
+#if defined(__FAST_MATH__) || (defined(__FINITE_MATH_ONLY__) && __FINITE_MATH_ONLY__)
+#error "topk.hip needs IEEE semantics for -0 and NaN: build it without fast-math"
+#endif
+
 // Order-preserving key: larger score -> larger key; -0 and +0 share a key; every NaN maps
 // to 1 (below -inf); 0 is never produced (it marks an absent element).
 // Five VALU instructions: x + 0 turns -0 into +0 and leaves every other non-NaN value as it is
