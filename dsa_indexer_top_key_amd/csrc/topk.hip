@@ -59,7 +59,10 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 // the others negative ones (all bits were flipped).  Key 1 (NaN) gives a NaN pattern.
 __device__ __forceinline__ float key_to_score(uint32_t k) {
     const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(k) >> 31);  // ~0 if top bit set
-    return __uint_as_float(k ^ (~m | 0x80000000u));
+    // k ^ (~m | 0x80000000) as one three-input bit operation: truth table f(s0, s1, s2) =
+    // s0 ^ (~s1 | s2) is f(0xF0, 0xCC, 0xAA) = 0x4B.  (Written as C, the shift becomes a
+    // compare and a select, and the xor a third instruction.)
+    return __uint_as_float(__builtin_amdgcn_bitop3_b32(k, m, 0x80000000u, 0x4B));
 }
 
 // Value-linear bin of a key: trunc(clamp(x * scale + off, 0, 2047)) with x its score and
