@@ -1255,8 +1255,8 @@ static void launch_topk_e(unsigned blocks, const float* scores, int64_t ld, cons
 }
 
 // Compute units of the current device (the persistent grid size, and the grid bound of the
-// LayerNorm cache fill), looked up once per device (threads that race on the first lookup
-// store the same value).
+// LayerNorm and FP8 cache fills), looked up once per device (threads that race on the first
+// lookup store the same value).
 int device_cus() {
     static std::atomic<int> cached[64] = {};
     int dev = 0;
