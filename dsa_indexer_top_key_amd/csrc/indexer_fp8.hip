@@ -56,50 +56,68 @@ int64_t f8_chunk(int32_t T, int64_t max_s) {
 
 }  // namespace
 
-// Half a wave (32 lanes) per key row: each lane holds four consecutive bf16 values (8 bytes)
-// and writes their four codes (4 bytes); the row maximum is reduced with xor-shuffles; lane 0
-// of the half writes the scale.  Grid-stride over rows, four rows per half-wave per iteration
-// loaded before any is encoded, non-temporal loads and stores (each key is read once, each
-// code written once): 2 M keys cold 227 -> 194 us (one row per iteration and plain accesses;
-// two rows 197 us, eight 210 us).
+// A quarter of a wave (16 lanes) per key row: each lane holds eight consecutive bf16 values
+// (one 16-byte load) and writes their eight codes (8 bytes); the row maximum is reduced with
+// xor-shuffles.  A 256-thread block takes 64 consecutive rows per iteration, four per
+// quarter-wave, all loaded before any is encoded; lane j of a quarter-wave keeps the scale of
+// its j-th row, so the block's 64 scales leave as two whole 128-byte lines.  Grid-stride over
+// rows, non-temporal loads and stores (each key is read once, each code written once).
+// 2 M keys cold, codes and scales identical in every variant: half a wave per row (8-byte
+// loads, 4-byte code stores, one scale store per row) 193-195 us; a quarter-wave per row 155
+// us at two rows in flight per quarter and 16 blocks per CU, 146 us at four rows and 32 blocks
+// per CU (kept).
+constexpr int kF8FillR = 4;                   // rows per quarter-wave per iteration
+constexpr int kF8FillRows = 16 * kF8FillR;    // consecutive rows per 256-thread block and iteration
+
 __global__ __launch_bounds__(256) void quantize_keys_fp8_kernel(const uint16_t* __restrict__ keys,
                                                                 int64_t n_rows,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales) {
-    const int sub = threadIdx.x & 31;
-    const int64_t group = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 5;
-    const int64_t n_groups = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 5;
-    constexpr int R = 4;  // rows per half-wave per iteration
-    for (int64_t row0 = group; row0 < n_rows; row0 += R * n_groups) {
-        u32x2 raw[R];
+    const int sub = threadIdx.x & 15;      // elements 8 sub .. 8 sub + 7 of a row
+    const int quarter = threadIdx.x >> 4;  // quarter-wave of the block, 0 .. 15
+    constexpr int R = kF8FillR;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kF8FillRows; base < n_rows;
+         base += static_cast<int64_t>(gridDim.x) * kF8FillRows) {
+        const int64_t row0 = base + R * quarter;  // this quarter-wave's rows row0 .. row0 + R - 1
+        u32x4 raw[R];
+        float my_scale = 0.f;  // lane j < R: the scale of row row0 + j
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            const int64_t row = row0 + j * n_groups;
-            raw[j] = row < n_rows ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(keys + row * kIndexDim + 4 * sub))
-                                  : u32x2{0u, 0u};
+            const int64_t row = row0 + j;
+            raw[j] = row < n_rows ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(keys + row * kIndexDim + 8 * sub))
+                                  : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            const int64_t row = row0 + j * n_groups;
-            float x[4] = {__uint_as_float(raw[j][0] << 16), __uint_as_float(raw[j][0] & 0xFFFF0000u),
-                          __uint_as_float(raw[j][1] << 16), __uint_as_float(raw[j][1] & 0xFFFF0000u)};
-            float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+            const int64_t row = row0 + j;
+            float x[8];
 #pragma unroll
-            for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = __uint_as_float(raw[j][i] << 16);
+                x[2 * i + 1] = __uint_as_float(raw[j][i] & 0xFFFF0000u);
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
             int e = 0;
             if (amax > 0.f) {
                 int xe;
                 const float f = frexpf(amax, &xe);  // amax = f * 2^xe, f in [0.5, 1)
                 e = (xe - 1) - 8 + (f > 0.875f ? 1 : 0);
             }
-            uint32_t packed = 0;
+            u32x2 packed = {0u, 0u};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) packed |= e4m3_encode(ldexpf(x[i], -e)) << (8 * i);
-            if (row < n_rows) {
-                __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t*>(codes + row * kF8Key + 4 * sub));
-                if (sub == 0) scales[row] = ldexpf(1.0f, e);
+            for (int i = 0; i < 4; ++i) {
+                packed[0] |= e4m3_encode(ldexpf(x[i], -e)) << (8 * i);
+                packed[1] |= e4m3_encode(ldexpf(x[4 + i], -e)) << (8 * i);
             }
+            if (row < n_rows) __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(codes + row * kF8Key + 8 * sub));
+            if (sub == j) my_scale = ldexpf(1.0f, e);
         }
+        // lanes 0 .. R-1 of every quarter-wave: the block's scales form one contiguous 128-byte line
+        if (sub < R && row0 + sub < n_rows) scales[row0 + sub] = my_scale;
     }
 }
 
@@ -236,10 +254,10 @@ __global__ __launch_bounds__(256) void indexer_decode_fp8_kernel(
 
 hipError_t launch_quantize_keys_fp8(const uint16_t* keys, int64_t n_rows, uint8_t* codes,
                                     float* scales, hipStream_t stream) {
-    // 8 rows per 256-thread block per pass; at most 16 blocks per CU (grid-stride: with four
-    // rows in flight per half-wave, 8 blocks per CU took 202 us and 32 took 202 us, against 194)
-    const int64_t want = (n_rows + 7) / 8;
-    const int64_t cap = 16 * static_cast<int64_t>(device_cus());
+    // 64 rows per 256-thread block per pass; at most 32 blocks per CU (grid-stride; 2 M keys
+    // cold: 8 per CU 162 us, 16 per CU 153 us, 32 per CU 146 us)
+    const int64_t want = (n_rows + kF8FillRows - 1) / kF8FillRows;
+    const int64_t cap = 32 * static_cast<int64_t>(device_cus());
     const int blocks = static_cast<int>(want < cap ? (want < 1 ? 1 : want) : cap);
     hipLaunchKernelGGL(quantize_keys_fp8_kernel, dim3(blocks), dim3(256), 0, stream, keys, n_rows,
                        codes, scales);

@@ -228,7 +228,8 @@ dsa_status_t dsa_sparse_mla_attn_paged(const uint16_t* q, const uint16_t* latent
  *
  * dsa_quantize_index_keys_fp8: keys [n_rows,128] bf16 (16-byte aligned) -> codes
  *   [n_rows,128] uint8 (16-byte aligned) and scales [n_rows] float32 (4-byte aligned).
- *   Bit-reproducible (exact power-of-two scaling, integer rounding).
+ *   Bit-reproducible (exact power-of-two scaling, integer rounding).  Keys must be finite:
+ *   a row holding +-inf or NaN gets unspecified codes and scale (no access leaves the row).
  * dsa_indexer_scores_fp8 / dsa_indexer_topk_fp8: as dsa_indexer_scores / dsa_indexer_topk with
  *   the keys replaced by (codes, scales): scores[t][j] = sum_h w[t][h] * max(0,
  *   q_idx[t][h] . decoded key j), fp32 sums; the workspace of dsa_indexer_topk_fp8 is sized by

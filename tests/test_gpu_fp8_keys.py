@@ -77,6 +77,36 @@ def test_quantization_bit_exact():
     assert np.array_equal(codes, rc)
 
 
+def test_quantization_every_bf16_value_bit_exact():
+    """Every finite bf16 value of magnitude <= 448 (both signs, zeros and bf16 subnormals
+    included), in rows whose maximum is 448 (scale 1), and the same values times 2^20 in rows
+    whose maximum is 448 * 2^20 (scale 2^20, the scaled values become fp32 subnormals at the
+    bottom): the codes must equal the oracle's correctly rounded E4M3 codes, every one."""
+    print("[fp8] every bf16 value", flush=True)
+    pos = np.arange(0, 0x43E1, dtype=np.uint32)            # +0 .. 448 (0x43E0 = 1.75 * 2^8)
+    bits = np.concatenate([pos, pos | 0x8000])
+    vals = (bits << 16).view(np.float32)
+    per_row = 127
+    n_rows = -(-vals.size // per_row)
+    body = np.zeros(n_rows * per_row, np.float32)
+    body[:vals.size] = vals
+    rows = []
+    for mult in (1.0, 2.0 ** 20):
+        x = np.concatenate([body.reshape(n_rows, per_row) * np.float32(mult),
+                            np.full((n_rows, 1), 448.0 * mult, np.float32)], axis=1)
+        rows.append(synth.bf16_bits_from_f32(x))
+    keys = np.concatenate(rows)
+    assert np.array_equal((keys[:n_rows, :per_row].astype(np.uint32) << 16).view(np.float32).ravel()[:vals.size].view(np.uint32),
+                          vals.view(np.uint32))                  # the bf16 rows hold the values exactly
+    codes, scales = quantize(keys)
+    rc, rs = O.quantize_keys_fp8(keys)
+    assert np.array_equal(rs[:n_rows], np.ones(n_rows)) and np.array_equal(rs[n_rows:], np.full(n_rows, 2.0 ** 20))
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
+    bad = np.nonzero(codes != rc)
+    assert bad[0].size == 0, (f"{bad[0].size} codes differ, first at row {bad[0][0]} col {bad[1][0]}: "
+                              f"got {codes[bad][0]:#04x}, oracle {rc[bad][0]:#04x}")
+
+
 def check_scores(lay, d, codes, scales, got):
     ref = O.indexer_scores_fp8(d["q_idx"], d["w"], codes, scales, lay.kv_off, lay.q_req, lay.q_pos)
     for t in range(lay.T):
